@@ -1,0 +1,14 @@
+"""CPU oracle (test infrastructure only; see paged_attention.py)."""
+from .paged_attention import (  # noqa: F401
+    append,
+    attend,
+    attend_split,
+    blocks_for,
+    combine,
+    gather,
+    kv_cache_bytes,
+    new_pool,
+    paged_decode,
+    paged_prefill_chunk,
+    softmax_summary,
+)
