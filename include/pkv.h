@@ -1,0 +1,182 @@
+/*
+ * pkv.h — paged KV-cache attention for one continuous-batching step, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The problem (pages by title and section):
+ *   - Each sequence's keys/values live in fixed-size blocks of a shared pool;
+ *     a per-sequence block table maps logical block j to a physical block;
+ *     only a sequence's last block may be partly filled.
+ *     ("LLM 7 - Efficient LLM Serving", 3. KV Cache and PagedAttention,
+ *     "Paging the Cache"; "The Serving Playbook", "Paged KV cache".)
+ *   - Each step appends the new tokens' K/V into slots assigned by a slot
+ *     mapping, then attends ("LLM 7", 3., "What the Cache Stores"; "The
+ *     Serving Playbook", "CUDA graphs and the CPU you forgot about").
+ *   - Context lengths are read from a device buffer, not passed as launch
+ *     arguments, so launches are identical from step to step ("Inference
+ *     Engineering, Part 2: What Actually Runs the Model", "What a kernel is,
+ *     and three meanings of the word").
+ *   - Query heads share KV heads in contiguous groups (grouped-query
+ *     attention: "Inference Engineering, Part 2", "The KV cache").
+ *   - A decode row is split along the KV axis into partitions whose partial
+ *     softmax summaries a second pass rescales into the answer ("The Serving
+ *     Playbook", "The block table lives in the hottest kernel in the system";
+ *     "Kernel fusion, briefly"); the partial summaries combine by the online
+ *     softmax rule ("LLM 7", 2. FlashAttention, "Online Softmax Makes Tiling
+ *     Possible").
+ *   - A prefill chunk attends causally to the cached prefix and to itself
+ *     ("The Serving Playbook", "Chunked prefill"; "Prefill and decode want
+ *     different machines").
+ *
+ * Conventions for every entry point
+ *   - All tensors are device memory owned by the caller; the library never
+ *     allocates or frees device memory and never synchronizes the host.
+ *     Every call only enqueues kernels on `stream` (a hipStream_t; NULL = the
+ *     null stream), so calls may be captured into a HIP graph.
+ *   - Element type: the pool's dtype (PKV_F32 or PKV_BF16) for query, key,
+ *     value and out. Integer tensors are int32 except slot_mapping (int64).
+ *   - Every pointer must be 16-byte aligned; tensors are dense row-major.
+ *   - Errors: a non-zero pkv_status is returned and nothing is enqueued;
+ *     pkv_last_error() gives a message (thread-local). Values *inside*
+ *     device buffers (block ids, lengths, slots) cannot be checked without a
+ *     synchronization and are the caller's contract: block ids in
+ *     [0, num_blocks), 0 <= context_lens[b] <= max_blocks_per_seq*block_size,
+ *     slots < num_blocks*block_size, no two tokens of one call with the same
+ *     slot (they would race).
+ *   - Supported geometry: block_size 16; head_dim 64 or 128; query heads per
+ *     KV head (num_q_heads / num_kv_heads) from 1 to 8.
+ *
+ * Pool layout in HBM, per layer (this is the "reshape" of reshape_and_cache:
+ * the head dimension is cut into 16-byte vectors so that loads stay wide
+ * despite the block-table indirection):
+ *   K: [num_blocks][num_kv_heads][head_dim/x][block_size][x], x = 16/elem_bytes
+ *      (8 for bf16, 4 for fp32): for a fixed 16-byte slice of the head
+ *      dimension, the 16 tokens of a block are consecutive 16-byte vectors.
+ *   V: [num_blocks][num_kv_heads][block_size][head_dim]: each token's value
+ *      row is contiguous.
+ *   One (block, kv head) tile of K or V is block_size*head_dim*elem_bytes
+ *   contiguous bytes (4 KiB for bf16 at head_dim 128).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = -1,   /* bad pointer, size, alignment or index */
+    PKV_ERR_UNSUPPORTED = -2,   /* valid but not implemented (geometry, dtype) */
+    PKV_ERR_HIP = -3,           /* the HIP runtime reported an error */
+    PKV_ERR_WORKSPACE = -4      /* workspace missing or too small */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Opaque handle: geometry plus per-layer K/V pool pointers (host memory only). */
+typedef struct pkv_pool pkv_pool;
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Bytes of one layer's K pool and V pool for the given geometry (each is
+ * num_blocks*num_kv_heads*block_size*head_dim*elem_bytes). */
+pkv_status kv_pool_bytes(int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                         pkv_dtype dtype, size_t* k_bytes_per_layer,
+                         size_t* v_bytes_per_layer);
+
+/* Wrap caller-allocated per-layer pools (device pointers, each at least
+ * kv_pool_bytes() long, 16-byte aligned) in a handle. The handle copies the
+ * two pointer arrays; it does not own the device memory. */
+pkv_status kv_pool_create(pkv_pool** out, int num_layers, int num_blocks, int block_size,
+                          int num_kv_heads, int head_dim, pkv_dtype dtype,
+                          void* const* k_layers, void* const* v_layers);
+
+/* Free the handle (never the device memory). NULL is accepted. */
+pkv_status kv_pool_destroy(pkv_pool* pool);
+
+/* Append: for t < num_tokens with slot s = slot_mapping[t] >= 0, write
+ * key[t][h][:] and value[t][h][:] (all KV heads h) into block s / block_size,
+ * offset s % block_size of `layer`'s pools, in the layout above. Negative
+ * slots are skipped. Values are copied bit for bit.
+ *   key, value: [num_tokens][num_kv_heads][head_dim], pool dtype.
+ *   slot_mapping: int64 [num_tokens].
+ * num_tokens == 0 is a no-op. */
+pkv_status reshape_and_cache(const pkv_pool* pool, int layer, const void* key,
+                             const void* value, const int64_t* slot_mapping,
+                             int num_tokens, void* stream);
+
+/* Workspace bytes paged_attention_decode needs for these arguments (0 when no
+ * sequence can be split). Depends only on host-side sizes. */
+pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_seqs,
+                                                  int num_q_heads, int max_blocks_per_seq,
+                                                  int partition_size, size_t* bytes);
+
+/* Decode attention: sequence b's single query row attends to the first
+ * context_lens[b] tokens of its cache (the token appended this step included):
+ *   out[b][i] = sum_t softmax_t(scale * <query[b][i], K_b[t][i/G]>) V_b[t][i/G]
+ * with G = num_q_heads / num_kv_heads and K_b/V_b read through
+ * block_tables[b][t / block_size]. context_lens[b] == 0 gives a zero row.
+ *   out, query: [num_seqs][num_q_heads][head_dim], pool dtype (out is rounded
+ *     to nearest even from fp32 accumulators).
+ *   block_tables: int32 [num_seqs][max_blocks_per_seq]; entries past a
+ *     sequence's last block are never read.
+ *   context_lens: int32 [num_seqs].
+ *   partition_size: tokens per KV partition, a positive multiple of 64;
+ *     0 = the library's choice; < 0 = never split. A sequence longer than one
+ *     partition is processed by several workgroups whose partial (max, sum,
+ *     output) are combined by a second kernel.
+ *   workspace: device memory of at least
+ *     paged_attention_decode_workspace_bytes(...) bytes (may be NULL when
+ *     that is 0). Contents on entry are ignored. */
+pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
+                                  const void* query, const int32_t* block_tables,
+                                  const int32_t* context_lens, int num_seqs,
+                                  int num_q_heads, int max_blocks_per_seq, float scale,
+                                  int partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Prefill-chunk attention: sequence s owns query rows
+ * cu_q_lens[s] .. cu_q_lens[s+1]-1 (T_s = its chunk length, T_s <= max_q_len).
+ * The chunk's own K/V must already be appended, so the cache holds
+ * ctx_s = context_lens[s] >= T_s tokens; chunk row r is at absolute position
+ * ctx_s - T_s + r and attends causally to positions 0 .. ctx_s - T_s + r.
+ *   out, query: [total_q_tokens][num_q_heads][head_dim], pool dtype.
+ *   cu_q_lens: int32 [num_seqs + 1], cu_q_lens[0] == 0, non-decreasing,
+ *     cu_q_lens[num_seqs] == total_q_tokens.
+ *   block_tables: int32 [num_seqs][max_blocks_per_seq]; context_lens: int32
+ *     [num_seqs]. The contraction runs on bf16 MFMA (PKV_BF16 pools only). */
+pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* out,
+                                         const void* query, const int32_t* cu_q_lens,
+                                         const int32_t* block_tables,
+                                         const int32_t* context_lens, int num_seqs,
+                                         int total_q_tokens, int max_q_len, int num_q_heads,
+                                         int max_blocks_per_seq, float scale, void* stream);
+
+/* ---- kernel timing (measurement support, not part of the attention path) ----
+ * While enabled, every kernel the library enqueues is bracketed by a pair of
+ * HIP events on the same stream (events are created by pkv_timing_enable,
+ * never inside the calls). pkv_timing_read waits for the recorded events and
+ * returns, for one kernel kind, the number of launches recorded and their
+ * summed duration in milliseconds. Recording stops silently once
+ * max_launches launches have been recorded. Not for use under graph capture. */
+typedef enum {
+    PKV_KERNEL_APPEND = 0,
+    PKV_KERNEL_DECODE_PARTITION = 1,
+    PKV_KERNEL_DECODE_REDUCE = 2,
+    PKV_KERNEL_PREFILL = 3,
+    PKV_KERNEL_KINDS = 4
+} pkv_kernel_kind;
+
+pkv_status pkv_timing_enable(int max_launches);
+pkv_status pkv_timing_disable(void);
+pkv_status pkv_timing_read(pkv_kernel_kind kind, int* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

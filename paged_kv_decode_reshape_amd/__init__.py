@@ -1,0 +1,183 @@
+"""Python binding of ``libpkv.so``, the gfx950 paged-KV attention library.
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name declared in ``include/pkv.h``; all work runs in the library's
+HIP kernels. Pointer arguments accept an integer device address or any object
+with ``data_ptr()`` (e.g. a torch tensor); ``stream`` accepts a HIP stream
+handle as an integer, an object with ``cuda_stream`` (torch's stream), or
+None for the null stream. A non-OK status raises :class:`PkvError`.
+
+The library is built in-tree by ``__graft_entry__.build()`` (or
+``python -m paged_kv_decode_reshape_amd._build``); calling any function
+without it raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "PkvError", "F32", "BF16", "KERNEL_APPEND", "KERNEL_DECODE_PARTITION",
+    "KERNEL_DECODE_REDUCE", "KERNEL_PREFILL", "library_path", "load",
+    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "reshape_and_cache",
+    "paged_attention_decode_workspace_bytes", "paged_attention_decode",
+    "paged_attention_prefill_chunk", "pkv_timing_enable", "pkv_timing_disable",
+    "pkv_timing_read", "pkv_last_error", "EXPORTED_SYMBOLS",
+]
+
+F32, BF16 = 0, 1
+KERNEL_APPEND, KERNEL_DECODE_PARTITION, KERNEL_DECODE_REDUCE, KERNEL_PREFILL = 0, 1, 2, 3
+
+_STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID_ARG", -2: "PKV_ERR_UNSUPPORTED",
+           -3: "PKV_ERR_HIP", -4: "PKV_ERR_WORKSPACE"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+_P = ctypes.POINTER
+
+# name -> (restype, argtypes); the C-ABI of include/pkv.h
+_SIGNATURES = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "kv_pool_bytes": (c_int, [c_int, c_int, c_int, c_int, c_int, _P(c_size_t), _P(c_size_t)]),
+    "kv_pool_create": (c_int, [_P(c_void_p), c_int, c_int, c_int, c_int, c_int, c_int,
+                               _P(c_void_p), _P(c_void_p)]),
+    "kv_pool_destroy": (c_int, [c_void_p]),
+    "reshape_and_cache": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p]),
+    "paged_attention_decode_workspace_bytes": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
+                                                       _P(c_size_t)]),
+    "paged_attention_decode": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_int, c_int, c_int, c_float, c_int, c_void_p, c_size_t,
+                                       c_void_p]),
+    "paged_attention_prefill_chunk": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                                              c_int, c_float, c_void_p]),
+    "pkv_timing_enable": (c_int, [c_int]),
+    "pkv_timing_disable": (c_int, []),
+    "pkv_timing_read": (c_int, [c_int, _P(c_int), _P(ctypes.c_double)]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libpkv.so")
+
+
+def load():
+    """Load libpkv.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                               "(there is no fallback implementation)")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise PkvError(status, load().pkv_last_error().decode())
+
+
+def pkv_last_error() -> str:
+    return load().pkv_last_error().decode()
+
+
+def kv_pool_bytes(num_blocks, block_size, num_kv_heads, head_dim, dtype):
+    k, v = c_size_t(), c_size_t()
+    _check(load().kv_pool_bytes(num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                                ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
+
+
+def kv_pool_create(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                   k_layers, v_layers):
+    """Returns the opaque pool handle (an integer). The caller keeps the device
+    memory alive and calls kv_pool_destroy when done."""
+    n = len(k_layers)
+    karr = (c_void_p * n)(*[_ptr(t) for t in k_layers])
+    varr = (c_void_p * n)(*[_ptr(t) for t in v_layers])
+    handle = c_void_p()
+    _check(load().kv_pool_create(ctypes.byref(handle), num_layers, num_blocks, block_size,
+                                 num_kv_heads, head_dim, dtype, karr, varr))
+    return handle.value
+
+
+def kv_pool_destroy(pool):
+    _check(load().kv_pool_destroy(pool))
+
+
+def reshape_and_cache(pool, layer, key, value, slot_mapping, num_tokens, stream=None):
+    _check(load().reshape_and_cache(pool, layer, _ptr(key), _ptr(value), _ptr(slot_mapping),
+                                    num_tokens, _stream(stream)))
+
+
+def paged_attention_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                                           partition_size=0):
+    out = c_size_t()
+    _check(load().paged_attention_decode_workspace_bytes(pool, num_seqs, num_q_heads,
+                                                         max_blocks_per_seq, partition_size,
+                                                         ctypes.byref(out)))
+    return out.value
+
+
+def paged_attention_decode(pool, layer, out, query, block_tables, context_lens, num_seqs,
+                           num_q_heads, max_blocks_per_seq, scale, partition_size=0,
+                           workspace=None, workspace_bytes=0, stream=None):
+    _check(load().paged_attention_decode(pool, layer, _ptr(out), _ptr(query), _ptr(block_tables),
+                                         _ptr(context_lens), num_seqs, num_q_heads,
+                                         max_blocks_per_seq, float(scale), partition_size,
+                                         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def paged_attention_prefill_chunk(pool, layer, out, query, cu_q_lens, block_tables,
+                                  context_lens, num_seqs, total_q_tokens, max_q_len,
+                                  num_q_heads, max_blocks_per_seq, scale, stream=None):
+    _check(load().paged_attention_prefill_chunk(pool, layer, _ptr(out), _ptr(query),
+                                                _ptr(cu_q_lens), _ptr(block_tables),
+                                                _ptr(context_lens), num_seqs, total_q_tokens,
+                                                max_q_len, num_q_heads, max_blocks_per_seq,
+                                                float(scale), _stream(stream)))
+
+
+def pkv_timing_enable(max_launches):
+    _check(load().pkv_timing_enable(max_launches))
+
+
+def pkv_timing_disable():
+    _check(load().pkv_timing_disable())
+
+
+def pkv_timing_read(kind):
+    """Returns (launches, total_ms) for one kernel kind."""
+    n, ms = c_int(), ctypes.c_double()
+    _check(load().pkv_timing_read(kind, ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value

@@ -1,0 +1,72 @@
+// KV append ("reshape_and_cache") for gfx950: scatter this step's new K/V
+// rows into their slots of the paged pool, bit for bit.
+//
+// What is computed: the new token's key and value are appended to the cache
+// ("LLM 7 - Efficient LLM Serving", 3. KV Cache and PagedAttention, "What the
+// Cache Stores"), at the slot the scheduler assigned (slot mappings: "The
+// Serving Playbook", "CUDA graphs and the CPU you forgot about"), with the
+// head dimension cut into 16-byte vectors so the attention kernels' loads stay
+// wide ("The Serving Playbook", "The block table lives in the hottest kernel
+// in the system").
+//
+// One thread moves one 16-byte vector of K and the same vector of V. Threads
+// are numbered (token, kv head, vector) with the vector fastest, so reads of
+// the token-major input and writes of V rows are contiguous 16-byte runs; K
+// vectors land 256 bytes apart (bf16, D=128) in the pool's K layout
+// [block][head][D/x][16][x].
+#include "device_common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+namespace {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams prm) {
+  constexpr int EPV = ElemTraits<T>::kPerVec;
+  constexpr int VPR = D / EPV;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long per_token = (long)prm.num_kv_heads * VPR;
+  if (idx >= per_token * prm.num_tokens) return;
+  const int t = (int)(idx / per_token);
+  const int rem = (int)(idx % per_token);
+  const int h = rem / VPR;
+  const int c = rem % VPR;
+  const int64_t slot = prm.slots[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / kBlockSize;
+  const int off = (int)(slot % kBlockSize);
+  const size_t src = ((size_t)t * prm.num_kv_heads + h) * D + (size_t)c * EPV;
+  const size_t tile = ((size_t)blk * prm.num_kv_heads + h) * (size_t)kBlockSize * D;
+  const Vec16 k = ld16(reinterpret_cast<const T*>(prm.key) + src);
+  const Vec16 v = ld16(reinterpret_cast<const T*>(prm.value) + src);
+  st16(reinterpret_cast<T*>(prm.kpool) + tile + ((size_t)c * kBlockSize + off) * EPV, k);
+  st16(reinterpret_cast<T*>(prm.vpool) + tile + (size_t)off * D + (size_t)c * EPV, v);
+}
+
+template <typename T, int D>
+hipError_t launch_append_t(const AppendParams& prm, hipStream_t stream, const KernelTimer& timer) {
+  constexpr int VPR = D / ElemTraits<T>::kPerVec;
+  const long threads = (long)prm.num_tokens * prm.num_kv_heads * VPR;
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  timer.begin(KernelKind::kAppend, stream);
+  hipLaunchKernelGGL((append_kernel<T, D>), dim3(grid), dim3(256), 0, stream, prm);
+  timer.end(KernelKind::kAppend, stream);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& prm, bool bf16, hipStream_t stream,
+                         const KernelTimer& timer) {
+  if (bf16) {
+    if (prm.head_dim == 128) return launch_append_t<uint16_t, 128>(prm, stream, timer);
+    if (prm.head_dim == 64) return launch_append_t<uint16_t, 64>(prm, stream, timer);
+  } else {
+    if (prm.head_dim == 128) return launch_append_t<float, 128>(prm, stream, timer);
+    if (prm.head_dim == 64) return launch_append_t<float, 64>(prm, stream, timer);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

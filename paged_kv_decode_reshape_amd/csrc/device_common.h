@@ -1,0 +1,142 @@
+// Device helpers shared by the gfx950 kernels: element formats, 16-byte
+// vectors, and cross-lane reductions over a 64-lane wavefront.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlockSize = 16;   // tokens per KV block
+constexpr int kWave = 64;        // CDNA wavefront width
+
+// bf16 is carried as raw uint16_t bits; fp32 as float.
+template <typename T> struct ElemTraits;
+template <> struct ElemTraits<float> { static constexpr int kPerVec = 4; };
+template <> struct ElemTraits<uint16_t> { static constexpr int kPerVec = 8; };
+
+struct alignas(16) Vec16 { uint32_t w[4]; };
+
+__device__ __forceinline__ Vec16 ld16(const void* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  return Vec16{{v.x, v.y, v.z, v.w}};
+}
+__device__ __forceinline__ void st16(void* p, const Vec16& v) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+}
+__device__ __forceinline__ Vec16 zero16() { return Vec16{{0u, 0u, 0u, 0u}}; }
+
+// bf16 <-> fp32. Widening is exact; narrowing rounds to nearest, ties to even.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;   // keep NaN a NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Widen one 16-byte vector to floats.
+template <typename T> __device__ __forceinline__ void widen(const Vec16& v, float* f);
+template <> __device__ __forceinline__ void widen<uint16_t>(const Vec16& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[2 * i] = bf16_lo(v.w[i]); f[2 * i + 1] = bf16_hi(v.w[i]); }
+}
+template <> __device__ __forceinline__ void widen<float>(const Vec16& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v.w[i]);
+}
+
+// Narrow kPerVec floats into one 16-byte vector of T.
+template <typename T> __device__ __forceinline__ Vec16 narrow(const float* f);
+template <> __device__ __forceinline__ Vec16 narrow<uint16_t>(const float* f) {
+  Vec16 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v.w[i] = f32_to_bf16_bits(f[2 * i]) | (f32_to_bf16_bits(f[2 * i + 1]) << 16);
+  return v;
+}
+template <> __device__ __forceinline__ Vec16 narrow<float>(const float* f) {
+  Vec16 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v.w[i] = __float_as_uint(f[i]);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane data movement.
+// DPP controls (GFX9 encoding): quad_perm, row_half_mirror, row_mirror, row_ror.
+// ---------------------------------------------------------------------------
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowRor8 = 0x128;      // row_ror:8 == lane ^ 8 inside a 16-lane row
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
+}
+
+// Value of lane (l ^ 16) and (l ^ 32), through the gfx950 permlane swaps.
+// permlane32_swap(a, a) yields {[a_lo, a_lo], [a_hi, a_hi]}; summing (or
+// taking the max of) both halves combines lane l with lane l ^ 32, and
+// likewise permlane16_swap pairs row 2k with row 2k+1.
+__device__ __forceinline__ float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Maximum over the 16 lanes of each row, result in every lane of the row.
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<kDppQuadXor1>(x);
+  x += dpp<kDppQuadXor2>(x);
+  x += dpp<kDppRowHalfMirror>(x);
+  x += dpp<kDppRowMirror>(x);
+  return x;
+}
+
+// Wavefront-wide maximum / sum, result in every lane.
+__device__ __forceinline__ float wave_max(float x) { return xor32_max(xor16_max(row_max(x))); }
+__device__ __forceinline__ float wave_sum(float x) { return xor32_sum(xor16_sum(row_sum(x))); }
+
+// Sum over the lanes l, l ^ (1 << k) for every k with (1 << k) >= Stride,
+// i.e. over all lanes that share (l % Stride). Stride in {8, 16, 32, 64}.
+template <int Stride>
+__device__ __forceinline__ float sum_lanes_above(float x) {
+  if constexpr (Stride <= 8) x += dpp<kDppRowRor8>(x);
+  if constexpr (Stride <= 16) x = xor16_sum(x);
+  if constexpr (Stride <= 32) x = xor32_sum(x);
+  return x;
+}
+
+// Compiler-level ordering for LDS traffic exchanged between lanes of one
+// wavefront (the hardware executes one wave's LDS operations in order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv

@@ -1,0 +1,372 @@
+// C-ABI host layer: argument validation, pool handles, workspace sizing,
+// launch geometry and kernel timing. No device memory is allocated here and
+// no call synchronizes the host, so every entry point can be captured into a
+// HIP graph.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "pkv.h"
+
+struct pkv_pool {
+  int num_layers;
+  int num_blocks;
+  int block_size;
+  int num_kv_heads;
+  int head_dim;
+  pkv_dtype dtype;
+  std::vector<void*> k_layers;
+  std::vector<void*> v_layers;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pkv_status hip_fail(hipError_t err, const char* what) {
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : 4; }
+
+pkv_status check_geometry(int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                          pkv_dtype dtype) {
+  if (num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive (got %d)", num_blocks);
+  if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be positive (got %d)", num_kv_heads);
+  if (block_size <= 0 || head_dim <= 0) return fail(PKV_ERR_INVALID_ARG, "block_size and head_dim must be positive");
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (block_size != pkv::kPoolBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
+  return PKV_OK;
+}
+
+pkv_status check_pool_layer(const pkv_pool* pool, int layer) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (layer < 0 || layer >= pool->num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, pool->num_layers);
+  return PKV_OK;
+}
+
+// Decode partitioning. Returns tokens per partition and the partition count of
+// the longest possible sequence.
+pkv_status decode_partitioning(const pkv_pool* pool, int num_seqs, int num_q_heads,
+                               int max_blocks_per_seq, int partition_size, int* part_tokens,
+                               int* max_parts) {
+  (void)num_seqs;
+  (void)num_q_heads;
+  const long max_ctx = (long)max_blocks_per_seq * pool->block_size;
+  long p;
+  if (partition_size < 0) {
+    p = (max_ctx + 63) / 64 * 64;
+  } else if (partition_size == 0) {
+    p = 512;
+  } else {
+    if (partition_size % 64 != 0)
+      return fail(PKV_ERR_INVALID_ARG, "partition_size %d must be a multiple of 64", partition_size);
+    p = partition_size;
+  }
+  if (p > (1L << 30)) p = 1L << 30;
+  if (p < 64) p = 64;
+  *part_tokens = (int)p;
+  *max_parts = (int)std::max(1L, (max_ctx + p - 1) / p);
+  return PKV_OK;
+}
+
+size_t round16(size_t x) { return (x + 15) / 16 * 16; }
+
+// ---- kernel timing ----
+struct TimingState {
+  std::mutex mu;
+  bool enabled = false;
+  int cap = 0;
+  int used = 0;
+  std::vector<hipEvent_t> start, stop;
+  std::vector<int> kind;
+};
+TimingState g_timing;
+thread_local int g_timing_slot = -1;
+
+void destroy_events_locked() {
+  for (auto e : g_timing.start) (void)hipEventDestroy(e);
+  for (auto e : g_timing.stop) (void)hipEventDestroy(e);
+  g_timing.start.clear();
+  g_timing.stop.clear();
+  g_timing.kind.clear();
+  g_timing.cap = g_timing.used = 0;
+  g_timing.enabled = false;
+}
+
+}  // namespace
+
+namespace pkv {
+
+void KernelTimer::begin(KernelKind kind, hipStream_t stream) const {
+  g_timing_slot = -1;
+  if (!g_timing.enabled) return;
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (!g_timing.enabled || g_timing.used >= g_timing.cap) return;
+  const int slot = g_timing.used++;
+  g_timing.kind[slot] = (int)kind;
+  (void)hipEventRecord(g_timing.start[slot], stream);
+  g_timing_slot = slot;
+}
+
+void KernelTimer::end(KernelKind kind, hipStream_t stream) const {
+  (void)kind;
+  if (g_timing_slot < 0) return;
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (g_timing_slot < (int)g_timing.stop.size())
+    (void)hipEventRecord(g_timing.stop[g_timing_slot], stream);
+  g_timing_slot = -1;
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+pkv_status kv_pool_bytes(int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                         pkv_dtype dtype, size_t* k_bytes_per_layer,
+                         size_t* v_bytes_per_layer) {
+  pkv_status st = check_geometry(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  if (!k_bytes_per_layer || !v_bytes_per_layer)
+    return fail(PKV_ERR_INVALID_ARG, "output pointers must not be NULL");
+  const size_t bytes = (size_t)num_blocks * num_kv_heads * block_size * head_dim * elem_bytes(dtype);
+  *k_bytes_per_layer = bytes;
+  *v_bytes_per_layer = bytes;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_create(pkv_pool** out, int num_layers, int num_blocks, int block_size,
+                          int num_kv_heads, int head_dim, pkv_dtype dtype,
+                          void* const* k_layers, void* const* v_layers) {
+  if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  pkv_status st = check_geometry(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  if (num_layers <= 0) return fail(PKV_ERR_INVALID_ARG, "num_layers must be positive (got %d)", num_layers);
+  if (!k_layers || !v_layers) return fail(PKV_ERR_INVALID_ARG, "layer pointer arrays must not be NULL");
+  for (int l = 0; l < num_layers; ++l) {
+    if (!k_layers[l] || !v_layers[l]) return fail(PKV_ERR_INVALID_ARG, "layer %d pool pointer is NULL", l);
+    if (!aligned(k_layers[l], 16) || !aligned(v_layers[l], 16))
+      return fail(PKV_ERR_INVALID_ARG, "layer %d pool pointer is not 16-byte aligned", l);
+  }
+  pkv_pool* p = new (std::nothrow) pkv_pool;
+  if (!p) return fail(PKV_ERR_INVALID_ARG, "out of host memory");
+  p->num_layers = num_layers;
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->num_kv_heads = num_kv_heads;
+  p->head_dim = head_dim;
+  p->dtype = dtype;
+  p->k_layers.assign(k_layers, k_layers + num_layers);
+  p->v_layers.assign(v_layers, v_layers + num_layers);
+  *out = p;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_destroy(pkv_pool* pool) {
+  delete pool;
+  return PKV_OK;
+}
+
+pkv_status reshape_and_cache(const pkv_pool* pool, int layer, const void* key,
+                             const void* value, const int64_t* slot_mapping, int num_tokens,
+                             void* stream) {
+  pkv_status st = check_pool_layer(pool, layer);
+  if (st != PKV_OK) return st;
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping) return fail(PKV_ERR_INVALID_ARG, "key, value and slot_mapping must not be NULL");
+  if (!aligned(key, 16) || !aligned(value, 16)) return fail(PKV_ERR_INVALID_ARG, "key/value must be 16-byte aligned");
+  if (!aligned(slot_mapping, 8)) return fail(PKV_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
+  const long threads = (long)num_tokens * pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype) / 16;
+  if (threads >= (1L << 32) - 256) return fail(PKV_ERR_UNSUPPORTED, "too many tokens in one call");
+  pkv::AppendParams prm{pool->k_layers[layer], pool->v_layers[layer], key, value, slot_mapping,
+                        num_tokens, pool->num_kv_heads, pool->head_dim};
+  (void)hipGetLastError();
+  hipError_t err = pkv::launch_append(prm, pool->dtype == PKV_BF16, (hipStream_t)stream, pkv::KernelTimer{});
+  if (err != hipSuccess) return hip_fail(err, "reshape_and_cache launch");
+  return PKV_OK;
+}
+
+pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_seqs,
+                                                  int num_q_heads, int max_blocks_per_seq,
+                                                  int partition_size, size_t* bytes) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (!bytes) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs >= 0, num_q_heads > 0 and max_blocks_per_seq > 0 required");
+  int part_tokens = 0, max_parts = 0;
+  pkv_status st = decode_partitioning(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                                      partition_size, &part_tokens, &max_parts);
+  if (st != PKV_OK) return st;
+  if (max_parts <= 1) {
+    *bytes = 0;
+    return PKV_OK;
+  }
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  *bytes = round16(rows * 2 * sizeof(float)) + rows * pool->head_dim * sizeof(float);
+  return PKV_OK;
+}
+
+pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
+                                  const void* query, const int32_t* block_tables,
+                                  const int32_t* context_lens, int num_seqs,
+                                  int num_q_heads, int max_blocks_per_seq, float scale,
+                                  int partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  pkv_status st = check_pool_layer(pool, layer);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, pool->num_kv_heads);
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group > 8) return fail(PKV_ERR_UNSUPPORTED, "%d query heads per KV head unsupported (1..8)", group);
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "out, query, block_tables and context_lens must not be NULL");
+  if (!aligned(out, 16) || !aligned(query, 16)) return fail(PKV_ERR_INVALID_ARG, "out/query must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PKV_ERR_INVALID_ARG, "block_tables/context_lens must be 4-byte aligned");
+  int part_tokens = 0, max_parts = 0;
+  st = decode_partitioning(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size,
+                           &part_tokens, &max_parts);
+  if (st != PKV_OK) return st;
+  size_t need = 0;
+  st = paged_attention_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                                              partition_size, &need);
+  if (st != PKV_OK) return st;
+  if (need > 0) {
+    if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+    if (!aligned(workspace, 16)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
+  }
+  const long units = (long)pool->num_kv_heads * num_seqs * max_parts;
+  if ((units + 3) / 4 >= (1L << 24)) return fail(PKV_ERR_UNSUPPORTED, "too many work units in one call");
+  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  float* ws_ml = static_cast<float*>(workspace);
+  float* ws_o = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round16(rows * 2 * sizeof(float)))
+                         : nullptr;
+  pkv::DecodeParams prm{out, ws_ml, ws_o, query, pool->k_layers[layer], pool->v_layers[layer],
+                        block_tables, context_lens, num_seqs, pool->num_kv_heads, group,
+                        pool->head_dim, max_blocks_per_seq, part_tokens, max_parts,
+                        scale * 1.4426950408889634f};
+  (void)hipGetLastError();
+  hipError_t err = pkv::launch_decode(prm, pool->dtype == PKV_BF16, (hipStream_t)stream, pkv::KernelTimer{});
+  if (err != hipSuccess) return hip_fail(err, "paged_attention_decode launch");
+  return PKV_OK;
+}
+
+pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* out,
+                                         const void* query, const int32_t* cu_q_lens,
+                                         const int32_t* block_tables,
+                                         const int32_t* context_lens, int num_seqs,
+                                         int total_q_tokens, int max_q_len, int num_q_heads,
+                                         int max_blocks_per_seq, float scale, void* stream) {
+  pkv_status st = check_pool_layer(pool, layer);
+  if (st != PKV_OK) return st;
+  if (pool->dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill chunks run on bf16 MFMA: bf16 pools only");
+  if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs, total_q_tokens and max_q_len must be >= 0");
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, pool->num_kv_heads);
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group > 8) return fail(PKV_ERR_UNSUPPORTED, "%d query heads per KV head unsupported (1..8)", group);
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  if (num_seqs == 0 || total_q_tokens == 0) return PKV_OK;
+  if (max_q_len == 0) return fail(PKV_ERR_INVALID_ARG, "max_q_len must be positive when there are query rows");
+  if (!out || !query || !cu_q_lens || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "out, query, cu_q_lens, block_tables and context_lens must not be NULL");
+  if (!aligned(out, 16) || !aligned(query, 16)) return fail(PKV_ERR_INVALID_ARG, "out/query must be 16-byte aligned");
+  if (!aligned(cu_q_lens, 4) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PKV_ERR_INVALID_ARG, "integer arrays must be 4-byte aligned");
+  pkv::PrefillParams prm{out, query, pool->k_layers[layer], pool->v_layers[layer], cu_q_lens,
+                         block_tables, context_lens, num_seqs, total_q_tokens, max_q_len,
+                         pool->num_kv_heads, group, pool->head_dim, max_blocks_per_seq,
+                         scale * 1.4426950408889634f};
+  (void)hipGetLastError();
+  hipError_t err = pkv::launch_prefill(prm, (hipStream_t)stream, pkv::KernelTimer{});
+  if (err == hipErrorNotSupported) return fail(PKV_ERR_UNSUPPORTED, "prefill geometry not supported");
+  if (err != hipSuccess) return hip_fail(err, "paged_attention_prefill_chunk launch");
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_enable(int max_launches) {
+  if (max_launches <= 0) return fail(PKV_ERR_INVALID_ARG, "max_launches must be positive");
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  destroy_events_locked();
+  g_timing.start.resize(max_launches);
+  g_timing.stop.resize(max_launches);
+  g_timing.kind.assign(max_launches, -1);
+  for (int i = 0; i < max_launches; ++i) {
+    hipError_t e1 = hipEventCreate(&g_timing.start[i]);
+    hipError_t e2 = e1 == hipSuccess ? hipEventCreate(&g_timing.stop[i]) : e1;
+    if (e2 != hipSuccess) {
+      if (e1 == hipSuccess) (void)hipEventDestroy(g_timing.start[i]);
+      g_timing.start.resize(i);
+      g_timing.stop.resize(i);
+      destroy_events_locked();
+      return hip_fail(e2, "hipEventCreate");
+    }
+  }
+  g_timing.cap = max_launches;
+  g_timing.used = 0;
+  g_timing.enabled = true;
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_disable(void) {
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  destroy_events_locked();
+  return PKV_OK;
+}
+
+pkv_status pkv_timing_read(pkv_kernel_kind kind, int* launches, double* total_ms) {
+  if (!launches || !total_ms) return fail(PKV_ERR_INVALID_ARG, "output pointers must not be NULL");
+  if ((int)kind < 0 || (int)kind >= PKV_KERNEL_KINDS) return fail(PKV_ERR_INVALID_ARG, "unknown kernel kind");
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  int n = 0;
+  double sum = 0.0;
+  for (int i = 0; i < g_timing.used; ++i) {
+    if (g_timing.kind[i] != (int)kind) continue;
+    hipError_t err = hipEventSynchronize(g_timing.stop[i]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
+    float ms = 0.f;
+    err = hipEventElapsedTime(&ms, g_timing.start[i], g_timing.stop[i]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventElapsedTime");
+    sum += ms;
+    ++n;
+  }
+  *launches = n;
+  *total_ms = sum;
+  return PKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Launch interfaces between the C-ABI host layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kPoolBlockSize = 16;  // tokens per KV block supported by the kernels
+
+enum class KernelKind : int { kAppend = 0, kDecodePartition = 1, kDecodeReduce = 2, kPrefill = 3 };
+
+// Records a pair of HIP events around a launch when kernel timing is enabled
+// (a no-op otherwise). Defined in host.hip.
+struct KernelTimer {
+  void begin(KernelKind kind, hipStream_t stream) const;
+  void end(KernelKind kind, hipStream_t stream) const;
+};
+
+struct AppendParams {
+  void* kpool;
+  void* vpool;
+  const void* key;
+  const void* value;
+  const int64_t* slots;
+  int num_tokens;
+  int num_kv_heads;
+  int head_dim;
+};
+
+struct DecodeParams {
+  void* out;
+  float* ws_ml;            // float2 [B][Hq][max_parts]: (max in base 2, normalizer)
+  float* ws_o;             // float  [B][Hq][max_parts][D]: unnormalized partial output
+  const void* query;
+  const void* kpool;
+  const void* vpool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs;
+  int num_kv_heads;
+  int group;               // query heads per KV head
+  int head_dim;
+  int max_blocks;
+  int part_tokens;         // tokens per partition (multiple of 64)
+  int max_parts;           // partitions of the longest possible sequence
+  float scale_log2;        // scale * log2(e)
+};
+
+struct PrefillParams {
+  void* out;
+  const void* query;
+  const void* kpool;
+  const void* vpool;
+  const int32_t* cu_q_lens;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs;
+  int total_q;
+  int max_q_len;
+  int num_kv_heads;
+  int group;
+  int head_dim;
+  int max_blocks;
+  float scale_log2;
+};
+
+hipError_t launch_append(const AppendParams& prm, bool bf16, hipStream_t stream,
+                         const KernelTimer& timer);
+hipError_t launch_decode(const DecodeParams& prm, bool bf16, hipStream_t stream,
+                         const KernelTimer& timer);
+hipError_t launch_prefill(const PrefillParams& prm, hipStream_t stream, const KernelTimer& timer);
+
+}  // namespace pkv

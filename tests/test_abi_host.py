@@ -1,0 +1,93 @@
+"""The C-ABI library loads without a GPU, exports every symbol the header
+declares, and rejects invalid arguments before touching the device (CPU)."""
+import os
+import re
+
+import pytest
+
+import paged_kv_decode_reshape_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pkv.library_path()),
+                                reason="libpkv.so not built (run __graft_entry__.build())")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for n in ("kv_pool_create", "reshape_and_cache", "paged_attention_decode",
+              "paged_attention_prefill_chunk"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = pkv.load()
+    names = header_functions()
+    assert set(names) == set(pkv.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _status(fn, *args):
+    with pytest.raises(pkv.PkvError) as e:
+        fn(*args)
+    return e.value.status, str(e.value)
+
+
+def test_pool_bytes_and_geometry_checks():
+    assert pkv.kv_pool_bytes(10, 16, 8, 128, pkv.BF16) == (10 * 8 * 16 * 128 * 2,) * 2
+    assert pkv.kv_pool_bytes(3, 16, 1, 64, pkv.F32) == (3 * 16 * 64 * 4,) * 2
+    assert _status(pkv.kv_pool_bytes, 10, 32, 8, 128, pkv.BF16)[0] == -2   # block_size 32
+    assert _status(pkv.kv_pool_bytes, 10, 16, 8, 96, pkv.BF16)[0] == -2    # head_dim 96
+    assert _status(pkv.kv_pool_bytes, 0, 16, 8, 128, pkv.BF16)[0] == -1
+    assert _status(pkv.kv_pool_bytes, 10, 16, 8, 128, 7)[0] == -1
+
+
+def test_pool_create_validates_pointers():
+    assert _status(pkv.kv_pool_create, 1, 4, 16, 1, 64, pkv.F32, [0], [256])[0] == -1
+    assert _status(pkv.kv_pool_create, 1, 4, 16, 1, 64, pkv.F32, [8], [256])[0] == -1   # misaligned
+    h = pkv.kv_pool_create(2, 4, 16, 1, 64, pkv.F32, [256, 512], [768, 1024])
+    try:
+        assert h
+        # layer out of range, bad head counts, bad partition size: all rejected on the host
+        st, msg = _status(pkv.paged_attention_decode, h, 2, 16, 16, 16, 16, 1, 4, 1, 1.0)
+        assert st == -1 and "layer" in msg
+        assert _status(pkv.paged_attention_decode, h, 0, 16, 16, 16, 16, 1, 9, 1, 1.0)[0] == -2
+        assert _status(pkv.paged_attention_decode, h, 0, 16, 16, 16, 16, 1, 4, 1, 1.0, 100)[0] == -1
+        assert _status(pkv.paged_attention_decode, h, 0, 16, 16, 16, 16, 1, 4, 1,
+                       float("nan"))[0] == -1
+        assert _status(pkv.reshape_and_cache, h, 0, 16, 16, 16, -1)[0] == -1
+        assert _status(pkv.reshape_and_cache, h, 0, 8, 16, 16, 1)[0] == -1        # misaligned key
+        # prefill runs on bf16 MFMA only
+        assert _status(pkv.paged_attention_prefill_chunk, h, 0, 16, 16, 16, 16, 16, 1, 4, 4, 4, 1,
+                       1.0)[0] == -2
+        # zero-sized calls are no-ops that succeed without touching the device
+        pkv.reshape_and_cache(h, 0, 16, 16, 16, 0)
+        pkv.paged_attention_decode(h, 0, 16, 16, 16, 16, 0, 4, 1, 1.0)
+    finally:
+        pkv.kv_pool_destroy(h)
+
+
+def test_workspace_sizing_and_check():
+    h = pkv.kv_pool_create(1, 4096, 16, 8, 128, pkv.BF16, [256], [512])
+    try:
+        # max context 2048 tokens, 512-token partitions -> 4 partitions per sequence
+        nb = pkv.paged_attention_decode_workspace_bytes(h, 3, 32, 128, 512)
+        rows = 3 * 32 * 4
+        assert nb == ((rows * 8 + 15) // 16) * 16 + rows * 128 * 4
+        assert pkv.paged_attention_decode_workspace_bytes(h, 3, 32, 128, -1) == 0
+        assert pkv.paged_attention_decode_workspace_bytes(h, 3, 32, 32, 512) == 0   # fits one partition
+        st, msg = _status(pkv.paged_attention_decode, h, 0, 256, 256, 256, 256, 3, 32, 128, 0.1,
+                          512, 256, nb - 16)
+        assert st == -4 and "too small" in msg
+        assert _status(pkv.paged_attention_decode, h, 0, 256, 256, 256, 256, 3, 32, 128, 0.1,
+                       512, None, nb)[0] == -4
+    finally:
+        pkv.kv_pool_destroy(h)
