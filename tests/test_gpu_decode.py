@@ -59,8 +59,8 @@ def test_append_bit_exact(dtype, d):
                                   (step.new_key, step.new_value, step.new_slots)):
         keep = slots >= 0
         blk, off = slots[keep] // 16, slots[keep] % 16
-        ref_k[blk, off] = vals_k.bits[keep]
-        ref_v[blk, off] = vals_v.bits[keep]
+        ref_k[blk, off] = vals_k.bits[keep].view(bits_dt)
+        ref_v[blk, off] = vals_v.bits[keep].view(bits_dt)
     assert np.array_equal(kbits, ref_k)
     assert np.array_equal(vbits, ref_v)
 
