@@ -1,0 +1,296 @@
+"""Benchmark: one attention layer-step over a paged KV cache on one MI355X.
+
+A step is the whole hot path for one layer: append this step's new K/V
+(reshape_and_cache), then paged decode attention (partition kernel plus the
+split-K reduction) and, for workloads with a prefill chunk, the MFMA
+prefill-chunk kernel. Inputs are seeded synthetic tensors of the workload's
+shapes, resident in HBM before timing starts. Steps rotate over R copies of the
+pool (one library "layer" each, >= 2 GiB in total) so the 256 MB Infinity
+Cache cannot serve repeated reads.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4|5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (no sparsity)
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama8b_b256_counters.txt")
+KERNEL_SOURCES = ["decode.hip", "device_common.h", "kernels.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_decode_reshape_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def make_step(config: int):
+    from paged_kv_decode_reshape_amd import workloads as W
+    if config == 3:
+        return W.llama8b_continuous()
+    if config == 4:
+        return W.long_context()
+    if config == 5:
+        return W.mixed_chunked_prefill()
+    raise SystemExit(f"--config {config}: the bench runs configs 3, 4 or 5 (1 and 2 are parity cases)")
+
+
+def algorithmic_bytes(step):
+    """Bytes a perfect implementation moves (each byte once)."""
+    e = 2 if step.dtype == "bf16" else 4
+    hkv, hq, d = step.num_kv_heads, step.num_q_heads, step.head_dim
+    _, dec_ctx = step.decode_inputs()
+    b = len(dec_ctx)
+    decode_kv = int(dec_ctx.astype(np.int64).sum()) * hkv * d * 2 * e
+    decode_qo = 2 * b * hq * d * e
+    n_new = len(step.new_slots)
+    append = 4 * n_new * hkv * d * e                    # read new K,V + write them
+    out = {"decode_kv": decode_kv, "decode_qo": decode_qo, "append": append}
+    if step.cu_q_lens is not None:
+        _, pctx = step.prefill_inputs()
+        qlens = np.diff(step.cu_q_lens)
+        kv = int(pctx.astype(np.int64).sum()) * hkv * d * 2 * e
+        out["prefill_bytes"] = kv + 2 * int(qlens.sum()) * hq * d * e
+        pairs = sum(int(np.sum(c - t + np.arange(t) + 1)) for c, t in zip(pctx, qlens))
+        out["prefill_flops"] = 4 * hq * d * pairs
+    return out
+
+
+def read_traffic(achieved_launch_bytes: int):
+    """HBM bytes per partition-kernel launch from committed rocprofv3 counters,
+    if they were taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    for line in open(COUNTERS_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(step, reps: int = 3):
+    """The oracle, as it stands, on the same workload: append + decode (+ prefill)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    s = step
+    pk = oracle.new_pool(s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim, np.float32)
+    pv = oracle.new_pool(s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim, np.float32)
+    oracle.append(pk, pv, s.cached_key.f32, s.cached_value.f32, s.cached_slots)
+    nk, nv, q = s.new_key.f32, s.new_value.f32, s.decode_query.f32
+    bt, cl = s.decode_inputs()
+    pq = s.prefill_query.f32 if s.prefill_query is not None else None
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.append(pk, pv, nk, nv, s.new_slots)
+        oracle.paged_decode(q, pk, pv, bt, cl, s.scale)
+        if pq is not None:
+            pbt, pcl = s.prefill_inputs()
+            oracle.paged_prefill_chunk(pq, s.cu_q_lens, pk, pv, pbt, pcl, s.scale)
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), threads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto, >= 2 GiB)")
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the attention step "
+              "has no cross-GPU part in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_decode_reshape_amd as pkv
+    pkv.load()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB")
+
+    t0 = time.time()
+    step = make_step(args.config)
+    s = step
+    log(f"workload {s.name}: generated in {time.time() - t0:.1f}s; "
+        f"{len(s.decode_seqs)} decode seqs, tokens {int(s.context_lens.sum())}, info {s.info}")
+    ab = algorithmic_bytes(s)
+    e = 2 if s.dtype == "bf16" else 4
+    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+
+    def dev_vals(v):
+        if v.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(v.bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(v.bits)).to(dev)
+
+    def dev_int(a, dt=torch.int32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
+
+    # ---- pools: R replicas = R library layers ----
+    kb, _ = pkv.kv_pool_bytes(s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim,
+                              pkv.BF16 if s.dtype == "bf16" else pkv.F32)
+    reps = args.replicas or max(2, math.ceil(2 * 2**30 / (2 * kb)))
+    k_layers = [torch.empty(kb // e, dtype=tdt, device=dev) for _ in range(reps)]
+    v_layers = [torch.empty(kb // e, dtype=tdt, device=dev) for _ in range(reps)]
+    dt_code = pkv.BF16 if s.dtype == "bf16" else pkv.F32
+    pool = pkv.kv_pool_create(reps, s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim,
+                              dt_code, k_layers, v_layers)
+    stream = torch.cuda.current_stream(dev)
+    pkv.reshape_and_cache(pool, 0, dev_vals(s.cached_key), dev_vals(s.cached_value),
+                          dev_int(s.cached_slots, torch.int64), len(s.cached_slots), stream)
+    for r in range(1, reps):
+        k_layers[r].copy_(k_layers[0])
+        v_layers[r].copy_(v_layers[0])
+    new_k, new_v = dev_vals(s.new_key), dev_vals(s.new_value)
+    new_slots = dev_int(s.new_slots, torch.int64)
+    n_new = len(s.new_slots)
+    bt, cl = s.decode_inputs()
+    bt_d, cl_d = dev_int(bt), dev_int(cl)
+    q_d = dev_vals(s.decode_query)
+    nseq = len(cl)
+    out = torch.empty((nseq, s.num_q_heads, s.head_dim), dtype=tdt, device=dev)
+    part = s.partition_size if args.partition_size is None else args.partition_size
+    wsb = pkv.paged_attention_decode_workspace_bytes(pool, nseq, s.num_q_heads, bt.shape[1], part)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    has_prefill = s.cu_q_lens is not None
+    if has_prefill:
+        pbt, pcl = s.prefill_inputs()
+        pbt_d, pcl_d, cu_d = dev_int(pbt), dev_int(pcl), dev_int(s.cu_q_lens)
+        pq_d = dev_vals(s.prefill_query)
+        ptotal = int(s.cu_q_lens[-1])
+        pmax = int(np.max(np.diff(s.cu_q_lens)))
+        pout = torch.empty((ptotal, s.num_q_heads, s.head_dim), dtype=tdt, device=dev)
+    torch.cuda.synchronize()
+    log(f"pool: {reps} replicas x {2 * kb / 2**30:.2f} GiB (K+V); workspace {wsb / 2**20:.1f} MiB")
+
+    def one_step(i):
+        layer = i % reps
+        pkv.reshape_and_cache(pool, layer, new_k, new_v, new_slots, n_new, stream)
+        pkv.paged_attention_decode(pool, layer, out, q_d, bt_d, cl_d, nseq, s.num_q_heads,
+                                   bt.shape[1], s.scale, part, ws, wsb, stream)
+        if has_prefill:
+            pkv.paged_attention_prefill_chunk(pool, layer, pout, pq_d, cu_d, pbt_d, pcl_d,
+                                              len(pcl), ptotal, pmax, s.num_q_heads,
+                                              pbt.shape[1], s.scale, stream)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    pkv.pkv_timing_enable(4 * args.steps + 8)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        one_step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    kt = {name: pkv.pkv_timing_read(kind) for name, kind in
+          (("append", pkv.KERNEL_APPEND), ("partition", pkv.KERNEL_DECODE_PARTITION),
+           ("reduce", pkv.KERNEL_DECODE_REDUCE), ("prefill", pkv.KERNEL_PREFILL))}
+    pkv.pkv_timing_disable()
+    ms_per_step = wall * 1e3 / args.steps
+    avg_us = {k: (ms / n * 1e3 if n else 0.0) for k, (n, ms) in kt.items()}
+    log("kernel avg us: " + ", ".join(f"{k} {v:.1f}" for k, v in avg_us.items()))
+
+    step_bytes = ab["decode_kv"] + ab["decode_qo"] + ab["append"] + ab.get("prefill_bytes", 0)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    part_bytes = ab["decode_kv"] + ab["decode_qo"]
+    achieved = part_bytes / (avg_us["partition"] * 1e-6) / 1e9 if avg_us["partition"] else 0.0
+    decode_us = avg_us["partition"] + avg_us["reduce"]
+    result = {
+        "metric": "paged decode attention: achieved HBM GB/s (% of peak) and us per layer-step",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": s.dtype,
+        "data": "synthetic (seeded N(0,1) values, lognormal lengths, churned block tables)",
+        "config": {
+            "workload": s.name,
+            "batch": nseq,
+            "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+            "head_dim": s.head_dim, "block_size": s.block_size,
+            "context_tokens": int(cl.sum()),
+            "partition_size": part if part else "auto",
+            "pool_replicas": reps,
+            "parallelism": "single GPU",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+        "us_per_layer_step": round(ms_per_step * 1e3, 2),
+        "kernel_us": {k: round(v, 2) for k, v in avg_us.items()},
+        "decode_attention_gbs": round(part_bytes / (decode_us * 1e-6) / 1e9, 1) if decode_us else None,
+        "algorithmic_bytes": ab,
+        "roofline": {
+            "kernel": "decode_partition_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic(part_bytes),
+            "algorithmic_bytes_per_launch": part_bytes,
+        },
+    }
+    if has_prefill and avg_us["prefill"]:
+        tf = ab["prefill_flops"] / (avg_us["prefill"] * 1e-6) / 1e12
+        result["prefill_mfma"] = {"tflops": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                                  "utilisation": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                  "flops_per_launch": ab["prefill_flops"]}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the same step ...")
+        t_cpu, threads = cpu_baseline(s)
+        result["cpu_baseline"] = {
+            "value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the whole step ({s.name}: append + decode of all {nseq} sequences"
+                      f"{' + prefill chunk' if has_prefill else ''}), numpy float64, median of 3;"
+                      f" {t_cpu:.2f} s per step on {os.cpu_count()} host CPUs",
+        }
+    pkv.kv_pool_destroy(pool)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -125,13 +125,20 @@ pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_
  *   block_tables: int32 [num_seqs][max_blocks_per_seq]; entries past a
  *     sequence's last block are never read.
  *   context_lens: int32 [num_seqs].
- *   partition_size: tokens per KV partition, a positive multiple of 64;
- *     0 = the library's choice; < 0 = never split. A sequence longer than one
- *     partition is processed by several workgroups whose partial (max, sum,
- *     output) are combined by a second kernel.
+ *   partition_size: how the KV axis is split over wavefronts.
+ *     0 (recommended): balanced split. The 64-token windows of all
+ *       (sequence, KV head) rows are shared equally by one wavefront per
+ *       resident wave slot of the GPU; rows cut between wavefronts leave
+ *       partial (max, sum, output) summaries that a second kernel combines.
+ *       The split is derived on the device from context_lens. Used for up
+ *       to 4096 sequences; larger batches fall back to 512-token partitions.
+ *     > 0: fixed partitions of that many tokens (a multiple of 64); a
+ *       sequence longer than one partition is combined by a second kernel.
+ *     < 0: never split (one wavefront per (sequence, KV head)).
  *   workspace: device memory of at least
  *     paged_attention_decode_workspace_bytes(...) bytes (may be NULL when
- *     that is 0). Contents on entry are ignored. */
+ *     that is 0), 16-byte aligned. Contents on entry are ignored; calls that
+ *     share a workspace must be ordered (same stream). */
 pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
                                   const void* query, const int32_t* block_tables,
                                   const int32_t* context_lens, int num_seqs,

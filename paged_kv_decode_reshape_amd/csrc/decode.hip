@@ -1,5 +1,5 @@
-// Paged decode attention for gfx950: a split-K partition kernel and the
-// reduction kernel that rescales the partial softmax summaries.
+// Paged decode attention for gfx950: partition kernels and the reduction
+// kernels that rescale their partial softmax summaries.
 //
 // What is computed (pages by title, section): scaled dot-product attention
 // with the row maximum subtracted ("LLM 7 - Efficient LLM Serving",
@@ -10,32 +10,40 @@
 // ("The Serving Playbook", "The block table lives in the hottest kernel in
 // the system"; Flash-Decoding in "Kernel fusion, briefly").
 //
-// Work decomposition. A work unit is (sequence b, KV head h, partition p):
-// the tokens [p*P, min((p+1)*P, ctx_b)) of one KV head, for all G query heads
-// of that head's group, so every K/V byte is read from HBM exactly once. One
-// wavefront owns one unit; a 256-thread workgroup holds four units. Units
-// are numbered with h fastest and p slowest, so the first partitions of all
-// sequences are dispatched first and the dispatcher retires the empty tail
-// units (partitions past a short sequence's end) last.
-//
-// Inside a unit the wave walks 64 tokens (4 blocks) per iteration:
+// Work. A segment is a contiguous token range of one (sequence b, KV head h)
+// for all G query heads of that head's group, so every K/V byte is read from
+// HBM exactly once. One wavefront runs a segment 64 tokens (4 blocks) at a
+// time:
 //   * q.K: lane l owns token l of the window. The K pool stores, for each
 //     16-byte slice of the head dimension, the 16 tokens of a block as
 //     consecutive vectors, so one load instruction reads 4 x 256 contiguous
 //     bytes (one per block) and each lane accumulates full dot products for
 //     its token with no cross-lane reduction (bf16 pairs on v_dot2_f32_bf16).
-//     The query slice is wave-uniform.
+//     The query rows sit in LDS and are read as wave-uniform slices.
 //   * online softmax: the window maximum per query head is reduced across the
 //     wavefront with DPP row operations and the gfx950 permlane swaps; the
-//     probabilities p = 2^(s - m) are written to LDS.
+//     probabilities p = 2^(s - m) go to LDS.
 //   * P.V: the V pool stores each token's row contiguously; one load
 //     instruction reads 4 (bf16, D=128) consecutive token rows (1 KiB), lane
 //     l holding 16 bytes of head dimension of one token. Each lane keeps fp32
 //     accumulators for its slice of the head dimension for all G heads and
 //     reads its tokens' probabilities from LDS (broadcast). Lanes sharing a
-//     head-dimension slice are summed once, at the end of the unit.
-// Scores are kept in base 2 (scale * log2(e) is folded in) so one v_exp_f32
+//     slice are summed once, at the end of the segment.
+// Scores are kept in base 2 (scale * log2(e) folded in) so one v_exp_f32
 // gives each probability.
+//
+// Two ways of cutting the work into segments:
+//   * balanced (the default): the launch has one wavefront per resident wave
+//     slot of the GPU, and the global sequence of 64-token windows, ordered
+//     (b, h, window), is split into equal contiguous shares. A wave writes
+//     the (b, h) rows it covers completely and leaves a partial summary for
+//     the pieces at the two ends of its share; the reduction combines them.
+//     Every workgroup derives the split on the device from context_lens (a
+//     prefix sum in LDS), so the launch does not depend on the lengths and
+//     stays graph-capturable. Waves finish within one window of each other
+//     whatever the length mix.
+//   * fixed partitions of P tokens: one wavefront per (b, h, partition),
+//     partitions dispatched in descending index order (long sequences first).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -48,15 +56,16 @@ struct DecodeShape {
   static constexpr int kEpv = ElemTraits<T>::kPerVec;   // elements per 16-byte vector
   static constexpr int kVecPerRow = D / kEpv;           // vectors per token row (K or V)
   static constexpr int kVInstPerBlock = kBlockSize * kVecPerRow / kWave;
-  static constexpr int kLanesPerRowV = kVecPerRow;      // lanes covering one V token row
   static constexpr int kTokensPerWindow = 64;
   static constexpr int kBlocksPerWindow = kTokensPerWindow / kBlockSize;
+  static constexpr int kKGroup = kVecPerRow < 16 ? kVecPerRow : 16;   // K vectors loaded at once
+  static constexpr int kVGroup = (kBlocksPerWindow * kVInstPerBlock <= 16)
+                                     ? kBlocksPerWindow
+                                     : 16 / kVInstPerBlock;            // V blocks loaded at once
   static_assert(kVecPerRow == 8 || kVecPerRow == 16 || kVecPerRow == 32, "head_dim");
 };
 
-// q.K for one 16-byte K vector against the query slices of all G heads.
-template <typename T, int G>
-__device__ __forceinline__ void dot_vec(float (&acc)[G], const Vec16& k, const Vec16 (&q)[G]);
+constexpr int kMaxBalancedSeqs = 4096;   // LDS prefix-sum capacity of the balanced kernels
 
 template <int G>
 __device__ __forceinline__ void dot_vec_bf16(float (&acc)[G], const Vec16& k, const Vec16 (&q)[G]) {
@@ -82,33 +91,289 @@ __device__ __forceinline__ void dot_vec_f32(float (&acc)[G], const Vec16& k, con
   }
 }
 
+// Opaque zero: stops the compiler from hoisting loop-invariant LDS reads of
+// the query out of the window loop (which would pin G*D/2 VGPRs).
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
+// Per-wave scratch in LDS.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void decode_partition_kernel(
-    T* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
-    const T* __restrict__ query, const T* __restrict__ kpool, const T* __restrict__ vpool,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    DecodeParams prm) {
+struct WaveLds {
+  float p[DecodeShape<T, D, G>::kTokensPerWindow][G];   // probabilities of the window
+  Vec16 q[G][DecodeShape<T, D, G>::kVecPerRow];          // the group's query rows
+};
+
+// Running online-softmax summary of one segment, for G query heads. m is
+// wave-uniform; l and o are per-lane partial sums until the end of the segment.
+template <int G, int EPV>
+struct Summary {
+  float m[G];
+  float l[G];
+  float o[G][EPV];
+};
+
+// Everything a wave needs to run segments of one launch.
+struct DecodeArgs {
+  const void* query;
+  const void* kpool;
+  const void* vpool;
+  const int32_t* block_tables;
+  int hkv;
+  int max_blocks;
+  float scale_log2;
+};
+
+// Accumulate tokens [tok_begin, tok_end) of (b, h) into a fresh summary.
+template <typename T, int D, int G>
+__device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
+    const DecodeArgs& a, WaveLds<T, D, G>& lds, int b, int h, int tok_begin, int tok_end) {
   using S = DecodeShape<T, D, G>;
   constexpr int EPV = S::kEpv;
   constexpr int VPR = S::kVecPerRow;
   constexpr int NVI = S::kVInstPerBlock;
-
-  __shared__ float p_lds[4][S::kTokensPerWindow][G];
+  constexpr int TPW = S::kTokensPerWindow;
+  constexpr int BPW = S::kBlocksPerWindow;
+  constexpr int KG = S::kKGroup;
+  constexpr int VB = S::kVGroup;
+  const T* __restrict__ query = static_cast<const T*>(a.query);
+  const T* __restrict__ kpool = static_cast<const T*>(a.kpool);
+  const T* __restrict__ vpool = static_cast<const T*>(a.vpool);
 
   const int lane = threadIdx.x & 63;
+  const int hq = a.hkv * G;
+  const int nwin = (tok_end - tok_begin + TPW - 1) / TPW;
+  const int lb_begin = tok_begin / kBlockSize;
+  const int nblk = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;   // blocks of the segment
+
+  wave_lds_sync();   // the wave's previous segment may still be reading q / p
+  {
+    const T* qbase = query + ((size_t)b * hq + (size_t)h * G) * D;
+    for (int i = lane; i < G * VPR; i += kWave) lds.q[i / VPR][i % VPR] = ld16(qbase + (size_t)i * EPV);
+  }
+
+  // Block ids of the segment, 64 per vector register: lane j holds logical
+  // block lb_begin + 64*chunk + j, clamped to the segment's last block so
+  // that every id is a real block of this sequence and every address formed
+  // below is in bounds (values read for tokens past the end are masked where
+  // they are used).
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin;
+  int ids = bt[min(lane, nblk - 1)];
+
+  const size_t tile = (size_t)kBlockSize * D;           // elements per (block, head) tile
+  const size_t head_off = (size_t)h * tile;
+  const size_t blk_stride = (size_t)a.hkv * tile;
+  const int row = lane >> 4;                            // block of the window for this lane's K token
+  const int tin = lane & 15;                            // token within that block
+  const int vvec = lane % VPR;                          // head-dim slice this lane owns for V
+  const int vtok0 = lane / VPR;                         // first token (within a block) it reads for V
+  const uint32_t voff = (uint32_t)(vtok0 * D + vvec * EPV) * (uint32_t)sizeof(T);
+
+  Summary<G, EPV> st;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.m[g] = -INFINITY;
+    st.l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) st.o[g][e] = 0.f;
+  }
+  wave_lds_sync();
+
+#pragma unroll 1
+  for (int w = 0; w < nwin; ++w) {
+    const int t0 = tok_begin + w * TPW;
+    const int lb = 4 * w;                               // first local block of the window
+    if (lb > 0 && (lb & 63) == 0) ids = bt[min(lb + lane, nblk - 1)];
+    int bid[BPW];
+#pragma unroll
+    for (int r = 0; r < BPW; ++r) bid[r] = __builtin_amdgcn_readlane(ids, min(lb + r, nblk - 1) & 63);
+    int kb = bid[0];
+#pragma unroll
+    for (int r = 1; r < BPW; ++r) kb = (row == r) ? bid[r] : kb;
+
+    // ---- q.K for this lane's token ----
+    // K loads: lane = token; one instruction reads 4 x 256 contiguous bytes;
+    // at most 16 vectors (64 VGPRs) are loaded at once. Query slices come from
+    // LDS one vector ahead of their use; the scheduling barriers stop the
+    // compiler from hoisting all G*VPR reads at once.
+    const char* kt = reinterpret_cast<const char*>(kpool + (size_t)kb * blk_stride + head_off) +
+                     (uint32_t)tin * 16u;
+    const int qz = opaque_zero();
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll
+    for (int c0 = 0; c0 < VPR; c0 += KG) {
+      Vec16 kv[KG];
+#pragma unroll
+      for (int c = 0; c < KG; ++c) kv[c] = ld16(kt + (c0 + c) * (kBlockSize * 16));
+      Vec16 qcur[G], qnext[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) qcur[g] = lds.q[g][c0 + qz];
+#pragma unroll
+      for (int c = 0; c < KG; ++c) {
+        if (c + 1 < KG) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) qnext[g] = lds.q[g][c0 + c + 1 + qz];
+        }
+        if constexpr (EPV == 8) dot_vec_bf16<G>(acc, kv[c], qcur);
+        else dot_vec_f32<G>(acc, kv[c], qcur);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int g = 0; g < G; ++g) qcur[g] = qnext[g];
+      }
+    }
+    const bool kvalid = (t0 + lane) < tok_end;
+    __builtin_amdgcn_sched_barrier(0);   // phase boundary: q.K | softmax
+
+    // ---- online softmax over the window ----
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float s = kvalid ? acc[g] * a.scale_log2 : -INFINITY;
+      const float mw = wave_max(s);
+      const float mn = fmaxf(st.m[g], mw);
+      const float alpha = fast_exp2(st.m[g] - mn);
+      st.m[g] = mn;
+      const float p = fast_exp2(s - mn);
+      st.l[g] = st.l[g] * alpha + p;
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) st.o[g][e] *= alpha;
+      lds.p[lane][g] = p;
+    }
+    wave_lds_sync();
+    __builtin_amdgcn_sched_barrier(0);   // phase boundary: softmax | P.V
+
+    // ---- P.V ----
+    // V loads: one instruction reads consecutive token rows; address = wave-
+    // uniform block base + this lane's 32-bit byte offset. They are issued
+    // after q.K so K and V never hold registers at the same time, at most 16
+    // vectors at once.
+    const bool partial = (t0 + TPW > tok_end);
+#pragma unroll
+    for (int r0 = 0; r0 < BPW; r0 += VB) {
+      Vec16 vv[VB][NVI];
+#pragma unroll
+      for (int r = 0; r < VB; ++r) {
+        const char* vt = reinterpret_cast<const char*>(vpool + (size_t)bid[r0 + r] * blk_stride + head_off);
+#pragma unroll
+        for (int i = 0; i < NVI; ++i) vv[r][i] = ld16(vt + voff + i * ((kWave / VPR) * D * (int)sizeof(T)));
+      }
+      if (partial) {
+        // Last, partial window: tokens past the end may hold anything (even
+        // NaN) and carry p = 0, so their V rows are zeroed before the products.
+#pragma unroll
+        for (int r = 0; r < VB; ++r) {
+#pragma unroll
+          for (int i = 0; i < NVI; ++i) {
+            if (t0 + (r0 + r) * kBlockSize + vtok0 + i * (kWave / VPR) >= tok_end) vv[r][i] = zero16();
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < VB; ++r) {
+#pragma unroll
+        for (int i = 0; i < NVI; ++i) {
+          const int tb = vtok0 + i * (kWave / VPR);
+          float pv[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) pv[g] = lds.p[(r0 + r) * kBlockSize + tb][g];
+          float vf[EPV];
+          widen<T>(vv[r][i], vf);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) st.o[g][e] = fmaf(pv[g], vf[e], st.o[g][e]);
+          }
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // Sum the per-lane partials: normalizers over the wave, outputs over the
+  // lanes that share a head-dimension slice. Every lane ends with the totals.
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.l[g] = wave_sum(st.l[g]);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) st.o[g][e] = sum_lanes_above<VPR>(st.o[g][e]);
+  }
+  return st;
+}
+
+// Final rows: out[g] = o[g] / l[g], rounded to T. out_row points at query head 0 of the group.
+template <typename T, int D, int G>
+__device__ __forceinline__ void write_rows(T* out_row, const Summary<G, ElemTraits<T>::kPerVec>& st) {
+  constexpr int EPV = ElemTraits<T>::kPerVec;
+  constexpr int VPR = D / EPV;
+  const int lane = threadIdx.x & 63;
+  if (lane < VPR) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float r[EPV];
+      const float inv = 1.0f / st.l[g];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) r[e] = st.o[g][e] * inv;
+      st16(out_row + (size_t)g * D + (size_t)lane * EPV, narrow<T>(r));
+    }
+  }
+}
+
+// Partial summary: (m, l) of head g at ml[g * ml_stride], unnormalized o at o_base + g * o_stride.
+template <typename T, int D, int G>
+__device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base,
+                                              size_t o_stride,
+                                              const Summary<G, ElemTraits<T>::kPerVec>& st) {
+  constexpr int EPV = ElemTraits<T>::kPerVec;
+  constexpr int VPR = D / EPV;
+  const int lane = threadIdx.x & 63;
+  if (lane < VPR) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float* wo = o_base + g * o_stride + (size_t)lane * EPV;
+#pragma unroll
+      for (int e = 0; e < EPV; e += 4)
+        *reinterpret_cast<float4*>(wo + e) = make_float4(st.o[g][e], st.o[g][e + 1], st.o[g][e + 2], st.o[g][e + 3]);
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) ml[g * ml_stride] = make_float2(st.m[g], st.l[g]);
+  }
+}
+
+template <typename T, int D, int G>
+constexpr int decode_waves_per_simd() {
+  // bf16 q.K + P.V for up to 4 heads fits 168 VGPRs (3 waves per SIMD).
+  return (sizeof(T) == 2 && (G == 4 || G == 1)) ? 3 : 2;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed partitions: one wavefront per (b, h, partition).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_partition_kernel(
+    T* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
+    const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
+  constexpr int EPV = ElemTraits<T>::kPerVec;
+  __shared__ WaveLds<T, D, G> lds[4];
+  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+  // Unit numbering: KV head fastest, then sequence, then partition in
+  // descending order, so partitions that only long sequences have start first.
   const long unit = (long)blockIdx.x * 4 + wave;
-  const int hkv = prm.num_kv_heads;
-  const int h = (int)(unit % hkv);
-  const long rest = unit / hkv;
+  const int h = (int)(unit % args.hkv);
+  const long rest = unit / args.hkv;
   const int b = (int)(rest % prm.num_seqs);
-  const int part = (int)(rest / prm.num_seqs);
-  if (part >= prm.max_parts) return;
+  const long prev = rest / prm.num_seqs;
+  if (prev >= prm.max_parts) return;
+  const int part = prm.max_parts - 1 - (int)prev;
 
   const int ctx = context_lens[b];
-  const int hq = hkv * G;
-  const int tok_begin = part * prm.part_tokens;
-  T* out_row = out_ptr + ((size_t)b * hq + (size_t)h * G) * D;
+  const size_t qh0 = (size_t)b * args.hkv * G + (size_t)h * G;
+  T* out_row = out_ptr + qh0 * D;
   if (ctx <= 0) {
     // Defined result for an empty context: a zero row (written by partition 0).
     if (part == 0) {
@@ -116,161 +381,28 @@ __global__ __launch_bounds__(256) void decode_partition_kernel(
     }
     return;
   }
+  const int tok_begin = part * prm.part_tokens;
   if (tok_begin >= ctx) return;
   const int tok_end = min(ctx, tok_begin + prm.part_tokens);
-  const bool single = (ctx <= prm.part_tokens);
-
-  const int32_t* bt = block_tables + (size_t)b * prm.max_blocks;
-  const size_t tile = (size_t)kBlockSize * D;                     // elements per (block, head) tile
-  const T* qbase = query + ((size_t)b * hq + (size_t)h * G) * D;
-
-  float m_run[G];
-  float l_lane[G];
-  float o[G][EPV];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY;
-    l_lane[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) o[g][e] = 0.f;
-  }
-
-  const int row = lane >> 4;        // block of the window this lane's K token is in
-  const int tin = lane & 15;        // token within that block
-  const int vvec = lane % VPR;      // 16-byte slice of the head dim this lane owns for V
-  const int vtok0 = lane / VPR;     // first token (within a block) this lane reads for V
-
-  for (int t0 = tok_begin; t0 < tok_end; t0 += S::kTokensPerWindow) {
-    const int lb0 = t0 / kBlockSize;
-    // Physical block of each of the window's 4 blocks (wave-uniform copies).
-    const bool row_live = (t0 + row * kBlockSize) < tok_end;
-    const int my_blk = row_live ? bt[lb0 + row] : 0;
-    int blk[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) blk[r] = __builtin_amdgcn_readlane(my_blk, r * 16);
-
-    // ---- issue K loads (lane = token) ----
-    const int tok = t0 + lane;
-    const bool kvalid = tok < tok_end;
-    Vec16 kv[VPR];
-    {
-      const T* kt = kpool + ((size_t)my_blk * hkv + h) * tile + (size_t)tin * EPV;
-#pragma unroll
-      for (int c = 0; c < VPR; ++c)
-        kv[c] = kvalid ? ld16(kt + (size_t)c * kBlockSize * EPV) : zero16();
-    }
-    // ---- issue V loads for the window's blocks ----
-    Vec16 vv[4][NVI];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int bstart = t0 + r * kBlockSize;
-      const T* vt = vpool + ((size_t)blk[r] * hkv + h) * tile + (size_t)vvec * EPV;
-#pragma unroll
-      for (int i = 0; i < NVI; ++i) {
-        const int tb = vtok0 + i * (kWave / VPR);   // token within block
-        const bool ok = (bstart + tb) < tok_end;
-        vv[r][i] = ok ? ld16(vt + (size_t)tb * D) : zero16();
-      }
-    }
-
-    // ---- q.K ----
-    float acc[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
-#pragma unroll
-    for (int c = 0; c < VPR; ++c) {
-      Vec16 qv[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) qv[g] = ld16(qbase + (size_t)g * D + (size_t)c * EPV);
-      if constexpr (EPV == 8) dot_vec_bf16<G>(acc, kv[c], qv);
-      else dot_vec_f32<G>(acc, kv[c], qv);
-    }
-
-    // ---- online softmax over the window ----
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float s = kvalid ? acc[g] * prm.scale_log2 : -INFINITY;
-      const float mw = wave_max(s);
-      const float mn = fmaxf(m_run[g], mw);
-      const float alpha = fast_exp2(m_run[g] - mn);
-      m_run[g] = mn;
-      const float p = fast_exp2(s - mn);
-      l_lane[g] = l_lane[g] * alpha + p;
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) o[g][e] *= alpha;
-      p_lds[wave][lane][g] = p;
-    }
-    wave_lds_sync();
-
-    // ---- P.V ----
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int i = 0; i < NVI; ++i) {
-        const int tb = vtok0 + i * (kWave / VPR);
-        float pv[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) pv[g] = p_lds[wave][r * kBlockSize + tb][g];
-        float vf[EPV];
-        widen<T>(vv[r][i], vf);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) o[g][e] = fmaf(pv[g], vf[e], o[g][e]);
-        }
-      }
-    }
-    wave_lds_sync();
-  }
-
-  // ---- finish the unit ----
-  float l_tot[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    l_tot[g] = wave_sum(l_lane[g]);
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) o[g][e] = sum_lanes_above<VPR>(o[g][e]);
-  }
-  if (single) {
-    if (lane < VPR) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float r[EPV];
-        const float inv = 1.0f / l_tot[g];
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) r[e] = o[g][e] * inv;
-        st16(out_row + (size_t)g * D + (size_t)vvec * EPV, narrow<T>(r));
-      }
-    }
-    return;
-  }
-  // Partial summary for the reduction: max (base 2), normalizer, unnormalized output.
-  const size_t qh0 = (size_t)b * hq + (size_t)h * G;
-  if (lane < VPR) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float* wo = ws_o + ((qh0 + g) * prm.max_parts + part) * D + (size_t)vvec * EPV;
-#pragma unroll
-      for (int e = 0; e < EPV; e += 4)
-        *reinterpret_cast<float4*>(wo + e) = make_float4(o[g][e], o[g][e + 1], o[g][e + 2], o[g][e + 3]);
-    }
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float2* wml = reinterpret_cast<float2*>(ws_ml) + (qh0 + g) * prm.max_parts + part;
-      *wml = make_float2(m_run[g], l_tot[g]);
-    }
+  const auto st = run_segment<T, D, G>(args, lds[wave], b, h, tok_begin, tok_end);
+  if (ctx <= prm.part_tokens) {
+    write_rows<T, D, G>(out_row, st);
+  } else {
+    write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + qh0 * prm.max_parts + part, prm.max_parts,
+                           ws_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st);
   }
 }
 
 // One wavefront per (sequence, query head): combine the partitions' summaries.
 //   M = max_p m_p,  L = sum_p 2^(m_p - M) l_p,  out = sum_p 2^(m_p - M) o_p / L.
+// Lanes compute 64 partitions' weights at once; the output accumulation keeps
+// 8 partitions' loads in flight.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(
     T* __restrict__ out_ptr, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ context_lens, DecodeParams prm) {
   constexpr int PER_LANE = D / kWave;
+  constexpr int UNROLL = 8;
   const int lane = threadIdx.x & 63;
   const long pair = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hq = prm.num_kv_heads * prm.group;
@@ -285,49 +417,286 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   float mx = -INFINITY;
   for (int p = lane; p < nparts; p += kWave) mx = fmaxf(mx, ml[p].x);
   mx = wave_max(mx);
+
   float lsum = 0.f;
   float acc[PER_LANE];
 #pragma unroll
   for (int j = 0; j < PER_LANE; ++j) acc[j] = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float2 s = ml[p];
-    const float w = fast_exp2(s.x - mx);
-    lsum = fmaf(w, s.y, lsum);
+  for (int p0 = 0; p0 < nparts; p0 += kWave) {
+    float wl = 0.f;
+    if (p0 + lane < nparts) {
+      const float2 sm = ml[p0 + lane];
+      wl = fast_exp2(sm.x - mx);
+      lsum = fmaf(wl, sm.y, lsum);
+    }
+    const int n = min(kWave, nparts - p0);
+    for (int j = 0; j < n; j += UNROLL) {
+      float v[UNROLL][PER_LANE];
+      float wj[UNROLL];
 #pragma unroll
-    for (int j = 0; j < PER_LANE; ++j) acc[j] = fmaf(w, wo[(size_t)p * D + j * kWave + lane], acc[j]);
+      for (int u = 0; u < UNROLL; ++u) {
+        // Past the end: reread the last partition with weight 0 (its values are finite).
+        const int pj = min(p0 + j + u, nparts - 1);
+        wj[u] = (j + u < n) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + u)) : 0.f;
+#pragma unroll
+        for (int k = 0; k < PER_LANE; ++k) v[u][k] = wo[(size_t)pj * D + k * kWave + lane];
+      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+#pragma unroll
+        for (int k = 0; k < PER_LANE; ++k) acc[k] = fmaf(wj[u], v[u][k], acc[k]);
+      }
+    }
   }
-  const float inv = 1.0f / lsum;
+  const float inv = 1.0f / wave_sum(lsum);
   T* out = out_ptr + (size_t)pair * D;
 #pragma unroll
-  for (int j = 0; j < PER_LANE; ++j) {
-    const float r = acc[j] * inv;
-    if constexpr (sizeof(T) == 2) out[j * kWave + lane] = (T)f32_to_bf16_bits(r);
-    else out[j * kWave + lane] = r;
+  for (int k = 0; k < PER_LANE; ++k) {
+    const float r = acc[k] * inv;
+    if constexpr (sizeof(T) == 2) out[k * kWave + lane] = (T)f32_to_bf16_bits(r);
+    else out[k * kWave + lane] = r;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split.
+// ---------------------------------------------------------------------------
+
+// Exclusive prefix sum over sequences of their window counts times hkv, in
+// LDS: cum[b] = first global window of sequence b, cum[B] = total windows.
+// All 256 threads of the workgroup must call it. Returns the total.
+__device__ __forceinline__ int window_prefix_sum(const int32_t* __restrict__ context_lens,
+                                                 int num_seqs, int hkv, int* cum, int* scratch) {
+  const int t = threadIdx.x;
+  const int per = (num_seqs + 255) / 256;
+  const int lo = min(num_seqs, t * per), hi = min(num_seqs, lo + per);
+  int sum = 0;
+  for (int b = lo; b < hi; ++b) sum += (max(context_lens[b], 0) + 63) / 64 * hkv;
+  scratch[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {       // inclusive Hillis-Steele scan
+    const int v = t >= off ? scratch[t - off] : 0;
+    __syncthreads();
+    scratch[t] += v;
+    __syncthreads();
+  }
+  int run = scratch[t] - sum;                     // exclusive prefix of this thread's range
+  for (int b = lo; b < hi; ++b) {
+    cum[b] = run;
+    run += (max(context_lens[b], 0) + 63) / 64 * hkv;
+  }
+  if (t == 255) cum[num_seqs] = scratch[255];
+  __syncthreads();
+  return cum[num_seqs];
+}
+
+// Largest b with cum[b] <= x (cum non-decreasing, cum[0] = 0 <= x < cum[B]).
+__device__ __forceinline__ int find_seq(const int* cum, int num_seqs, int x) {
+  int lo = 0, hi = num_seqs;                      // invariant: cum[lo] <= x < cum[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cum[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Share of wave i out of n over total windows: [i*total/n, (i+1)*total/n).
+__device__ __forceinline__ int share_begin(long i, long n, long total) { return (int)(i * total / n); }
+// The wave whose share contains window x.
+__device__ __forceinline__ int share_of(long x, long n, long total) { return (int)(((x + 1) * n - 1) / total); }
+
+// Descriptor of a partial summary slot. Every wave writes both of its slots'
+// descriptors on every call (row < 0: slot unused), so stale workspace from
+// an earlier call is never read.
+struct alignas(16) SlotDesc {
+  int row;        // b * hkv + h, or -1
+  int row_start;  // global index of the row's first window
+  int w0, w1;     // windows [w0, w1) of the row held by this slot
+  int row_windows;
+  int total;      // windows of the whole launch
+  int pad[2];
+};
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_balanced_kernel(
+    T* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
+    SlotDesc* __restrict__ ws_desc, const int32_t* __restrict__ context_lens, DecodeArgs args,
+    DecodeParams prm) {
+  __shared__ WaveLds<T, D, G> lds[4];
+  __shared__ int cum[kMaxBalancedSeqs + 1];
+  __shared__ int scan_scratch[256];
+  const int total = window_prefix_sum(context_lens, prm.num_seqs, args.hkv, cum, scan_scratch);
+
+  // Defined result for empty contexts: zero rows, spread over the workgroups.
+  constexpr int EPV = ElemTraits<T>::kPerVec;
+  const size_t seq_vecs = (size_t)args.hkv * G * D / EPV;
+  for (int b = blockIdx.x; b < prm.num_seqs; b += gridDim.x) {
+    if (cum[b + 1] != cum[b]) continue;
+    T* o = out_ptr + (size_t)b * seq_vecs * EPV;
+    for (size_t i = threadIdx.x; i < seq_vecs; i += blockDim.x) st16(o + i * EPV, zero16());
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long wid = (long)blockIdx.x * 4 + wave;
+  const long nw = prm.num_waves;
+  if (wid >= nw) return;
+  SlotDesc desc[2];
+  desc[0].row = desc[1].row = -1;
+  const int x0 = total ? share_begin(wid, nw, total) : 0;
+  const int x1 = total ? share_begin(wid + 1, nw, total) : 0;
+  int x = x0;
+  while (x < x1) {
+    // Locate (b, h, first window) of x and run to the end of that (b, h) or of the share.
+    const int b = find_seq(cum, prm.num_seqs, x);
+    const int ctx = context_lens[b];
+    const int nwb = (ctx + 63) / 64;
+    const int r = x - cum[b];
+    const int h = r / nwb;
+    const int w0 = r % nwb;
+    const int w1 = min(nwb, w0 + (x1 - x));
+    const auto st = run_segment<T, D, G>(args, lds[wave], b, h, w0 * 64, min(ctx, w1 * 64));
+    const size_t qh0 = (size_t)b * args.hkv * G + (size_t)h * G;
+    if (w0 == 0 && w1 == nwb) {
+      write_rows<T, D, G>(out_ptr + qh0 * D, st);
+    } else {
+      // Slot 0 holds the share's first segment, slot 1 its last one.
+      const int slot = (x == x0) ? 0 : 1;
+      const size_t base = ((size_t)wid * 2 + slot) * G;
+      write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st);
+      desc[slot].row = b * args.hkv + h;
+      desc[slot].row_start = x - w0;
+      desc[slot].w0 = w0;
+      desc[slot].w1 = w1;
+      desc[slot].row_windows = nwb;
+      desc[slot].total = total;
+    }
+    x += w1 - w0;
+  }
+  if (lane == 0) {
+    ws_desc[wid * 2] = desc[0];
+    ws_desc[wid * 2 + 1] = desc[1];
+  }
+}
+
+// One wavefront per partition wave i: for each split (b, h) row whose first
+// piece (w0 == 0) wave i holds, combine the pieces held by waves i..last:
+//   M = max m,  L = sum 2^(m - M) l,  out = sum 2^(m - M) o / L,  per query head.
+// Pieces after the first sit in slot 0 of each later wave with a non-empty
+// share, so the piece list follows from the share arithmetic and all loads
+// are independent.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
+    T* __restrict__ out_ptr, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+    const SlotDesc* __restrict__ ws_desc, DecodeParams prm) {
+  constexpr int PER_LANE = D / kWave;
+  const int lane = threadIdx.x & 63;
+  const long wid = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long nw = prm.num_waves;
+  if (wid >= nw) return;
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml);
+  for (int slot = 0; slot < 2; ++slot) {
+    const SlotDesc d = ws_desc[wid * 2 + slot];
+    if (d.row < 0 || d.w0 != 0) continue;
+    const int total = d.total;
+    const long last = share_of((long)d.row_start + d.row_windows - 1, nw, total);
+    // Piece k (k = 0 .. n-1) is held by wave wid + k; waves with an empty share are skipped
+    // by giving them weight 0 (their slot rows are never read).
+    float m[G], lsum[G], acc[G][PER_LANE];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      lsum[g] = 0.f;
+#pragma unroll
+      for (int k = 0; k < PER_LANE; ++k) acc[g][k] = 0.f;
+    }
+    // Pass 1: the maximum over pieces, lanes spread over pieces.
+    for (long i = wid + lane; i <= last; i += kWave) {
+      if (share_begin(i, nw, total) == share_begin(i + 1, nw, total)) continue;
+      const size_t rowi = ((size_t)i * 2 + (i == wid ? slot : 0)) * G;
+#pragma unroll
+      for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], ml[rowi + g].x);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = wave_max(m[g]);
+    // Pass 2: weighted sums; every lane walks the pieces (uniform), lanes over D.
+    for (long i = wid; i <= last; ++i) {
+      if (share_begin(i, nw, total) == share_begin(i + 1, nw, total)) continue;
+      const size_t rowi = ((size_t)i * 2 + (i == wid ? slot : 0)) * G;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float2 sm = ml[rowi + g];
+        const float w = fast_exp2(sm.x - m[g]);
+        lsum[g] = fmaf(w, sm.y, lsum[g]);
+#pragma unroll
+        for (int k = 0; k < PER_LANE; ++k)
+          acc[g][k] = fmaf(w, ws_o[(rowi + g) * D + k * kWave + lane], acc[g][k]);
+      }
+    }
+    T* out = out_ptr + (size_t)d.row * G * D;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float inv = 1.0f / lsum[g];
+#pragma unroll
+      for (int k = 0; k < PER_LANE; ++k) {
+        const float r = acc[g][k] * inv;
+        if constexpr (sizeof(T) == 2) out[(size_t)g * D + k * kWave + lane] = (T)f32_to_bf16_bits(r);
+        else out[(size_t)g * D + k * kWave + lane] = r;
+      }
+    }
   }
 }
 
 template <typename T, int D, int G>
 hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
+  const DecodeArgs args{prm.query, prm.kpool, prm.vpool, prm.block_tables, prm.num_kv_heads,
+                        prm.max_blocks, prm.scale_log2};
+  T* out = static_cast<T*>(prm.out);
+  hipError_t err;
+  if (prm.num_waves > 0) {
+    timer.begin(KernelKind::kDecodePartition, stream);
+    SlotDesc* desc = static_cast<SlotDesc*>(prm.ws_desc);
+    hipLaunchKernelGGL((decode_balanced_kernel<T, D, G>), dim3((unsigned)((prm.num_waves + 3) / 4)),
+                       dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
+    timer.end(KernelKind::kDecodePartition, stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    timer.begin(KernelKind::kDecodeReduce, stream);
+    hipLaunchKernelGGL((decode_balanced_reduce_kernel<T, D, G>), dim3((unsigned)((prm.num_waves + 3) / 4)),
+                       dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, desc, prm);
+    timer.end(KernelKind::kDecodeReduce, stream);
+    return hipGetLastError();
+  }
   const long units = (long)prm.num_kv_heads * prm.num_seqs * prm.max_parts;
-  const unsigned grid = (unsigned)((units + 3) / 4);
   timer.begin(KernelKind::kDecodePartition, stream);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), dim3(grid), dim3(256), 0, stream,
-                     static_cast<T*>(prm.out), prm.ws_ml, prm.ws_o,
-                     static_cast<const T*>(prm.query), static_cast<const T*>(prm.kpool),
-                     static_cast<const T*>(prm.vpool), prm.block_tables, prm.context_lens, prm);
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), dim3((unsigned)((units + 3) / 4)), dim3(256),
+                     0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
   timer.end(KernelKind::kDecodePartition, stream);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   if (prm.max_parts > 1) {
     const long pairs = (long)prm.num_seqs * prm.num_kv_heads * G;
     timer.begin(KernelKind::kDecodeReduce, stream);
     hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256),
-                       0, stream, static_cast<T*>(prm.out), prm.ws_ml, prm.ws_o,
-                       prm.context_lens, prm);
+                       0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, prm);
     timer.end(KernelKind::kDecodeReduce, stream);
     err = hipGetLastError();
   }
   return err;
+}
+
+template <typename T, int D, int G>
+int balanced_waves_per_cu() {
+  static int cached = 0;
+  if (cached == 0) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G>, 256, 0) !=
+            hipSuccess ||
+        blocks <= 0) {
+      (void)hipGetLastError();
+      blocks = decode_waves_per_simd<T, D, G>();
+    }
+    cached = 4 * blocks;
+  }
+  return cached;
 }
 
 template <typename T, int D>
@@ -345,7 +714,31 @@ hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream, const Ke
   }
 }
 
+template <typename T, int D>
+int waves_per_cu_t(int group) {
+  switch (group) {
+    case 1: return balanced_waves_per_cu<T, D, 1>();
+    case 2: return balanced_waves_per_cu<T, D, 2>();
+    case 3: return balanced_waves_per_cu<T, D, 3>();
+    case 4: return balanced_waves_per_cu<T, D, 4>();
+    case 5: return balanced_waves_per_cu<T, D, 5>();
+    case 6: return balanced_waves_per_cu<T, D, 6>();
+    case 7: return balanced_waves_per_cu<T, D, 7>();
+    case 8: return balanced_waves_per_cu<T, D, 8>();
+    default: return 8;
+  }
+}
+
 }  // namespace
+
+int decode_balanced_max_seqs() { return kMaxBalancedSeqs; }
+
+size_t decode_balanced_desc_bytes() { return sizeof(SlotDesc); }
+
+int decode_balanced_waves_per_cu(bool bf16, int head_dim, int group) {
+  if (bf16) return head_dim == 128 ? waves_per_cu_t<uint16_t, 128>(group) : waves_per_cu_t<uint16_t, 64>(group);
+  return head_dim == 128 ? waves_per_cu_t<float, 128>(group) : waves_per_cu_t<float, 64>(group);
+}
 
 hipError_t launch_decode(const DecodeParams& prm, bool bf16, hipStream_t stream,
                          const KernelTimer& timer) {

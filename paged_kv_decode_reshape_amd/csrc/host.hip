@@ -65,14 +65,31 @@ pkv_status check_pool_layer(const pkv_pool* pool, int layer) {
   return PKV_OK;
 }
 
-// Decode partitioning. Returns tokens per partition and the partition count of
-// the longest possible sequence.
-pkv_status decode_partitioning(const pkv_pool* pool, int num_seqs, int num_q_heads,
-                               int max_blocks_per_seq, int partition_size, int* part_tokens,
-                               int* max_parts) {
-  (void)num_seqs;
-  (void)num_q_heads;
+// Decode work split. Balanced (partition_size == 0, up to 4096 sequences):
+// the window sequence is shared equally by num_waves wavefronts, the
+// workspace holding two partial summaries per wavefront. Otherwise fixed
+// partitions of part_tokens tokens (partition_size < 0: one partition as
+// long as the longest possible sequence).
+constexpr long kBalancedWaveCap = 4096;
+
+struct DecodeSplit {
+  bool balanced = false;
+  int part_tokens = 0;
+  int max_parts = 1;
+  long wave_cap = 0;       // balanced: upper bound of num_waves (sizes the workspace)
+};
+
+pkv_status decode_split(const pkv_pool* pool, int num_seqs, int num_q_heads,
+                        int max_blocks_per_seq, int partition_size, DecodeSplit* sp) {
   const long max_ctx = (long)max_blocks_per_seq * pool->block_size;
+  const long max_windows = (long)num_seqs * pool->num_kv_heads * ((max_ctx + 63) / 64);
+  *sp = DecodeSplit{};
+  if (partition_size == 0 && num_seqs <= pkv::decode_balanced_max_seqs() &&
+      max_windows < (1L << 31)) {
+    sp->balanced = true;
+    sp->wave_cap = std::max(1L, std::min(kBalancedWaveCap, max_windows));
+    return PKV_OK;
+  }
   long p;
   if (partition_size < 0) {
     p = (max_ctx + 63) / 64 * 64;
@@ -83,11 +100,37 @@ pkv_status decode_partitioning(const pkv_pool* pool, int num_seqs, int num_q_hea
       return fail(PKV_ERR_INVALID_ARG, "partition_size %d must be a multiple of 64", partition_size);
     p = partition_size;
   }
-  if (p > (1L << 30)) p = 1L << 30;
-  if (p < 64) p = 64;
-  *part_tokens = (int)p;
-  *max_parts = (int)std::max(1L, (max_ctx + p - 1) / p);
+  (void)num_q_heads;
+  p = std::max(64L, std::min(p, 1L << 30));
+  sp->part_tokens = (int)p;
+  sp->max_parts = (int)std::max(1L, (max_ctx + p - 1) / p);
   return PKV_OK;
+}
+
+// Summary rows (one per query head and partition / wave slot) the split writes.
+size_t decode_summary_rows(const DecodeSplit& sp, int num_seqs, int num_q_heads, int group) {
+  if (sp.balanced) return (size_t)sp.wave_cap * 2 * group;
+  if (sp.max_parts <= 1) return 0;
+  return (size_t)num_seqs * num_q_heads * sp.max_parts;
+}
+
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 size_t round16(size_t x) { return (x + 15) / 16 * 16; }
@@ -217,16 +260,15 @@ pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_
   if (!bytes) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs >= 0, num_q_heads > 0 and max_blocks_per_seq > 0 required");
-  int part_tokens = 0, max_parts = 0;
-  pkv_status st = decode_partitioning(pool, num_seqs, num_q_heads, max_blocks_per_seq,
-                                      partition_size, &part_tokens, &max_parts);
+  if (num_q_heads % pool->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                num_q_heads, pool->num_kv_heads);
+  DecodeSplit sp;
+  pkv_status st = decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
   if (st != PKV_OK) return st;
-  if (max_parts <= 1) {
-    *bytes = 0;
-    return PKV_OK;
-  }
-  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
-  *bytes = round16(rows * 2 * sizeof(float)) + rows * pool->head_dim * sizeof(float);
+  const size_t rows = decode_summary_rows(sp, num_seqs, num_q_heads, num_q_heads / pool->num_kv_heads);
+  *bytes = rows == 0 ? 0 : round16(rows * 2 * sizeof(float)) + rows * pool->head_dim * sizeof(float);
+  if (sp.balanced) *bytes += (size_t)sp.wave_cap * 2 * pkv::decode_balanced_desc_bytes();
   return PKV_OK;
 }
 
@@ -252,9 +294,8 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
   if (!aligned(out, 16) || !aligned(query, 16)) return fail(PKV_ERR_INVALID_ARG, "out/query must be 16-byte aligned");
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
     return fail(PKV_ERR_INVALID_ARG, "block_tables/context_lens must be 4-byte aligned");
-  int part_tokens = 0, max_parts = 0;
-  st = decode_partitioning(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size,
-                           &part_tokens, &max_parts);
+  DecodeSplit sp;
+  st = decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
   if (st != PKV_OK) return st;
   size_t need = 0;
   st = paged_attention_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
@@ -266,18 +307,27 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
     if (workspace_bytes < need)
       return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
   }
-  const long units = (long)pool->num_kv_heads * num_seqs * max_parts;
-  if ((units + 3) / 4 >= (1L << 24)) return fail(PKV_ERR_UNSUPPORTED, "too many work units in one call");
-  const size_t rows = (size_t)num_seqs * num_q_heads * max_parts;
+  const bool bf16 = pool->dtype == PKV_BF16;
+  int num_waves = 0;
+  if (sp.balanced) {
+    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(bf16, pool->head_dim, group);
+    num_waves = (int)std::max(1L, std::min(sp.wave_cap, slots));
+  } else {
+    const long units = (long)pool->num_kv_heads * num_seqs * sp.max_parts;
+    if ((units + 3) / 4 >= (1L << 24)) return fail(PKV_ERR_UNSUPPORTED, "too many work units in one call");
+  }
+  const size_t rows = decode_summary_rows(sp, num_seqs, num_q_heads, group);
   float* ws_ml = static_cast<float*>(workspace);
   float* ws_o = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round16(rows * 2 * sizeof(float)))
                          : nullptr;
-  pkv::DecodeParams prm{out, ws_ml, ws_o, query, pool->k_layers[layer], pool->v_layers[layer],
+  void* ws_desc = sp.balanced ? static_cast<void*>(reinterpret_cast<char*>(ws_o) + rows * pool->head_dim * sizeof(float))
+                              : nullptr;
+  pkv::DecodeParams prm{out, ws_ml, ws_o, ws_desc, query, pool->k_layers[layer], pool->v_layers[layer],
                         block_tables, context_lens, num_seqs, pool->num_kv_heads, group,
-                        pool->head_dim, max_blocks_per_seq, part_tokens, max_parts,
-                        scale * 1.4426950408889634f};
+                        pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
+                        num_waves, scale * 1.4426950408889634f};
   (void)hipGetLastError();
-  hipError_t err = pkv::launch_decode(prm, pool->dtype == PKV_BF16, (hipStream_t)stream, pkv::KernelTimer{});
+  hipError_t err = pkv::launch_decode(prm, bf16, (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "paged_attention_decode launch");
   return PKV_OK;
 }

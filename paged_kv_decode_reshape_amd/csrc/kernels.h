@@ -32,6 +32,7 @@ struct DecodeParams {
   void* out;
   float* ws_ml;            // float2 [B][Hq][max_parts]: (max in base 2, normalizer)
   float* ws_o;             // float  [B][Hq][max_parts][D]: unnormalized partial output
+  void* ws_desc;           // balanced split: two slot descriptors per wave
   const void* query;
   const void* kpool;
   const void* vpool;
@@ -42,8 +43,9 @@ struct DecodeParams {
   int group;               // query heads per KV head
   int head_dim;
   int max_blocks;
-  int part_tokens;         // tokens per partition (multiple of 64)
-  int max_parts;           // partitions of the longest possible sequence
+  int part_tokens;         // fixed partitions: tokens per partition (multiple of 64)
+  int max_parts;           // fixed partitions: partitions of the longest possible sequence
+  int num_waves;           // > 0: balanced split over this many wavefronts
   float scale_log2;        // scale * log2(e)
 };
 
@@ -69,6 +71,11 @@ hipError_t launch_append(const AppendParams& prm, bool bf16, hipStream_t stream,
                          const KernelTimer& timer);
 hipError_t launch_decode(const DecodeParams& prm, bool bf16, hipStream_t stream,
                          const KernelTimer& timer);
+// Balanced decode: resident wavefronts per CU of its kernel, the largest
+// batch its in-LDS prefix sum handles, and the size of one slot descriptor.
+int decode_balanced_waves_per_cu(bool bf16, int head_dim, int group);
+int decode_balanced_max_seqs();
+size_t decode_balanced_desc_bytes();
 hipError_t launch_prefill(const PrefillParams& prm, hipStream_t stream, const KernelTimer& timer);
 
 }  // namespace pkv
