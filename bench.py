@@ -130,6 +130,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto, >= 2 GiB)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before warmup, copy this many MiB device-to-device once (a plain copy "
+                         "of known size, to scale hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -211,6 +214,13 @@ def main():
                                               len(pcl), ptotal, pmax, s.num_q_heads,
                                               pbt.shape[1], s.scale, stream)
 
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()

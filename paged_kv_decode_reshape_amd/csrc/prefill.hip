@@ -10,15 +10,18 @@
 // running maximum rescaling the accumulators ("LLM 7 - Efficient LLM
 // Serving", 2. FlashAttention, "Online Softmax Makes Tiling Possible").
 //
-// Tiling. A workgroup owns (sequence, KV head, 16 query rows) and has one
-// wavefront per query head of the GQA group, so every K/V tile is staged in
-// LDS once for all G heads. Per 64-token key tile (4 paged blocks):
+// Tiling. A workgroup owns (sequence, KV head, a tile of query rows) and has
+// one wavefront per (query head of the GQA group, 16-row sub-tile), at least
+// four, so every K/V tile is staged in LDS once for all G heads. The next
+// tile's K/V loads are issued into registers as soon as the current tile is
+// in LDS, so their latency overlaps the MFMAs. Per 64-token key tile (4
+// paged blocks):
 //   * K: the pool's (block, head) tiles are copied to LDS as they are; their
 //     layout (16-byte head-dim vectors, tokens consecutive) is exactly the
 //     B-operand fragment of v_mfma_f32_16x16x32_bf16, one ds_read_b128 each.
-//   * V: staged transposed (head dim major) so its B fragments, 8 consecutive
-//     keys of one head-dim column, are also single 16-byte reads. Keys past
-//     the context are stored as zeros.
+//   * V: copied in its natural layout; the V^T operand fragments (8 keys of
+//     one head-dim column) come from gfx950's transposing LDS read
+//     (ds_read_b64_tr_b16). Keys past the context are stored as zeros.
 //   * S = Q K^T: 4 x (D/32) MFMAs per wave, Q fragments held in registers.
 //   * mask, online softmax: a row's 16 columns of an MFMA tile sit in the 16
 //     lanes of one DPP row, so row maxima and sums are DPP row reductions.
@@ -33,7 +36,9 @@ namespace pkv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQRows = 16;          // query rows per workgroup (the MFMA M)
 constexpr int kKeyTile = 64;        // keys per tile = 4 blocks
@@ -47,63 +52,74 @@ __device__ __forceinline__ Vec16 lds_ld16(const void* p) {
   return Vec16{{v.x, v.y, v.z, v.w}};
 }
 
-template <int D>
+template <int D, int NW>
 struct alignas(16) PrefillLds {
-  static constexpr int kVtStride = kKeyTile + 8;            // bf16 elements per transposed V row
-  static constexpr int kPStride = kKeyTile + 8;             // bf16 elements per P row
-  alignas(16) uint16_t k[kKeyTile / kBlockSize][kBlockSize * D];      // K tiles in pool layout
-  alignas(16) uint16_t vt[D][kVtStride];                             // V transposed: [head dim][key]
-  alignas(16) uint16_t p[kMaxGroup][kQRows][kPStride];               // per-wave probabilities, bf16 high part
-  alignas(16) uint16_t plo[kMaxGroup][kQRows][kPStride];             // and the bf16 remainder p - high
+  // V rows padded by 32 bytes: the transposed reads of 8 consecutive keys then
+  // fall on distinct LDS banks.
+  static constexpr int kVStride = D + 16;                   // bf16 elements per V row
+  alignas(16) uint16_t k[kKeyTile / kBlockSize][kBlockSize * D];   // K tiles in pool layout
+  alignas(16) uint16_t v[kKeyTile][kVStride];                     // V tile: [key][head dim]
 };
 
-template <int D>
-__global__ __launch_bounds__(64 * kMaxGroup) void prefill_chunk_kernel(
+// Waves per workgroup for a GQA group of G heads: one per (head, 16-row
+// sub-tile), at least 4 so that K/V staging is spread over >= 256 threads.
+__host__ __device__ constexpr int prefill_row_subtiles(int g) { return (g <= 4 && 4 % g == 0) ? 4 / g : 1; }
+
+template <int D, int G>
+__global__ __launch_bounds__(64 * G * prefill_row_subtiles(G)) void prefill_chunk_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query, const uint16_t* __restrict__ kpool,
     const uint16_t* __restrict__ vpool, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     PrefillParams prm) {
+  constexpr int RT = prefill_row_subtiles(G);
+  constexpr int NW = G * RT;              // waves per workgroup
+  constexpr int NT = 64 * NW;             // threads per workgroup
   constexpr int KSTEPS = D / 32;          // MFMA k-steps over the head dim for S
   constexpr int NTILES = D / 16;          // 16-column output tiles over the head dim
   constexpr int VPR = D / 8;              // 16-byte vectors per token row
-  __shared__ PrefillLds<D> lds;
+  constexpr int kVecs = kKeyTile * VPR;   // 16-byte vectors per key tile of K (and of V)
+  constexpr int PER = (kVecs + NT - 1) / NT;   // vectors each thread stages per tile
+  __shared__ PrefillLds<D, NW> lds;
 
   const int s = blockIdx.z;
   const int h = blockIdx.y;
   const int q_lo = cu_q_lens[s];
   const int T = cu_q_lens[s + 1] - q_lo;
-  const int r0 = blockIdx.x * kQRows;     // first chunk row of this workgroup
-  if (r0 >= T) return;
+  const int r_wg = blockIdx.x * kQRows * RT;   // first chunk row of this workgroup
+  if (r_wg >= T) return;
   const int ctx = context_lens[s];
-  const int first_pos = ctx - T;          // absolute position of chunk row 0
-  const int G = prm.group;
+  const int first_pos = ctx - T;               // absolute position of chunk row 0
   const int hkv = prm.num_kv_heads;
-  const int nthreads = 64 * G;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);   // query head within the group
-  const int quad = lane >> 4;             // 0..3
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = w % G;                         // query head within the group
+  const int r0 = r_wg + (w / G) * kQRows;      // first chunk row of this wave
+  const bool wave_live = r0 < T;
+  const int quad = lane >> 4;                  // 0..3
   const int col = lane & 15;
 
-  // Key range: up to the last valid row's position.
-  const int rows_here = min(kQRows, T - r0);
-  const int kv_end = min(ctx, first_pos + r0 + rows_here);
+  // Key range of the workgroup: up to its last valid row's position.
+  const int wg_rows = min(kQRows * RT, T - r_wg);
+  const int kv_end = min(ctx, first_pos + r_wg + wg_rows);
   const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
+  // Last key this wave's rows can see (its compute stops after that tile).
+  const int wave_last_key = wave_live ? min(ctx - 1, first_pos + min(r0 + kQRows, T) - 1) : -1;
 
-  // Positions of the 4 rows this lane holds in S / O (rows 4*quad + i); rows
-  // past the chunk are clamped onto the last key so they stay finite.
-  int pos[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pos[i] = min(first_pos + r0 + 4 * quad + i, ctx - 1);
+  // This lane's query row (lane % 16 of the wave's 16 rows) and its absolute
+  // position; rows past the chunk are clamped onto the last key so they stay finite.
+  const int my_row = r0 + col;
+  const int my_pos = min(first_pos + my_row, ctx - 1);
+  // Smallest position among the wave's rows: tiles ending at or below it need no mask.
+  const int wave_first_pos = first_pos + r0;
 
-  // Q fragments (A operand): lane holds Q[row col][32k + 8*quad .. +8].
+  // Q fragments (B operand of S^T = K Q^T): lane holds Q[row col][32k + 8*quad .. +8].
   const int hq = hkv * G;
   const int qh = h * G + g;
   bf16x8 qf[KSTEPS];
   {
-    const int row = r0 + col;
-    const bool ok = row < T;
-    const uint16_t* qrow = query + ((size_t)(q_lo + (ok ? row : 0)) * hq + qh) * D;
+    const bool ok = my_row < T;
+    const uint16_t* qrow = query + ((size_t)(q_lo + (ok ? my_row : 0)) * hq + qh) * D;
 #pragma unroll
     for (int k = 0; k < KSTEPS; ++k) {
       const Vec16 v = ok ? ld16(qrow + 32 * k + 8 * quad) : zero16();
@@ -111,10 +127,10 @@ __global__ __launch_bounds__(64 * kMaxGroup) void prefill_chunk_kernel(
     }
   }
 
-  float m[4], l[4];
+  // Online softmax state of this lane's row; O^T accumulators: lane holds
+  // O^T[d = 16n + 4*quad + i][row col].
+  float m_row = -INFINITY, l_row = 0.f;
   f32x4 o[NTILES];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { m[i] = -INFINITY; l[i] = 0.f; }
 #pragma unroll
   for (int n = 0; n < NTILES; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -123,110 +139,216 @@ __global__ __launch_bounds__(64 * kMaxGroup) void prefill_chunk_kernel(
   const size_t head_off = (size_t)h * tile_elems;
   const size_t blk_stride = (size_t)hkv * tile_elems;
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int key0 = j * kKeyTile;
-    __syncthreads();   // previous tile fully consumed
-    // ---- stage K (pool layout) and V (transposed) ----
-    constexpr int kVecs = kKeyTile * VPR;                    // 16-byte vectors per tile of K (or V)
-    for (int q = tid; q < kVecs; q += nthreads) {
-      const int blk = q / (kBlockSize * VPR);                // block of the tile
-      const int within = q % (kBlockSize * VPR);
-      const int lb = key0 / kBlockSize + blk;
-      Vec16 kvv = zero16();
-      if (lb * kBlockSize < kv_end) {
-        const int phys = bt[lb];
-        kvv = ld16(kpool + (size_t)phys * blk_stride + head_off + (size_t)within * 8);
-      }
-      *reinterpret_cast<uint4*>(&lds.k[blk][within * 8]) = make_uint4(kvv.w[0], kvv.w[1], kvv.w[2], kvv.w[3]);
-    }
-    for (int q = tid; q < kVecs; q += nthreads) {
-      const int tok = q % kKeyTile;                          // consecutive lanes: consecutive keys
-      const int c = q / kKeyTile;                            // head-dim vector
-      const int key = key0 + tok;
-      Vec16 vv = zero16();
-      if (key < kv_end) {
-        const int phys = bt[key / kBlockSize];
-        vv = ld16(vpool + (size_t)phys * blk_stride + head_off + (size_t)(key % kBlockSize) * D + c * 8);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lds.vt[c * 8 + 2 * e][tok] = (uint16_t)(vv.w[e] & 0xffffu);
-        lds.vt[c * 8 + 2 * e + 1][tok] = (uint16_t)(vv.w[e] >> 16);
-      }
-    }
-    __syncthreads();
-
-    // ---- S = Q K^T: 4 column tiles (one per block) of 16 keys ----
-    f32x4 sacc[4];
+  // Register staging of one key tile: thread-strided 16-byte vectors, both
+  // copied to LDS in their pool order (coalesced reads, 16-byte LDS writes).
+  //   K vector q: block q / (16*VPR) of the tile, offset q % (16*VPR) in pool layout.
+  //   V vector q: key q / VPR, head-dim vector q % VPR.
+  // The tile's 4 block ids are wave-uniform and fetched one tile earlier than
+  // its data, so a prefetch costs one memory latency, not two.
+  Vec16 kreg[PER], vreg[PER];
+  auto tile_ids = [&](int j, int (&ids)[4]) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int lb = j * (kKeyTile / kBlockSize) + r;
+      ids[r] = (lb * kBlockSize < kv_end) ? bt[lb] : 0;
+    }
+  };
+  auto load_tile = [&](int j, const int (&ids)[4]) {
+    const int key0 = j * kKeyTile;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + u * NT;
+      kreg[u] = zero16();
+      vreg[u] = zero16();
+      if (q < kVecs) {
+        const int kb = q / (kBlockSize * VPR);
+        if (key0 + kb * kBlockSize < kv_end) {
+          const int id = kb == 0 ? ids[0] : kb == 1 ? ids[1] : kb == 2 ? ids[2] : ids[3];
+          kreg[u] = ld16(kpool + (size_t)id * blk_stride + head_off + (size_t)(q % (kBlockSize * VPR)) * 8);
+        }
+        const int tok = q / VPR;                       // consecutive lanes: consecutive 16 bytes of a row
+        if (key0 + tok < kv_end) {
+          const int vb = tok / kBlockSize;
+          const int id = vb == 0 ? ids[0] : vb == 1 ? ids[1] : vb == 2 ? ids[2] : ids[3];
+          vreg[u] = ld16(vpool + (size_t)id * blk_stride + head_off + (size_t)(tok % kBlockSize) * D +
+                         (q % VPR) * 8);
+        }
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + u * NT;
+      if (q < kVecs) {
+        const int blk = q / (kBlockSize * VPR);
+        *reinterpret_cast<uint4*>(&lds.k[blk][(q % (kBlockSize * VPR)) * 8]) =
+            make_uint4(kreg[u].w[0], kreg[u].w[1], kreg[u].w[2], kreg[u].w[3]);
+        *reinterpret_cast<uint4*>(&lds.v[q / VPR][(q % VPR) * 8]) =
+            make_uint4(vreg[u].w[0], vreg[u].w[1], vreg[u].w[2], vreg[u].w[3]);
+      }
+    }
+  };
+
+  int ids_next[4] = {0, 0, 0, 0};
+  if (ntiles > 0) {
+    int ids0[4];
+    tile_ids(0, ids0);
+    load_tile(0, ids0);
+    if (ntiles > 1) tile_ids(1, ids_next);
+  }
+  for (int j = 0; j < ntiles; ++j) {
+    const int key0 = j * kKeyTile;
+    __syncthreads();   // the previous tile is no longer read
+    store_tile();
+    __syncthreads();   // this tile is in LDS
+    if (j + 1 < ntiles) {                   // in flight during the MFMAs below
+      load_tile(j + 1, ids_next);
+      if (j + 2 < ntiles) tile_ids(j + 2, ids_next);
+    }
+    if (key0 > wave_last_key) continue;     // entirely above this wave's causal diagonal
+
+    // ---- S^T = K Q^T, one 16-key tile per block: lane holds S^T[16r + 4*quad + i][row col] ----
+    f32x4 st[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      st[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) {
         const Vec16 kf = lds_ld16(&lds.k[r][((4 * k + quad) * kBlockSize + col) * 8]);
-        sacc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[k], as_bf16x8(kf), sacc[r], 0, 0, 0);
+        st[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), qf[k], st[r], 0, 0, 0);
       }
     }
 
-    // ---- causal mask, online softmax ----
-    float alpha[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mt = -INFINITY;
+    // ---- scale, causal mask (only on tiles that reach past the wave's first row), row max ----
+    float mt = -INFINITY;
+    if (key0 + kKeyTile - 1 > wave_first_pos) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = key0 + 16 * r + col;
-        const float sv = key <= pos[i] ? sacc[r][i] * prm.scale_log2 : -INFINITY;
-        sacc[r][i] = sv;
-        mt = fmaxf(mt, sv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = key0 + 16 * r + 4 * quad + i;
+          st[r][i] = key <= my_pos ? st[r][i] * prm.scale_log2 : -INFINITY;
+          mt = fmaxf(mt, st[r][i]);
+        }
       }
-      mt = row_max(mt);
-      const float mn = fmaxf(m[i], mt);
-      alpha[i] = fast_exp2(m[i] - mn);
-      m[i] = mn;
-      float ls = 0.f;
+    } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(sacc[r][i] - mn);
-        ls += p;
-        const uint32_t hi = f32_to_bf16_bits(p);
-        lds.p[g][4 * quad + i][16 * r + col] = (uint16_t)hi;
-        lds.plo[g][4 * quad + i][16 * r + col] = (uint16_t)f32_to_bf16_bits(p - __uint_as_float(hi << 16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          st[r][i] *= prm.scale_log2;
+          mt = fmaxf(mt, st[r][i]);
+        }
       }
-      l[i] = l[i] * alpha[i] + ls;
     }
+    // The row's 64 keys sit in lanes col, col+16, col+32, col+48.
+    mt = xor32_max(xor16_max(mt));
+    const float mn = fmaxf(m_row, mt);
+    const float alpha = fast_exp2(m_row - mn);
+    m_row = mn;
+
+    // ---- P^T fragments in registers: P split into bf16 high + remainder ----
+    // B operand of O^T += V^T P^T for key half kk: k-index j of lane (quad, col)
+    // is key 32kk + 16*(j/4) + 4*quad + j%4 -- the lane's own probabilities.
+    bf16x8 phi[2], plo[2];
+    float ls = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pv[j] = fast_exp2(st[2 * kk + j / 4][j % 4] - mn);
+        ls += pv[j];
+      }
+      bf16x8 hi, lo;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const bf16x2 h2 = __builtin_convertvector(f32x2{pv[j], pv[j + 1]}, bf16x2);
+        const uint32_t hb = __builtin_bit_cast(uint32_t, h2);
+        const float r0f = pv[j] - __uint_as_float(hb << 16);
+        const float r1f = pv[j + 1] - __uint_as_float(hb & 0xffff0000u);
+        const bf16x2 l2 = __builtin_convertvector(f32x2{r0f, r1f}, bf16x2);
+        hi[j] = h2[0]; hi[j + 1] = h2[1];
+        lo[j] = l2[0]; lo[j + 1] = l2[1];
+      }
+      phi[kk] = hi;
+      plo[kk] = lo;
+    }
+    l_row = l_row * alpha + ls;
 #pragma unroll
     for (int n = 0; n < NTILES; ++n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[n][i] *= alpha[i];
+      for (int i = 0; i < 4; ++i) o[n][i] *= alpha;
     }
-    wave_lds_sync();
 
-    // ---- O += P V, with P = high + low bf16 parts (P to ~2^-17 relative) ----
+    // ---- O^T += V^T P^T ----
+    // A = V^T[d][the same 8 keys] comes from the natural V tile through the
+    // gfx950 transposing LDS read: within each 16-lane group, lane L addresses
+    // 4 head-dim values of key 32kk + 4*quad + L/4 (+16 for the second half),
+    // starting at column 16n + 4*(L%4); the hardware hands lane i those keys'
+    // values at column 16n + i.
+    const int vkey = 4 * quad + (col >> 2);
+    const int vcol = 4 * (col & 3);
 #pragma unroll
-    for (int kk = 0; kk < kKeyTile / 32; ++kk) {
-      const bf16x8 pf = as_bf16x8(lds_ld16(&lds.p[g][col][32 * kk + 8 * quad]));
-      const bf16x8 pl = as_bf16x8(lds_ld16(&lds.plo[g][col][32 * kk + 8 * quad]));
+    for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int n = 0; n < NTILES; ++n) {
-        const bf16x8 vf = as_bf16x8(lds_ld16(&lds.vt[16 * n + col][32 * kk + 8 * quad]));
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf, vf, o[n], 0, 0, 0);
-        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vf, o[n], 0, 0, 0);
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)&lds.v[32 * kk + vkey][16 * n + vcol]);
+        const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)&lds.v[32 * kk + 16 + vkey][16 * n + vcol]);
+        const bf16x8 vf = __builtin_bit_cast(
+            bf16x8, make_uint4(__builtin_bit_cast(uint2, a0).x, __builtin_bit_cast(uint2, a0).y,
+                               __builtin_bit_cast(uint2, a1).x, __builtin_bit_cast(uint2, a1).y));
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[kk], o[n], 0, 0, 0);
+        o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[kk], o[n], 0, 0, 0);
       }
     }
   }
 
-  // ---- normalize and store rows 4*quad + i, columns 16n + col ----
+  // ---- normalize and store: lane writes row col, d = 16n + 4*quad .. +4 ----
+  if (!wave_live) return;
+  const float lt = xor32_sum(xor16_sum(l_row));
+  if (my_row < T) {
+    uint16_t* orow = out + ((size_t)(q_lo + my_row) * hq + qh) * D;
+    const float inv = 1.0f / lt;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lt = row_sum(l[i]);
-    const int row = r0 + 4 * quad + i;
-    if (row < T) {
-      uint16_t* orow = out + ((size_t)(q_lo + row) * hq + qh) * D;
-      const float inv = 1.0f / lt;
-#pragma unroll
-      for (int n = 0; n < NTILES; ++n) orow[16 * n + col] = (uint16_t)f32_to_bf16_bits(o[n][i] * inv);
+    for (int n = 0; n < NTILES; ++n) {
+      const bf16x2 a2 = __builtin_convertvector(f32x2{o[n][0] * inv, o[n][1] * inv}, bf16x2);
+      const bf16x2 b2 = __builtin_convertvector(f32x2{o[n][2] * inv, o[n][3] * inv}, bf16x2);
+      *reinterpret_cast<uint2*>(orow + 16 * n + 4 * quad) =
+          make_uint2(__builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, b2));
     }
+  }
+}
+
+
+template <int D, int G>
+hipError_t launch_prefill_dg(const PrefillParams& prm, hipStream_t stream) {
+  constexpr int RT = prefill_row_subtiles(G);
+  const dim3 grid((unsigned)((prm.max_q_len + kQRows * RT - 1) / (kQRows * RT)), (unsigned)prm.num_kv_heads,
+                  (unsigned)prm.num_seqs);
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), grid, dim3(64 * G * RT), 0, stream,
+                     static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
+                     static_cast<const uint16_t*>(prm.kpool), static_cast<const uint16_t*>(prm.vpool),
+                     prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_d(const PrefillParams& prm, hipStream_t stream) {
+  switch (prm.group) {
+    case 1: return launch_prefill_dg<D, 1>(prm, stream);
+    case 2: return launch_prefill_dg<D, 2>(prm, stream);
+    case 3: return launch_prefill_dg<D, 3>(prm, stream);
+    case 4: return launch_prefill_dg<D, 4>(prm, stream);
+    case 5: return launch_prefill_dg<D, 5>(prm, stream);
+    case 6: return launch_prefill_dg<D, 6>(prm, stream);
+    case 7: return launch_prefill_dg<D, 7>(prm, stream);
+    case 8: return launch_prefill_dg<D, 8>(prm, stream);
+    default: return hipErrorNotSupported;
   }
 }
 
@@ -234,26 +356,11 @@ __global__ __launch_bounds__(64 * kMaxGroup) void prefill_chunk_kernel(
 
 hipError_t launch_prefill(const PrefillParams& prm, hipStream_t stream, const KernelTimer& timer) {
   if (prm.group < 1 || prm.group > kMaxGroup) return hipErrorNotSupported;
-  const dim3 grid((unsigned)((prm.max_q_len + kQRows - 1) / kQRows), (unsigned)prm.num_kv_heads,
-                  (unsigned)prm.num_seqs);
-  const dim3 block((unsigned)(64 * prm.group));
+  if (prm.head_dim != 64 && prm.head_dim != 128) return hipErrorNotSupported;
   timer.begin(KernelKind::kPrefill, stream);
-  if (prm.head_dim == 128) {
-    hipLaunchKernelGGL(prefill_chunk_kernel<128>, grid, block, 0, stream,
-                       static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
-                       static_cast<const uint16_t*>(prm.kpool), static_cast<const uint16_t*>(prm.vpool),
-                       prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
-  } else if (prm.head_dim == 64) {
-    hipLaunchKernelGGL(prefill_chunk_kernel<64>, grid, block, 0, stream,
-                       static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
-                       static_cast<const uint16_t*>(prm.kpool), static_cast<const uint16_t*>(prm.vpool),
-                       prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
-  } else {
-    timer.end(KernelKind::kPrefill, stream);
-    return hipErrorNotSupported;
-  }
+  const hipError_t err = prm.head_dim == 128 ? launch_prefill_d<128>(prm, stream) : launch_prefill_d<64>(prm, stream);
   timer.end(KernelKind::kPrefill, stream);
-  return hipGetLastError();
+  return err;
 }
 
 }  // namespace pkv
