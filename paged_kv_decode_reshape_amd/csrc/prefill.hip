@@ -10,24 +10,25 @@
 // running maximum rescaling the accumulators ("LLM 7 - Efficient LLM
 // Serving", 2. FlashAttention, "Online Softmax Makes Tiling Possible").
 //
-// Tiling. A workgroup owns (sequence, KV head, a tile of query rows) and has
-// one wavefront per (query head of the GQA group, 16-row sub-tile), at least
-// four, so every K/V tile is staged in LDS once for all G heads. The next
-// tile's K/V loads are issued into registers as soon as the current tile is
-// in LDS, so their latency overlaps the MFMAs. Per 64-token key tile (4
-// paged blocks):
-//   * K: the pool's (block, head) tiles are copied to LDS as they are; their
-//     layout (16-byte head-dim vectors, tokens consecutive) is exactly the
-//     B-operand fragment of v_mfma_f32_16x16x32_bf16, one ds_read_b128 each.
-//   * V: copied in its natural layout; the V^T operand fragments (8 keys of
-//     one head-dim column) come from gfx950's transposing LDS read
+// Tiling. A workgroup owns (sequence, KV head, a tile of query rows). Its
+// wavefronts form two groups; in each group there is one wavefront per (query
+// head of the GQA group, 16-row sub-tile), at least four, so every K/V tile is
+// staged in LDS once for all G heads. The groups take alternate 64-key tiles
+// (staged together), each keeping its own online-softmax state for the same
+// rows, and are merged through LDS at the end: twice the resident waves of a
+// one-group tiling. The next pair of tiles is loaded into registers while the
+// MFMAs run. Per 64-key tile (4 paged blocks):
+//   * K: the pool's (block, head) tiles are copied to LDS as they are; a
+//     16-byte head-dim vector of one key is one MFMA operand fragment.
+//   * V: copied in its natural layout; the V^T operand fragments (keys of one
+//     head-dim column) come from gfx950's transposing LDS read
 //     (ds_read_b64_tr_b16). Keys past the context are stored as zeros.
-//   * S = Q K^T: 4 x (D/32) MFMAs per wave, Q fragments held in registers.
-//   * mask, online softmax: a row's 16 columns of an MFMA tile sit in the 16
-//     lanes of one DPP row, so row maxima and sums are DPP row reductions.
-//   * P goes through LDS into the A-operand layout as two bf16 parts (high
-//     and remainder), so the product keeps ~17 bits of each weight instead of
-//     bf16's 8; O += P V takes 2 x 2 x (D/16) MFMAs. O stays in fp32 registers.
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16. In this layout a lane holds one
+//     query row and 4 keys per 16-key block, which is exactly the B fragment
+//     of O^T += V^T P^T for a fixed ordering of the reduction index, so P
+//     stays in registers. A row's maximum and sum are two permlane swaps.
+//   * P is split into bf16 high and remainder parts, so each weight keeps ~17
+//     bits in the product; O^T stays in fp32 registers.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -39,8 +40,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-constexpr int kQRows = 16;          // query rows per workgroup (the MFMA M)
+constexpr int kQRows = 16;          // query rows per wavefront (the MFMA M / N)
 constexpr int kKeyTile = 64;        // keys per tile = 4 blocks
 constexpr int kMaxGroup = 8;
 
@@ -51,35 +53,45 @@ __device__ __forceinline__ Vec16 lds_ld16(const void* p) {
   const uint4 v = *reinterpret_cast<const uint4*>(p);
   return Vec16{{v.x, v.y, v.z, v.w}};
 }
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
 
-template <int D, int NW>
-struct alignas(16) PrefillLds {
-  // V rows padded by 32 bytes: the transposed reads of 8 consecutive keys then
-  // fall on distinct LDS banks.
-  static constexpr int kVStride = D + 16;                   // bf16 elements per V row
-  alignas(16) uint16_t k[kKeyTile / kBlockSize][kBlockSize * D];   // K tiles in pool layout
-  alignas(16) uint16_t v[kKeyTile][kVStride];                     // V tile: [key][head dim]
-};
-
-// Waves per workgroup for a GQA group of G heads: one per (head, 16-row
-// sub-tile), at least 4 so that K/V staging is spread over >= 256 threads.
+// Waves per group for a GQA group of G heads: one per (head, 16-row sub-tile),
+// at least 4 so that K/V staging is spread over enough threads.
 __host__ __device__ constexpr int prefill_row_subtiles(int g) { return (g <= 4 && 4 % g == 0) ? 4 / g : 1; }
 
+template <int D, int NWG>
+union PrefillLds {
+  // V rows padded by 32 bytes: the transposed reads of 8 consecutive keys then
+  // fall on distinct LDS banks.
+  static constexpr int kVStride = D + 16;
+  struct {
+    alignas(16) uint16_t k[2][kKeyTile / kBlockSize][kBlockSize * D];   // K tiles, pool layout
+    alignas(16) uint16_t v[2][kKeyTile][kVStride];                     // V tiles, [key][head dim]
+  } tile;
+  struct {                                                              // group 1's state, at the end
+    alignas(16) float o[NWG][D / 16][4][kWave];
+    float m[NWG][kWave];
+    float l[NWG][kWave];
+  } merge;
+};
+
 template <int D, int G>
-__global__ __launch_bounds__(64 * G * prefill_row_subtiles(G)) void prefill_chunk_kernel(
+__global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chunk_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query, const uint16_t* __restrict__ kpool,
     const uint16_t* __restrict__ vpool, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     PrefillParams prm) {
   constexpr int RT = prefill_row_subtiles(G);
-  constexpr int NW = G * RT;              // waves per workgroup
-  constexpr int NT = 64 * NW;             // threads per workgroup
+  constexpr int NWG = G * RT;             // waves per group
+  constexpr int NT = 2 * 64 * NWG;        // threads per workgroup (two groups)
   constexpr int KSTEPS = D / 32;          // MFMA k-steps over the head dim for S
-  constexpr int NTILES = D / 16;          // 16-column output tiles over the head dim
+  constexpr int NTILES = D / 16;          // 16-row output tiles over the head dim
   constexpr int VPR = D / 8;              // 16-byte vectors per token row
   constexpr int kVecs = kKeyTile * VPR;   // 16-byte vectors per key tile of K (and of V)
-  constexpr int PER = (kVecs + NT - 1) / NT;   // vectors each thread stages per tile
-  __shared__ PrefillLds<D, NW> lds;
+  constexpr int PER = (2 * kVecs + NT - 1) / NT;   // vectors each thread stages per tile pair
+  __shared__ PrefillLds<D, NWG> lds;
 
   const int s = blockIdx.z;
   const int h = blockIdx.y;
@@ -93,8 +105,10 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G)) void prefill_chun
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = w % G;                         // query head within the group
-  const int r0 = r_wg + (w / G) * kQRows;      // first chunk row of this wave
+  const int grp = w / NWG;                     // 0: even key tiles, 1: odd key tiles
+  const int wl = w % NWG;                      // wave within the group
+  const int g = wl % G;                        // query head within the GQA group
+  const int r0 = r_wg + (wl / G) * kQRows;     // first chunk row of this wave
   const bool wave_live = r0 < T;
   const int quad = lane >> 4;                  // 0..3
   const int col = lane & 15;
@@ -103,6 +117,7 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G)) void prefill_chun
   const int wg_rows = min(kQRows * RT, T - r_wg);
   const int kv_end = min(ctx, first_pos + r_wg + wg_rows);
   const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
+  const int npairs = (ntiles + 1) / 2;
   // Last key this wave's rows can see (its compute stops after that tile).
   const int wave_last_key = wave_live ? min(ctx - 1, first_pos + min(r0 + kQRows, T) - 1) : -1;
 
@@ -139,83 +154,86 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G)) void prefill_chun
   const size_t head_off = (size_t)h * tile_elems;
   const size_t blk_stride = (size_t)hkv * tile_elems;
 
-  // Register staging of one key tile: thread-strided 16-byte vectors, both
-  // copied to LDS in their pool order (coalesced reads, 16-byte LDS writes).
-  //   K vector q: block q / (16*VPR) of the tile, offset q % (16*VPR) in pool layout.
-  //   V vector q: key q / VPR, head-dim vector q % VPR.
-  // The tile's 4 block ids are wave-uniform and fetched one tile earlier than
-  // its data, so a prefetch costs one memory latency, not two.
+  // Register staging of a pair of key tiles: thread-strided 16-byte vectors,
+  // copied to LDS in pool order (coalesced reads, 16-byte LDS writes).
+  //   vector q of the pair: tile t = q / kVecs, qq = q % kVecs;
+  //   K: block qq / (16*VPR) of the tile, offset qq % (16*VPR) in pool layout;
+  //   V: key qq / VPR, head-dim vector qq % VPR.
+  // Both live in block q / (16*VPR) of the pair; a block spans a multiple of
+  // 64 vectors, so that block is the same for the whole wavefront. The block
+  // ids are thus wave-uniform and fetched one pair earlier than the data, so
+  // a prefetch costs one memory latency, not two.
+  constexpr int kBlockVecs = kBlockSize * VPR;
+  static_assert(kBlockVecs % kWave == 0, "a wavefront's vectors must share a block");
+  const int wave_vec0 = w * kWave;
   Vec16 kreg[PER], vreg[PER];
-  auto tile_ids = [&](int j, int (&ids)[4]) {
+  auto pair_ids = [&](int j, int (&ids)[PER]) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int lb = j * (kKeyTile / kBlockSize) + r;
-      ids[r] = (lb * kBlockSize < kv_end) ? bt[lb] : 0;
+    for (int u = 0; u < PER; ++u) {
+      const int pb = (wave_vec0 + u * NT) / kBlockVecs;   // block of the pair, uniform
+      const int lb = j * (2 * kKeyTile / kBlockSize) + pb;
+      ids[u] = (pb < 2 * kKeyTile / kBlockSize && lb * kBlockSize < kv_end) ? bt[lb] : 0;
     }
   };
-  auto load_tile = [&](int j, const int (&ids)[4]) {
-    const int key0 = j * kKeyTile;
+  auto load_pair = [&](int j, const int (&ids)[PER]) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * NT;
       kreg[u] = zero16();
       vreg[u] = zero16();
-      if (q < kVecs) {
-        const int kb = q / (kBlockSize * VPR);
-        if (key0 + kb * kBlockSize < kv_end) {
-          const int id = kb == 0 ? ids[0] : kb == 1 ? ids[1] : kb == 2 ? ids[2] : ids[3];
-          kreg[u] = ld16(kpool + (size_t)id * blk_stride + head_off + (size_t)(q % (kBlockSize * VPR)) * 8);
-        }
-        const int tok = q / VPR;                       // consecutive lanes: consecutive 16 bytes of a row
-        if (key0 + tok < kv_end) {
-          const int vb = tok / kBlockSize;
-          const int id = vb == 0 ? ids[0] : vb == 1 ? ids[1] : vb == 2 ? ids[2] : ids[3];
-          vreg[u] = ld16(vpool + (size_t)id * blk_stride + head_off + (size_t)(tok % kBlockSize) * D +
-                         (q % VPR) * 8);
-        }
+      if (q < 2 * kVecs) {
+        const int qq = q % kVecs;
+        const int key0 = j * 2 * kKeyTile + (q / kBlockVecs) * kBlockSize;   // first key of the block
+        const size_t base = (size_t)ids[u] * blk_stride + head_off;
+        if (key0 < kv_end) kreg[u] = ld16(kpool + base + (size_t)(qq % kBlockVecs) * 8);
+        const int tok = qq / VPR;
+        if (key0 + tok % kBlockSize < kv_end)
+          vreg[u] = ld16(vpool + base + (size_t)(tok % kBlockSize) * D + (qq % VPR) * 8);
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_pair = [&]() {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int q = tid + u * NT;
-      if (q < kVecs) {
-        const int blk = q / (kBlockSize * VPR);
-        *reinterpret_cast<uint4*>(&lds.k[blk][(q % (kBlockSize * VPR)) * 8]) =
+      if (q < 2 * kVecs) {
+        const int t = q / kVecs, qq = q % kVecs;
+        *reinterpret_cast<uint4*>(&lds.tile.k[t][qq / (kBlockSize * VPR)][(qq % (kBlockSize * VPR)) * 8]) =
             make_uint4(kreg[u].w[0], kreg[u].w[1], kreg[u].w[2], kreg[u].w[3]);
-        *reinterpret_cast<uint4*>(&lds.v[q / VPR][(q % VPR) * 8]) =
+        *reinterpret_cast<uint4*>(&lds.tile.v[t][qq / VPR][(qq % VPR) * 8]) =
             make_uint4(vreg[u].w[0], vreg[u].w[1], vreg[u].w[2], vreg[u].w[3]);
       }
     }
   };
 
-  int ids_next[4] = {0, 0, 0, 0};
-  if (ntiles > 0) {
-    int ids0[4];
-    tile_ids(0, ids0);
-    load_tile(0, ids0);
-    if (ntiles > 1) tile_ids(1, ids_next);
+  int ids_next[PER] = {};
+  if (npairs > 0) {
+    int ids0[PER];
+    pair_ids(0, ids0);
+    load_pair(0, ids0);
+    if (npairs > 1) pair_ids(1, ids_next);
   }
-  for (int j = 0; j < ntiles; ++j) {
-    const int key0 = j * kKeyTile;
-    __syncthreads();   // the previous tile is no longer read
-    store_tile();
-    __syncthreads();   // this tile is in LDS
-    if (j + 1 < ntiles) {                   // in flight during the MFMAs below
-      load_tile(j + 1, ids_next);
-      if (j + 2 < ntiles) tile_ids(j + 2, ids_next);
+  const int vkey = 4 * quad + (col >> 2);   // transposed V read: key offset and column of this lane
+  const int vcol = 4 * (col & 3);
+  for (int j = 0; j < npairs; ++j) {
+    __syncthreads();   // the previous pair is no longer read
+    store_pair();
+    __syncthreads();   // this pair is in LDS
+    if (j + 1 < npairs) {                   // in flight during the MFMAs below
+      load_pair(j + 1, ids_next);
+      if (j + 2 < npairs) pair_ids(j + 2, ids_next);
     }
-    if (key0 > wave_last_key) continue;     // entirely above this wave's causal diagonal
+    const int key0 = (2 * j + grp) * kKeyTile;
+    if (key0 >= kv_end || key0 > wave_last_key) continue;   // past the range or the causal diagonal
 
-    // ---- S^T = K Q^T, one 16-key tile per block: lane holds S^T[16r + 4*quad + i][row col] ----
+    // ---- S^T = K Q^T, one 16-key block per MFMA tile: lane holds S^T[16r + 4*quad + i][row col] ----
     f32x4 st[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       st[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) {
-        const Vec16 kf = lds_ld16(&lds.k[r][((4 * k + quad) * kBlockSize + col) * 8]);
+        const Vec16 kf = lds_ld16(&lds.tile.k[grp][r][((4 * k + quad) * kBlockSize + col) * 8]);
         st[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), qf[k], st[r], 0, 0, 0);
       }
     }
@@ -244,8 +262,11 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G)) void prefill_chun
     }
     // The row's 64 keys sit in lanes col, col+16, col+32, col+48.
     mt = xor32_max(xor16_max(mt));
+    // Group 1 starts at tile 1, which can lie wholly past a row's position:
+    // then the row has seen no key yet and its maximum is still -inf.
     const float mn = fmaxf(m_row, mt);
-    const float alpha = fast_exp2(m_row - mn);
+    const float msub = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(m_row - msub);
     m_row = mn;
 
     // ---- P^T fragments in registers: P split into bf16 high + remainder ----
@@ -255,25 +276,18 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G)) void prefill_chun
     float ls = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      float pv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        pv[j] = fast_exp2(st[2 * kk + j / 4][j % 4] - mn);
-        ls += pv[j];
-      }
-      bf16x8 hi, lo;
+      uint32_t hw[4], lw[4];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const bf16x2 h2 = __builtin_convertvector(f32x2{pv[j], pv[j + 1]}, bf16x2);
-        const uint32_t hb = __builtin_bit_cast(uint32_t, h2);
-        const float r0f = pv[j] - __uint_as_float(hb << 16);
-        const float r1f = pv[j + 1] - __uint_as_float(hb & 0xffff0000u);
-        const bf16x2 l2 = __builtin_convertvector(f32x2{r0f, r1f}, bf16x2);
-        hi[j] = h2[0]; hi[j + 1] = h2[1];
-        lo[j] = l2[0]; lo[j + 1] = l2[1];
+        const float p0 = fast_exp2(st[2 * kk + j / 4][j % 4] - msub);
+        const float p1 = fast_exp2(st[2 * kk + j / 4][j % 4 + 1] - msub);
+        ls += p0 + p1;
+        const uint32_t hb = pack_bf16x2(p0, p1);
+        hw[j / 2] = hb;
+        lw[j / 2] = pack_bf16x2(p0 - __uint_as_float(hb << 16), p1 - __uint_as_float(hb & 0xffff0000u));
       }
-      phi[kk] = hi;
-      plo[kk] = lo;
+      phi[kk] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+      plo[kk] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
     }
     l_row = l_row * alpha + ls;
 #pragma unroll
@@ -284,53 +298,65 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G)) void prefill_chun
 
     // ---- O^T += V^T P^T ----
     // A = V^T[d][the same 8 keys] comes from the natural V tile through the
-    // gfx950 transposing LDS read: within each 16-lane group, lane L addresses
-    // 4 head-dim values of key 32kk + 4*quad + L/4 (+16 for the second half),
+    // transposing LDS read: within each 16-lane group, lane L addresses 4
+    // head-dim values of key 32kk + 4*quad + L/4 (+16 for the second half),
     // starting at column 16n + 4*(L%4); the hardware hands lane i those keys'
     // values at column 16n + i.
-    const int vkey = 4 * quad + (col >> 2);
-    const int vcol = 4 * (col & 3);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int n = 0; n < NTILES; ++n) {
-        typedef short v4i16 __attribute__((ext_vector_type(4)));
         const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)&lds.v[32 * kk + vkey][16 * n + vcol]);
+            (__attribute__((address_space(3))) v4i16*)&lds.tile.v[grp][32 * kk + vkey][16 * n + vcol]);
         const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)&lds.v[32 * kk + 16 + vkey][16 * n + vcol]);
-        const bf16x8 vf = __builtin_bit_cast(
-            bf16x8, make_uint4(__builtin_bit_cast(uint2, a0).x, __builtin_bit_cast(uint2, a0).y,
-                               __builtin_bit_cast(uint2, a1).x, __builtin_bit_cast(uint2, a1).y));
+            (__attribute__((address_space(3))) v4i16*)&lds.tile.v[grp][32 * kk + 16 + vkey][16 * n + vcol]);
+        const uint2 u0 = __builtin_bit_cast(uint2, a0), u1 = __builtin_bit_cast(uint2, a1);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, make_uint4(u0.x, u0.y, u1.x, u1.y));
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[kk], o[n], 0, 0, 0);
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[kk], o[n], 0, 0, 0);
       }
     }
   }
 
+  // ---- merge the two groups' summaries of the same rows (online-softmax rule) ----
+  __syncthreads();   // tiles are no longer read; the LDS becomes the merge area
+  if (grp == 1) {
+#pragma unroll
+    for (int n = 0; n < NTILES; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds.merge.o[wl][n][i][lane] = o[n][i];
+    }
+    lds.merge.m[wl][lane] = m_row;
+    lds.merge.l[wl][lane] = l_row;
+  }
+  __syncthreads();
+  if (grp == 1 || !wave_live) return;
+  // Group 0 always holds tile 0 (key 0 is visible to every row), so m_row is finite.
+  const float m1 = lds.merge.m[wl][lane];
+  const float mx = fmaxf(m_row, m1);
+  const float w0 = fast_exp2(m_row - mx), w1 = fast_exp2(m1 - mx);
+  const float lt = xor32_sum(xor16_sum(l_row * w0 + lds.merge.l[wl][lane] * w1));
+
   // ---- normalize and store: lane writes row col, d = 16n + 4*quad .. +4 ----
-  if (!wave_live) return;
-  const float lt = xor32_sum(xor16_sum(l_row));
   if (my_row < T) {
     uint16_t* orow = out + ((size_t)(q_lo + my_row) * hq + qh) * D;
     const float inv = 1.0f / lt;
 #pragma unroll
     for (int n = 0; n < NTILES; ++n) {
-      const bf16x2 a2 = __builtin_convertvector(f32x2{o[n][0] * inv, o[n][1] * inv}, bf16x2);
-      const bf16x2 b2 = __builtin_convertvector(f32x2{o[n][2] * inv, o[n][3] * inv}, bf16x2);
-      *reinterpret_cast<uint2*>(orow + 16 * n + 4 * quad) =
-          make_uint2(__builtin_bit_cast(uint32_t, a2), __builtin_bit_cast(uint32_t, b2));
+      float r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = (o[n][i] * w0 + lds.merge.o[wl][n][i][lane] * w1) * inv;
+      *reinterpret_cast<uint2*>(orow + 16 * n + 4 * quad) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
     }
   }
 }
-
 
 template <int D, int G>
 hipError_t launch_prefill_dg(const PrefillParams& prm, hipStream_t stream) {
   constexpr int RT = prefill_row_subtiles(G);
   const dim3 grid((unsigned)((prm.max_q_len + kQRows * RT - 1) / (kQRows * RT)), (unsigned)prm.num_kv_heads,
                   (unsigned)prm.num_seqs);
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), grid, dim3(64 * G * RT), 0, stream,
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), grid, dim3(128 * G * RT), 0, stream,
                      static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
                      static_cast<const uint16_t*>(prm.kpool), static_cast<const uint16_t*>(prm.vpool),
                      prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
