@@ -208,7 +208,7 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
     for (int c0 = 0; c0 < VPR; c0 += KG) {
       Vec16 kv[KG];
 #pragma unroll
-      for (int c = 0; c < KG; ++c) kv[c] = ld16(kt + (c0 + c) * (kBlockSize * 16));
+      for (int c = 0; c < KG; ++c) kv[c] = ld16_stream(kt + (c0 + c) * (kBlockSize * 16));
       Vec16 qcur[G], qnext[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) qcur[g] = lds.q[g][c0 + qz];
@@ -258,7 +258,7 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
       for (int r = 0; r < VB; ++r) {
         const char* vt = reinterpret_cast<const char*>(vpool + (size_t)bid[r0 + r] * blk_stride + head_off);
 #pragma unroll
-        for (int i = 0; i < NVI; ++i) vv[r][i] = ld16(vt + voff + i * ((kWave / VPR) * D * (int)sizeof(T)));
+        for (int i = 0; i < NVI; ++i) vv[r][i] = ld16_stream(vt + voff + i * ((kWave / VPR) * D * (int)sizeof(T)));
       }
       if (partial) {
         // Last, partial window: tokens past the end may hold anything (even
