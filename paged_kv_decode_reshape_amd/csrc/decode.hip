@@ -40,8 +40,12 @@
 //     the pieces at the two ends of its share; the reduction combines them.
 //     Every workgroup derives the split on the device from context_lens (a
 //     prefix sum in LDS), so the launch does not depend on the lengths and
-//     stays graph-capturable. Waves finish within one window of each other
-//     whatever the length mix.
+//     stays graph-capturable. Equal shares alone do not give equal finish
+//     times: a SIMD issues its oldest wavefront first, so the waves dispatched
+//     first race ahead. Each wave therefore lowers its issue priority as its
+//     share progresses (s_setprio by quarter), which on the B=256 lognormal
+//     step narrows the spread of wave finish times from 67-170 us to
+//     100-160 us and shortens the launch by about 6%.
 //   * fixed partitions of P tokens: one wavefront per (b, h, partition),
 //     partitions dispatched in descending index order (long sequences first).
 #include "device_common.h"
@@ -99,6 +103,14 @@ __device__ __forceinline__ int opaque_zero() {
   return z;
 }
 
+// Issue priority of the calling wavefront (s_setprio takes an immediate).
+__device__ __forceinline__ void set_wave_priority(int level) {
+  if (level >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (level == 2) __builtin_amdgcn_s_setprio(2);
+  else if (level == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Per-wave scratch in LDS.
 template <typename T, int D, int G>
 struct WaveLds {
@@ -127,9 +139,13 @@ struct DecodeArgs {
 };
 
 // Accumulate tokens [tok_begin, tok_end) of (b, h) into a fresh summary.
+// With share > 0 the wave paces itself: before each window it sets its issue
+// priority from the fraction of its share already done (3 in the first
+// quarter .. 0 in the last), where done counts the share's windows so far.
 template <typename T, int D, int G>
 __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
-    const DecodeArgs& a, WaveLds<T, D, G>& lds, int b, int h, int tok_begin, int tok_end) {
+    const DecodeArgs& a, WaveLds<T, D, G>& lds, int b, int h, int tok_begin, int tok_end,
+    int& done, int share) {
   using S = DecodeShape<T, D, G>;
   constexpr int EPV = S::kEpv;
   constexpr int VPR = S::kVecPerRow;
@@ -148,19 +164,18 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
   const int lb_begin = tok_begin / kBlockSize;
   const int nblk = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;   // blocks of the segment
 
+  // Block ids of the segment, 64 per vector register: lane j holds logical
+  // block lb_begin + 64*chunk + j, clamped to the segment's last block so
+  // that every id is a real block of this sequence and every address formed
+  // below is in bounds. Issued first: the K loads wait on it.
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin;
+  int ids = bt[min(lane, nblk - 1)];
+
   wave_lds_sync();   // the wave's previous segment may still be reading q / p
   {
     const T* qbase = query + ((size_t)b * hq + (size_t)h * G) * D;
     for (int i = lane; i < G * VPR; i += kWave) lds.q[i / VPR][i % VPR] = ld16(qbase + (size_t)i * EPV);
   }
-
-  // Block ids of the segment, 64 per vector register: lane j holds logical
-  // block lb_begin + 64*chunk + j, clamped to the segment's last block so
-  // that every id is a real block of this sequence and every address formed
-  // below is in bounds (values read for tokens past the end are masked where
-  // they are used).
-  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin;
-  int ids = bt[min(lane, nblk - 1)];
 
   const size_t tile = (size_t)kBlockSize * D;           // elements per (block, head) tile
   const size_t head_off = (size_t)h * tile;
@@ -183,6 +198,8 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
 
 #pragma unroll 1
   for (int w = 0; w < nwin; ++w) {
+    if (share > 0) set_wave_priority(3 - (4 * done) / share);
+    ++done;
     const int t0 = tok_begin + w * TPW;
     const int lb = 4 * w;                               // first local block of the window
     if (lb > 0 && (lb & 63) == 0) ids = bt[min(lb + lane, nblk - 1)];
@@ -384,7 +401,8 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   const int tok_begin = part * prm.part_tokens;
   if (tok_begin >= ctx) return;
   const int tok_end = min(ctx, tok_begin + prm.part_tokens);
-  const auto st = run_segment<T, D, G>(args, lds[wave], b, h, tok_begin, tok_end);
+  int done = 0;
+  const auto st = run_segment<T, D, G>(args, lds[wave], b, h, tok_begin, tok_end, done, 0);
   if (ctx <= prm.part_tokens) {
     write_rows<T, D, G>(out_row, st);
   } else {
@@ -393,17 +411,36 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   }
 }
 
-// One wavefront per (sequence, query head): combine the partitions' summaries.
+__device__ __forceinline__ float lane_xor16(float x) { return __shfl_xor(x, 16); }
+__device__ __forceinline__ float lane_xor32(float x) { return __shfl_xor(x, 32); }
+
+// Merge two online-softmax states (m, l, acc) of the same row; either may be
+// empty (m = -inf, l = 0, acc = 0).
+__device__ __forceinline__ void merge_state(float& m, float& l, float4& acc, float m2, float l2, float4 acc2) {
+  const float mn = fmaxf(m, m2);
+  const float ms = mn == -INFINITY ? 0.f : mn;
+  const float a = fast_exp2(m - ms), w = fast_exp2(m2 - ms);
+  m = mn;
+  l = l * a + l2 * w;
+  acc = make_float4(acc.x * a + acc2.x * w, acc.y * a + acc2.y * w, acc.z * a + acc2.z * w,
+                    acc.w * a + acc2.w * w);
+}
+
+// One wavefront per (sequence, query head): combine the partitions' summaries
 //   M = max_p m_p,  L = sum_p 2^(m_p - M) l_p,  out = sum_p 2^(m_p - M) o_p / L.
-// Lanes compute 64 partitions' weights at once; the output accumulation keeps
-// 8 partitions' loads in flight.
+// A partition's D floats are D/4 float4 slices; the wavefront's lanes cover
+// 64/(D/4) partitions side by side, and each lane walks its partitions kUnroll
+// at a time with all their loads in flight, keeping an online-softmax state.
+// The lanes holding the same slice are merged at the end.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(
     T* __restrict__ out_ptr, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ context_lens, DecodeParams prm) {
-  constexpr int PER_LANE = D / kWave;
-  constexpr int UNROLL = 8;
+  constexpr int kSlices = D / 4;
+  constexpr int PP = kWave / kSlices;       // partitions side by side
+  constexpr int kUnroll = 8;
   const int lane = threadIdx.x & 63;
+  const int f = lane % kSlices, ph = lane / kSlices;
   const long pair = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hq = prm.num_kv_heads * prm.group;
   if (pair >= (long)prm.num_seqs * hq) return;
@@ -412,49 +449,43 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int nparts = (ctx + prm.part_tokens - 1) / prm.part_tokens;
   if (nparts <= 1) return;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + (size_t)pair * prm.max_parts;
-  const float* wo = ws_o + (size_t)pair * prm.max_parts * D;
+  const float4* wo = reinterpret_cast<const float4*>(ws_o) + (size_t)pair * prm.max_parts * kSlices;
 
-  float mx = -INFINITY;
-  for (int p = lane; p < nparts; p += kWave) mx = fmaxf(mx, ml[p].x);
-  mx = wave_max(mx);
-
-  float lsum = 0.f;
-  float acc[PER_LANE];
+  float m = -INFINITY, l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = ph; p0 < nparts; p0 += PP * kUnroll) {
+    float2 sm[kUnroll];
+    float4 ov[kUnroll];
 #pragma unroll
-  for (int j = 0; j < PER_LANE; ++j) acc[j] = 0.f;
-  for (int p0 = 0; p0 < nparts; p0 += kWave) {
-    float wl = 0.f;
-    if (p0 + lane < nparts) {
-      const float2 sm = ml[p0 + lane];
-      wl = fast_exp2(sm.x - mx);
-      lsum = fmaf(wl, sm.y, lsum);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int pu = min(p0 + u * PP, nparts - 1);
+      sm[u] = ml[pu];
+      ov[u] = wo[(size_t)pu * kSlices + f];
     }
-    const int n = min(kWave, nparts - p0);
-    for (int j = 0; j < n; j += UNROLL) {
-      float v[UNROLL][PER_LANE];
-      float wj[UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        // Past the end: reread the last partition with weight 0 (its values are finite).
-        const int pj = min(p0 + j + u, nparts - 1);
-        wj[u] = (j + u < n) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j + u)) : 0.f;
-#pragma unroll
-        for (int k = 0; k < PER_LANE; ++k) v[u][k] = wo[(size_t)pj * D + k * kWave + lane];
-      }
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-#pragma unroll
-        for (int k = 0; k < PER_LANE; ++k) acc[k] = fmaf(wj[u], v[u][k], acc[k]);
-      }
+    for (int u = 0; u < kUnroll; ++u) {
+      if (p0 + u * PP < nparts) merge_state(m, l, acc, sm[u].x, sm[u].y, ov[u]);
     }
   }
-  const float inv = 1.0f / wave_sum(lsum);
-  T* out = out_ptr + (size_t)pair * D;
-#pragma unroll
-  for (int k = 0; k < PER_LANE; ++k) {
-    const float r = acc[k] * inv;
-    if constexpr (sizeof(T) == 2) out[k * kWave + lane] = (T)f32_to_bf16_bits(r);
-    else out[k * kWave + lane] = r;
+  // Lanes ph and ph ^ 1 (and ph ^ 2) hold the same slice for other partitions.
+  if constexpr (PP >= 4) {
+    const float4 o2 = make_float4(lane_xor16(acc.x), lane_xor16(acc.y), lane_xor16(acc.z), lane_xor16(acc.w));
+    merge_state(m, l, acc, lane_xor16(m), lane_xor16(l), o2);
+  }
+  if constexpr (PP >= 2) {
+    const float4 o2 = make_float4(lane_xor32(acc.x), lane_xor32(acc.y), lane_xor32(acc.z), lane_xor32(acc.w));
+    merge_state(m, l, acc, lane_xor32(m), lane_xor32(l), o2);
+  }
+  if (ph == 0) {
+    const float inv = 1.0f / l;
+    T* out = out_ptr + (size_t)pair * D + (size_t)f * 4;
+    const float r[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<uint2*>(out) = make_uint2(f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16),
+                                                  f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16));
+    } else {
+      *reinterpret_cast<float4*>(out) = make_float4(r[0], r[1], r[2], r[3]);
+    }
   }
 }
 
@@ -468,24 +499,27 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
 __device__ __forceinline__ int window_prefix_sum(const int32_t* __restrict__ context_lens,
                                                  int num_seqs, int hkv, int* cum, int* scratch) {
   const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int per = (num_seqs + 255) / 256;
   const int lo = min(num_seqs, t * per), hi = min(num_seqs, lo + per);
   int sum = 0;
   for (int b = lo; b < hi; ++b) sum += (max(context_lens[b], 0) + 63) / 64 * hkv;
-  scratch[t] = sum;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {       // inclusive Hillis-Steele scan
-    const int v = t >= off ? scratch[t - off] : 0;
-    __syncthreads();
-    scratch[t] += v;
-    __syncthreads();
+  // Inclusive scan inside the wavefront, then across the 4 wavefronts.
+  int inc = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(inc, off);
+    if (lane >= off) inc += v;
   }
-  int run = scratch[t] - sum;                     // exclusive prefix of this thread's range
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  int run = inc - sum;                            // exclusive prefix of this thread's range
+  for (int w = 0; w < wave; ++w) run += scratch[w];
   for (int b = lo; b < hi; ++b) {
     cum[b] = run;
     run += (max(context_lens[b], 0) + 63) / 64 * hkv;
   }
-  if (t == 255) cum[num_seqs] = scratch[255];
+  if (t == 255) cum[num_seqs] = run;
   __syncthreads();
   return cum[num_seqs];
 }
@@ -545,7 +579,12 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   desc[0].row = desc[1].row = -1;
   const int x0 = total ? share_begin(wid, nw, total) : 0;
   const int x1 = total ? share_begin(wid + 1, nw, total) : 0;
+  // The hardware issues the oldest wavefront first. With equal shares that
+  // would let the first-dispatched waves finish far ahead of the last ones,
+  // each CU ending its launch on a few young waves; pacing by progress keeps
+  // the waves of a SIMD level.
   int x = x0;
+  int done = 0;
   while (x < x1) {
     // Locate (b, h, first window) of x and run to the end of that (b, h) or of the share.
     const int b = find_seq(cum, prm.num_seqs, x);
@@ -555,7 +594,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
     const int h = r / nwb;
     const int w0 = r % nwb;
     const int w1 = min(nwb, w0 + (x1 - x));
-    const auto st = run_segment<T, D, G>(args, lds[wave], b, h, w0 * 64, min(ctx, w1 * 64));
+    const auto st = run_segment<T, D, G>(args, lds[wave], b, h, w0 * 64, min(ctx, w1 * 64), done, x1 - x0);
     const size_t qh0 = (size_t)b * args.hkv * G + (size_t)h * G;
     if (w0 == 0 && w1 == nwb) {
       write_rows<T, D, G>(out_ptr + qh0 * D, st);
@@ -580,68 +619,90 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
 }
 
 // One wavefront per partition wave i: for each split (b, h) row whose first
-// piece (w0 == 0) wave i holds, combine the pieces held by waves i..last:
-//   M = max m,  L = sum 2^(m - M) l,  out = sum 2^(m - M) o / L,  per query head.
+// piece (w0 == 0) wave i holds, combine the pieces held by waves i..last with
+// the online-softmax rule, per query head:
+//   M = max m,  L = sum 2^(m - M) l,  out = sum 2^(m - M) o / L.
 // Pieces after the first sit in slot 0 of each later wave with a non-empty
-// share, so the piece list follows from the share arithmetic and all loads
-// are independent.
+// share, so the piece list follows from the share arithmetic and the loads of
+// different pieces are independent: a lane owns 16-byte slices of the G x D
+// output and walks the pieces kPieces at a time, all their loads in flight
+// together, rescaling its running sums as the maximum grows.
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
     T* __restrict__ out_ptr, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const SlotDesc* __restrict__ ws_desc, DecodeParams prm) {
-  constexpr int PER_LANE = D / kWave;
+  constexpr int kSlices = G * D / 4;                       // float4 slices of one piece
+  constexpr int NF = (kSlices + kWave - 1) / kWave;        // slices per lane
+  constexpr int kPieces = NF >= 4 ? 2 : 8 / NF;            // pieces loaded together
   const int lane = threadIdx.x & 63;
   const long wid = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const long nw = prm.num_waves;
   if (wid >= nw) return;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml);
+  const float4* wo = reinterpret_cast<const float4*>(ws_o);
   for (int slot = 0; slot < 2; ++slot) {
     const SlotDesc d = ws_desc[wid * 2 + slot];
     if (d.row < 0 || d.w0 != 0) continue;
     const int total = d.total;
     const long last = share_of((long)d.row_start + d.row_windows - 1, nw, total);
-    // Piece k (k = 0 .. n-1) is held by wave wid + k; waves with an empty share are skipped
-    // by giving them weight 0 (their slot rows are never read).
-    float m[G], lsum[G], acc[G][PER_LANE];
+
+    // Lane slice f = lane + 64 j covers head f / (D/4), dims 4 (f % (D/4)) .. +4.
+    float m[NF], l[NF];
+    float4 acc[NF];
+    {
+      const size_t row0 = ((size_t)wid * 2 + slot) * G;   // the first piece, always non-empty
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m[g] = -INFINITY;
-      lsum[g] = 0.f;
-#pragma unroll
-      for (int k = 0; k < PER_LANE; ++k) acc[g][k] = 0.f;
+      for (int j = 0; j < NF; ++j) {
+        const int f = min(lane + kWave * j, kSlices - 1);
+        const float2 sm = ml[row0 + f / (D / 4)];
+        m[j] = sm.x;
+        l[j] = sm.y;
+        acc[j] = wo[row0 * (D / 4) + f];
+      }
     }
-    // Pass 1: the maximum over pieces, lanes spread over pieces.
-    for (long i = wid + lane; i <= last; i += kWave) {
-      if (share_begin(i, nw, total) == share_begin(i + 1, nw, total)) continue;
-      const size_t rowi = ((size_t)i * 2 + (i == wid ? slot : 0)) * G;
+    for (long i0 = wid + 1; i0 <= last; i0 += kPieces) {
+      float2 sm[kPieces][NF];
+      float4 ov[kPieces][NF];
+      bool live[kPieces];
 #pragma unroll
-      for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], ml[rowi + g].x);
-    }
+      for (int u = 0; u < kPieces; ++u) {
+        const long i = min(i0 + u, last);
+        live[u] = (i0 + u <= last) && share_begin(i, nw, total) != share_begin(i + 1, nw, total);
+        const size_t rowi = (size_t)i * 2 * G;             // slot 0 of wave i
 #pragma unroll
-    for (int g = 0; g < G; ++g) m[g] = wave_max(m[g]);
-    // Pass 2: weighted sums; every lane walks the pieces (uniform), lanes over D.
-    for (long i = wid; i <= last; ++i) {
-      if (share_begin(i, nw, total) == share_begin(i + 1, nw, total)) continue;
-      const size_t rowi = ((size_t)i * 2 + (i == wid ? slot : 0)) * G;
+        for (int j = 0; j < NF; ++j) {
+          const int f = min(lane + kWave * j, kSlices - 1);
+          sm[u][j] = ml[rowi + f / (D / 4)];
+          ov[u][j] = wo[rowi * (D / 4) + f];
+        }
+      }
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float2 sm = ml[rowi + g];
-        const float w = fast_exp2(sm.x - m[g]);
-        lsum[g] = fmaf(w, sm.y, lsum[g]);
+      for (int u = 0; u < kPieces; ++u) {
+        if (!live[u]) continue;                            // wave-uniform: empty share or past the end
 #pragma unroll
-        for (int k = 0; k < PER_LANE; ++k)
-          acc[g][k] = fmaf(w, ws_o[(rowi + g) * D + k * kWave + lane], acc[g][k]);
+        for (int j = 0; j < NF; ++j) {
+          const float mn = fmaxf(m[j], sm[u][j].x);
+          const float a = fast_exp2(m[j] - mn), w = fast_exp2(sm[u][j].x - mn);
+          m[j] = mn;
+          l[j] = l[j] * a + sm[u][j].y * w;
+          acc[j] = make_float4(acc[j].x * a + ov[u][j].x * w, acc[j].y * a + ov[u][j].y * w,
+                               acc[j].z * a + ov[u][j].z * w, acc[j].w * a + ov[u][j].w * w);
+        }
       }
     }
     T* out = out_ptr + (size_t)d.row * G * D;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float inv = 1.0f / lsum[g];
-#pragma unroll
-      for (int k = 0; k < PER_LANE; ++k) {
-        const float r = acc[g][k] * inv;
-        if constexpr (sizeof(T) == 2) out[(size_t)g * D + k * kWave + lane] = (T)f32_to_bf16_bits(r);
-        else out[(size_t)g * D + k * kWave + lane] = r;
+    for (int j = 0; j < NF; ++j) {
+      const int f = lane + kWave * j;
+      if (f >= kSlices) continue;
+      const float inv = 1.0f / l[j];
+      const float r[4] = {acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv};
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<uint2*>(out + (size_t)f * 4) =
+            make_uint2(f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16),
+                       f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16));
+      } else {
+        *reinterpret_cast<float4*>(out + (size_t)f * 4) = make_float4(r[0], r[1], r[2], r[3]);
       }
     }
   }
