@@ -426,6 +426,18 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float4& acc, flo
                     acc.w * a + acc2.w * w);
 }
 
+// out[0..3] = acc * inv, rounded to T.
+template <typename T>
+__device__ __forceinline__ void store_row4(T* out, float4 acc, float inv) {
+  const float r[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint2*>(out) = make_uint2(f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16),
+                                                f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16));
+  } else {
+    *reinterpret_cast<float4*>(out) = make_float4(r[0], r[1], r[2], r[3]);
+  }
+}
+
 // One wavefront per (sequence, query head): combine the partitions' summaries
 //   M = max_p m_p,  L = sum_p 2^(m_p - M) l_p,  out = sum_p 2^(m_p - M) o_p / L.
 // A partition's D floats are D/4 float4 slices; the wavefront's lanes cover
@@ -476,17 +488,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
     const float4 o2 = make_float4(lane_xor32(acc.x), lane_xor32(acc.y), lane_xor32(acc.z), lane_xor32(acc.w));
     merge_state(m, l, acc, lane_xor32(m), lane_xor32(l), o2);
   }
-  if (ph == 0) {
-    const float inv = 1.0f / l;
-    T* out = out_ptr + (size_t)pair * D + (size_t)f * 4;
-    const float r[4] = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
-    if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<uint2*>(out) = make_uint2(f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16),
-                                                  f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16));
-    } else {
-      *reinterpret_cast<float4*>(out) = make_float4(r[0], r[1], r[2], r[3]);
-    }
-  }
+  if (ph == 0) store_row4<T>(out_ptr + (size_t)pair * D + (size_t)f * 4, acc, 1.0f / l);
 }
 
 // ---------------------------------------------------------------------------
@@ -694,16 +696,7 @@ __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
       const int f = lane + kWave * j;
-      if (f >= kSlices) continue;
-      const float inv = 1.0f / l[j];
-      const float r[4] = {acc[j].x * inv, acc[j].y * inv, acc[j].z * inv, acc[j].w * inv};
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<uint2*>(out + (size_t)f * 4) =
-            make_uint2(f32_to_bf16_bits(r[0]) | (f32_to_bf16_bits(r[1]) << 16),
-                       f32_to_bf16_bits(r[2]) | (f32_to_bf16_bits(r[3]) << 16));
-      } else {
-        *reinterpret_cast<float4*>(out + (size_t)f * 4) = make_float4(r[0], r[1], r[2], r[3]);
-      }
+      if (f < kSlices) store_row4<T>(out + (size_t)f * 4, acc[j], 1.0f / l[j]);
     }
   }
 }

@@ -11,12 +11,13 @@
 // Serving", 2. FlashAttention, "Online Softmax Makes Tiling Possible").
 //
 // Tiling. A workgroup owns (sequence, KV head, a tile of query rows). Its
-// wavefronts form two groups; in each group there is one wavefront per (query
-// head of the GQA group, 16-row sub-tile), at least four, so every K/V tile is
-// staged in LDS once for all G heads. The groups take alternate 64-key tiles
-// (staged together), each keeping its own online-softmax state for the same
-// rows, and are merged through LDS at the end: twice the resident waves of a
-// one-group tiling. The next pair of tiles is loaded into registers while the
+// wavefronts form NG groups (3 when a group has at most 4 waves, else 2); in
+// each group there is one wavefront per (query head of the GQA group, 16-row
+// sub-tile), at least four, so every K/V tile is staged in LDS once for all G
+// heads. The groups take every NG-th 64-key tile (a step stages NG tiles
+// together), each keeping its own online-softmax state for the same rows, and
+// are merged through LDS at the end: NG times the resident waves of a
+// one-group tiling. The next step's tiles are loaded into registers while the
 // MFMAs run. Per 64-key tile (4 paged blocks):
 //   * K: the pool's (block, head) tiles are copied to LDS as they are; a
 //     16-byte head-dim vector of one key is one MFMA operand fragment.
@@ -45,6 +46,9 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 constexpr int kQRows = 16;          // query rows per wavefront (the MFMA M / N)
 constexpr int kKeyTile = 64;        // keys per tile = 4 blocks
 constexpr int kMaxGroup = 8;
+// s_waitcnt immediate for vmcnt(0) alone on gfx9-family parts (expcnt and
+// lgkmcnt fields at their maximum, i.e. not waited for).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const Vec16& v) {
   return __builtin_bit_cast(bf16x8, make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]));
@@ -60,38 +64,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // Waves per group for a GQA group of G heads: one per (head, 16-row sub-tile),
 // at least 4 so that K/V staging is spread over enough threads.
 __host__ __device__ constexpr int prefill_row_subtiles(int g) { return (g <= 4 && 4 % g == 0) ? 4 / g : 1; }
+// Groups of waves per workgroup (each takes every NG-th key tile): three when a
+// group has at most 4 waves (12 waves, 3 per SIMD), else two.
+__host__ __device__ constexpr int prefill_groups(int g) { return g * prefill_row_subtiles(g) <= 4 ? 3 : 2; }
 
-template <int D, int NWG>
+template <int D, int NWG, int NG>
 union PrefillLds {
   // V rows padded by 32 bytes: the transposed reads of 8 consecutive keys then
   // fall on distinct LDS banks.
   static constexpr int kVStride = D + 16;
   struct {
-    alignas(16) uint16_t k[2][kKeyTile / kBlockSize][kBlockSize * D];   // K tiles, pool layout
-    alignas(16) uint16_t v[2][kKeyTile][kVStride];                     // V tiles, [key][head dim]
+    alignas(16) uint16_t k[NG][kKeyTile / kBlockSize][kBlockSize * D];   // K tiles, pool layout
+    alignas(16) uint16_t v[NG][kKeyTile][kVStride];                     // V tiles, [key][head dim]
   } tile;
-  struct {                                                              // group 1's state, at the end
-    alignas(16) float o[NWG][D / 16][4][kWave];
-    float m[NWG][kWave];
-    float l[NWG][kWave];
+  struct {                                                               // groups 1.., at the end
+    alignas(16) float o[NG - 1][NWG][D / 16][4][kWave];
+    float m[NG - 1][NWG][kWave];
+    float l[NG - 1][NWG][kWave];
   } merge;
 };
 
 template <int D, int G>
-__global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chunk_kernel(
+__global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G)) void prefill_chunk_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query, const uint16_t* __restrict__ kpool,
     const uint16_t* __restrict__ vpool, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     PrefillParams prm) {
   constexpr int RT = prefill_row_subtiles(G);
   constexpr int NWG = G * RT;             // waves per group
-  constexpr int NT = 2 * 64 * NWG;        // threads per workgroup (two groups)
+  constexpr int NG = prefill_groups(G);   // groups
+  constexpr int NT = NG * 64 * NWG;       // threads per workgroup
   constexpr int KSTEPS = D / 32;          // MFMA k-steps over the head dim for S
   constexpr int NTILES = D / 16;          // 16-row output tiles over the head dim
   constexpr int VPR = D / 8;              // 16-byte vectors per token row
   constexpr int kVecs = kKeyTile * VPR;   // 16-byte vectors per key tile of K (and of V)
-  constexpr int PER = (2 * kVecs + NT - 1) / NT;   // vectors each thread stages per tile pair
-  __shared__ PrefillLds<D, NWG> lds;
+  constexpr int PER = (NG * kVecs + NT - 1) / NT;   // vectors each thread stages per step
+  __shared__ PrefillLds<D, NWG, NG> lds;
 
   const int s = blockIdx.z;
   const int h = blockIdx.y;
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chu
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = w / NWG;                     // 0: even key tiles, 1: odd key tiles
+  const int grp = w / NWG;                     // takes key tiles grp, grp + NG, ...
   const int wl = w % NWG;                      // wave within the group
   const int g = wl % G;                        // query head within the GQA group
   const int r0 = r_wg + (wl / G) * kQRows;     // first chunk row of this wave
@@ -117,7 +125,7 @@ __global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chu
   const int wg_rows = min(kQRows * RT, T - r_wg);
   const int kv_end = min(ctx, first_pos + r_wg + wg_rows);
   const int ntiles = (kv_end + kKeyTile - 1) / kKeyTile;
-  const int npairs = (ntiles + 1) / 2;
+  const int nsteps = (ntiles + NG - 1) / NG;   // each step stages NG tiles, one per group
   // Last key this wave's rows can see (its compute stops after that tile).
   const int wave_last_key = wave_live ? min(ctx - 1, first_pos + min(r0 + kQRows, T) - 1) : -1;
 
@@ -154,76 +162,102 @@ __global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chu
   const size_t head_off = (size_t)h * tile_elems;
   const size_t blk_stride = (size_t)hkv * tile_elems;
 
-  // Register staging of a pair of key tiles: thread-strided 16-byte vectors,
-  // copied to LDS in pool order (coalesced reads, 16-byte LDS writes).
-  //   vector q of the pair: tile t = q / kVecs, qq = q % kVecs;
+  // Register staging of a step's NG key tiles: thread-strided 16-byte
+  // vectors, copied to LDS in pool order (coalesced reads, 16-byte LDS writes).
+  //   vector q of the step: tile t = q / kVecs, qq = q % kVecs;
   //   K: block qq / (16*VPR) of the tile, offset qq % (16*VPR) in pool layout;
   //   V: key qq / VPR, head-dim vector qq % VPR.
-  // Both live in block q / (16*VPR) of the pair; a block spans a multiple of
-  // 64 vectors, so that block is the same for the whole wavefront. The block
-  // ids are thus wave-uniform and fetched one pair earlier than the data, so
-  // a prefetch costs one memory latency, not two.
+  // Both live in block q / (16*VPR) of the step; a block spans a multiple of
+  // 64 vectors, so for vector slot u of a wavefront that block, the tile and
+  // everything but a lane term are wave-uniform: a load is a scalar block
+  // base plus a per-lane offset that does not change from step to step. The
+  // block ids are fetched one step earlier than the data, so a prefetch costs
+  // one memory latency, not two.
+  //   Blocks past the staged range are not read. K rows past the range need
+  //   no clearing (their scores are masked); V rows are cleared (they may
+  //   hold anything, NaN included, and their zero weights would not cancel
+  //   a NaN).
   constexpr int kBlockVecs = kBlockSize * VPR;
+  constexpr int kStepBlocks = NG * kKeyTile / kBlockSize;
+  constexpr bool kAllSlots = NT * PER == NG * kVecs;   // every thread's slots hold a vector
   static_assert(kBlockVecs % kWave == 0, "a wavefront's vectors must share a block");
   const int wave_vec0 = w * kWave;
+  const uint32_t lane_k = (uint32_t)lane * 16u;                                   // K: byte offset of the lane
+  const uint32_t lane_vg = (uint32_t)((lane / VPR) * D + (lane % VPR) * 8) * 2u;  // V in the pool tile
+  const uint32_t lane_vl = (uint32_t)((lane / VPR) * PrefillLds<D, NWG, NG>::kVStride + (lane % VPR) * 8) * 2u;  // V in LDS
+  const int lane_tok = lane / VPR;                                                // V: token offset of the lane
+  char* const lds_k = reinterpret_cast<char*>(&lds.tile.k[0][0][0]);
+  char* const lds_v = reinterpret_cast<char*>(&lds.tile.v[0][0][0]);
+  // A slot whose block is not read keeps its previous contents: stale K rows
+  // are masked, and V rows past the range are cleared when stored.
   Vec16 kreg[PER], vreg[PER];
-  auto pair_ids = [&](int j, int (&ids)[PER]) {
+#pragma unroll
+  for (int u = 0; u < PER; ++u) kreg[u] = vreg[u] = zero16();
+  auto step_ids = [&](int j, int (&ids)[PER]) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int pb = (wave_vec0 + u * NT) / kBlockVecs;   // block of the pair, uniform
-      const int lb = j * (2 * kKeyTile / kBlockSize) + pb;
-      ids[u] = (pb < 2 * kKeyTile / kBlockSize && lb * kBlockSize < kv_end) ? bt[lb] : 0;
+      const int pb = (wave_vec0 + u * NT) / kBlockVecs;   // block of the step, uniform
+      const int lb = j * kStepBlocks + pb;
+      ids[u] = (pb < kStepBlocks && lb * kBlockSize < kv_end) ? bt[lb] : 0;
     }
   };
-  auto load_pair = [&](int j, const int (&ids)[PER]) {
+  auto load_step = [&](int j, const int (&ids)[PER]) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int q = tid + u * NT;
-      kreg[u] = zero16();
-      vreg[u] = zero16();
-      if (q < 2 * kVecs) {
-        const int qq = q % kVecs;
-        const int key0 = j * 2 * kKeyTile + (q / kBlockVecs) * kBlockSize;   // first key of the block
-        const size_t base = (size_t)ids[u] * blk_stride + head_off;
-        if (key0 < kv_end) kreg[u] = ld16(kpool + base + (size_t)(qq % kBlockVecs) * 8);
-        const int tok = qq / VPR;
-        if (key0 + tok % kBlockSize < kv_end)
-          vreg[u] = ld16(vpool + base + (size_t)(tok % kBlockSize) * D + (qq % VPR) * 8);
+      const int q0 = wave_vec0 + u * NT;                   // uniform
+      if (!kAllSlots && q0 >= NG * kVecs) continue;
+      const int qq0 = q0 % kVecs;
+      const int key0 = j * NG * kKeyTile + (q0 / kBlockVecs) * kBlockSize;   // first key of the block
+      if (key0 < kv_end) {                                 // uniform: blocks past the range are not read
+        const size_t base = ((size_t)ids[u] * blk_stride + head_off) * sizeof(uint16_t);
+        const char* kb = reinterpret_cast<const char*>(kpool) + base;
+        const char* vb = reinterpret_cast<const char*>(vpool) + base;
+        kreg[u] = ld16(kb + (uint32_t)(qq0 % kBlockVecs) * 16u + lane_k);
+        const int tok0 = (qq0 / VPR) % kBlockSize;         // uniform
+        vreg[u] = ld16(vb + (uint32_t)(tok0 * D * 2) + lane_vg);
       }
     }
   };
-  auto store_pair = [&]() {
+  // Clearing happens here, when the loaded values are needed anyway, so the
+  // loads of the next step are not waited for early.
+  auto store_step = [&](int j) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int q = tid + u * NT;
-      if (q < 2 * kVecs) {
-        const int t = q / kVecs, qq = q % kVecs;
-        *reinterpret_cast<uint4*>(&lds.tile.k[t][qq / (kBlockSize * VPR)][(qq % (kBlockSize * VPR)) * 8]) =
-            make_uint4(kreg[u].w[0], kreg[u].w[1], kreg[u].w[2], kreg[u].w[3]);
-        *reinterpret_cast<uint4*>(&lds.tile.v[t][qq / VPR][(qq % VPR) * 8]) =
-            make_uint4(vreg[u].w[0], vreg[u].w[1], vreg[u].w[2], vreg[u].w[3]);
-      }
+      const int q0 = wave_vec0 + u * NT;
+      if (!kAllSlots && q0 >= NG * kVecs) continue;
+      const int t = q0 / kVecs, qq0 = q0 % kVecs;
+      const int key0 = j * NG * kKeyTile + (q0 / kBlockVecs) * kBlockSize;   // first key of the block
+      const int tok0 = (qq0 / VPR) % kBlockSize;
+      if (key0 + tok0 + lane_tok >= kv_end) vreg[u] = zero16();
+      *reinterpret_cast<uint4*>(lds_k + (uint32_t)(t * (kKeyTile * D) + qq0 * 8) * 2u + lane_k) =
+          make_uint4(kreg[u].w[0], kreg[u].w[1], kreg[u].w[2], kreg[u].w[3]);
+      *reinterpret_cast<uint4*>(lds_v + (uint32_t)((t * kKeyTile + qq0 / VPR) * PrefillLds<D, NWG, NG>::kVStride) * 2u +
+                                lane_vl) = make_uint4(vreg[u].w[0], vreg[u].w[1], vreg[u].w[2], vreg[u].w[3]);
     }
   };
 
   int ids_next[PER] = {};
-  if (npairs > 0) {
+  if (nsteps > 0) {
     int ids0[PER];
-    pair_ids(0, ids0);
-    load_pair(0, ids0);
-    if (npairs > 1) pair_ids(1, ids_next);
+    step_ids(0, ids0);
+    load_step(0, ids0);
+    if (nsteps > 1) step_ids(1, ids_next);
   }
+  // Let the query fragments and the first step land here, where they are
+  // needed anyway: the loop then enters with no vector load outstanding, and
+  // the compiler does not hold the tile's MFMAs for the prefetched step.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   const int vkey = 4 * quad + (col >> 2);   // transposed V read: key offset and column of this lane
   const int vcol = 4 * (col & 3);
-  for (int j = 0; j < npairs; ++j) {
-    __syncthreads();   // the previous pair is no longer read
-    store_pair();
-    __syncthreads();   // this pair is in LDS
-    if (j + 1 < npairs) {                   // in flight during the MFMAs below
-      load_pair(j + 1, ids_next);
-      if (j + 2 < npairs) pair_ids(j + 2, ids_next);
+  for (int j = 0; j < nsteps; ++j) {
+    __syncthreads();   // the previous step's tiles are no longer read
+    store_step(j);
+    __syncthreads();   // this step's tiles are in LDS
+    if (j + 1 < nsteps) {                   // in flight during the MFMAs below
+      load_step(j + 1, ids_next);
+      if (j + 2 < nsteps) step_ids(j + 2, ids_next);
     }
-    const int key0 = (2 * j + grp) * kKeyTile;
+    const int key0 = (NG * j + grp) * kKeyTile;
     if (key0 >= kv_end || key0 > wave_last_key) continue;   // past the range or the causal diagonal
 
     // ---- S^T = K Q^T, one 16-key block per MFMA tile: lane holds S^T[16r + 4*quad + i][row col] ----
@@ -238,36 +272,42 @@ __global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chu
       }
     }
 
-    // ---- scale, causal mask (only on tiles that reach past the wave's first row), row max ----
-    float mt = -INFINITY;
+    // ---- causal mask (only on tiles that reach past the wave's first row), row max ----
     if (key0 + kKeyTile - 1 > wave_first_pos) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int key = key0 + 16 * r + 4 * quad + i;
-          st[r][i] = key <= my_pos ? st[r][i] * prm.scale_log2 : -INFINITY;
-          mt = fmaxf(mt, st[r][i]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          st[r][i] *= prm.scale_log2;
-          mt = fmaxf(mt, st[r][i]);
+          if (key0 + 16 * r + 4 * quad + i > my_pos) st[r][i] = -INFINITY;
         }
       }
     }
-    // The row's 64 keys sit in lanes col, col+16, col+32, col+48.
-    mt = xor32_max(xor16_max(mt));
-    // Group 1 starts at tile 1, which can lie wholly past a row's position:
-    // then the row has seen no key yet and its maximum is still -inf.
-    const float mn = fmaxf(m_row, mt);
-    const float msub = mn == -INFINITY ? 0.f : mn;
-    const float alpha = fast_exp2(m_row - msub);
-    m_row = mn;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, st[r][i]);
+    }
+    // The row's 64 keys sit in lanes col, col+16, col+32, col+48. Scores are
+    // raw dot products; the scale (times log2 e) is applied in the exponent.
+    mt = xor32_max(xor16_max(mt)) * prm.scale_log2;
+    // The reference maximum m_row moves only when a row's maximum exceeds it
+    // by more than 2^8: weights then stay below 256 and the common factor
+    // cancels in the final division, so most tiles skip the rescale. A row
+    // that has seen no key yet (group 1 starts at tile 1, which can lie wholly
+    // past a row's position) keeps m_row = -inf and gets zero weights.
+    const bool grow = mt > m_row + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? fast_exp2(m_row - mt) : 1.f;
+      m_row = grow ? mt : m_row;
+      l_row *= alpha;
+#pragma unroll
+      for (int n = 0; n < NTILES; ++n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[n][i] *= alpha;
+      }
+    }
+    const float msub = m_row == -INFINITY ? 0.f : m_row;
 
     // ---- P^T fragments in registers: P split into bf16 high + remainder ----
     // B operand of O^T += V^T P^T for key half kk: k-index j of lane (quad, col)
@@ -279,8 +319,8 @@ __global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chu
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const float p0 = fast_exp2(st[2 * kk + j / 4][j % 4] - msub);
-        const float p1 = fast_exp2(st[2 * kk + j / 4][j % 4 + 1] - msub);
+        const float p0 = fast_exp2(fmaf(st[2 * kk + j / 4][j % 4], prm.scale_log2, -msub));
+        const float p1 = fast_exp2(fmaf(st[2 * kk + j / 4][j % 4 + 1], prm.scale_log2, -msub));
         ls += p0 + p1;
         const uint32_t hb = pack_bf16x2(p0, p1);
         hw[j / 2] = hb;
@@ -289,12 +329,7 @@ __global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chu
       phi[kk] = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
       plo[kk] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
     }
-    l_row = l_row * alpha + ls;
-#pragma unroll
-    for (int n = 0; n < NTILES; ++n) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[n][i] *= alpha;
-    }
+    l_row += ls;
 
     // ---- O^T += V^T P^T ----
     // A = V^T[d][the same 8 keys] comes from the natural V tile through the
@@ -318,24 +353,33 @@ __global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chu
     }
   }
 
-  // ---- merge the two groups' summaries of the same rows (online-softmax rule) ----
+  // ---- merge the groups' summaries of the same rows (online-softmax rule) ----
   __syncthreads();   // tiles are no longer read; the LDS becomes the merge area
-  if (grp == 1) {
+  if (grp > 0) {
 #pragma unroll
     for (int n = 0; n < NTILES; ++n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds.merge.o[wl][n][i][lane] = o[n][i];
+      for (int i = 0; i < 4; ++i) lds.merge.o[grp - 1][wl][n][i][lane] = o[n][i];
     }
-    lds.merge.m[wl][lane] = m_row;
-    lds.merge.l[wl][lane] = l_row;
+    lds.merge.m[grp - 1][wl][lane] = m_row;
+    lds.merge.l[grp - 1][wl][lane] = l_row;
   }
   __syncthreads();
-  if (grp == 1 || !wave_live) return;
-  // Group 0 always holds tile 0 (key 0 is visible to every row), so m_row is finite.
-  const float m1 = lds.merge.m[wl][lane];
-  const float mx = fmaxf(m_row, m1);
-  const float w0 = fast_exp2(m_row - mx), w1 = fast_exp2(m1 - mx);
-  const float lt = xor32_sum(xor16_sum(l_row * w0 + lds.merge.l[wl][lane] * w1));
+  if (grp > 0 || !wave_live) return;
+  // Group 0 always holds tile 0 (key 0 is visible to every row), so m_row is
+  // finite; a group that saw no key has m = -inf and weight 0.
+  float mx = m_row;
+#pragma unroll
+  for (int k = 0; k < NG - 1; ++k) mx = fmaxf(mx, lds.merge.m[k][wl][lane]);
+  float wk[NG];
+  wk[0] = fast_exp2(m_row - mx);
+  float lsum = l_row * wk[0];
+#pragma unroll
+  for (int k = 1; k < NG; ++k) {
+    wk[k] = fast_exp2(lds.merge.m[k - 1][wl][lane] - mx);
+    lsum += lds.merge.l[k - 1][wl][lane] * wk[k];
+  }
+  const float lt = xor32_sum(xor16_sum(lsum));
 
   // ---- normalize and store: lane writes row col, d = 16n + 4*quad .. +4 ----
   if (my_row < T) {
@@ -345,7 +389,12 @@ __global__ __launch_bounds__(128 * G * prefill_row_subtiles(G)) void prefill_chu
     for (int n = 0; n < NTILES; ++n) {
       float r[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = (o[n][i] * w0 + lds.merge.o[wl][n][i][lane] * w1) * inv;
+      for (int i = 0; i < 4; ++i) {
+        float acc = o[n][i] * wk[0];
+#pragma unroll
+        for (int k = 1; k < NG; ++k) acc += lds.merge.o[k - 1][wl][n][i][lane] * wk[k];
+        r[i] = acc * inv;
+      }
       *reinterpret_cast<uint2*>(orow + 16 * n + 4 * quad) = make_uint2(pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]));
     }
   }
@@ -356,7 +405,7 @@ hipError_t launch_prefill_dg(const PrefillParams& prm, hipStream_t stream) {
   constexpr int RT = prefill_row_subtiles(G);
   const dim3 grid((unsigned)((prm.max_q_len + kQRows * RT - 1) / (kQRows * RT)), (unsigned)prm.num_kv_heads,
                   (unsigned)prm.num_seqs);
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), grid, dim3(128 * G * RT), 0, stream,
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), grid, dim3(64 * G * RT * prefill_groups(G)), 0, stream,
                      static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
                      static_cast<const uint16_t*>(prm.kpool), static_cast<const uint16_t*>(prm.vpool),
                      prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
