@@ -94,8 +94,10 @@ def read_traffic(achieved_launch_bytes: int):
         return None
 
 
-def cpu_baseline(step, reps: int = 3):
-    """The oracle, as it stands, on the same workload: append + decode (+ prefill)."""
+def cpu_baseline(step, min_seconds: float = 10.0, max_reps: int = 30):
+    """The oracle, as it stands, on the same workload: append + decode (+ prefill),
+    repeated until about ``min_seconds`` of CPU work (at least 3 runs) and timed
+    per run; returns the median seconds per step, the runs and the threads."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -110,7 +112,7 @@ def cpu_baseline(step, reps: int = 3):
     bt, cl = s.decode_inputs()
     pq = s.prefill_query.f32 if s.prefill_query is not None else None
     times = []
-    for _ in range(reps):
+    while len(times) < 3 or (sum(times) < min_seconds and len(times) < max_reps):
         t0 = time.perf_counter()
         oracle.append(pk, pv, nk, nv, s.new_slots)
         oracle.paged_decode(q, pk, pv, bt, cl, s.scale)
@@ -118,7 +120,7 @@ def cpu_baseline(step, reps: int = 3):
             pbt, pcl = s.prefill_inputs()
             oracle.paged_prefill_chunk(pq, s.cu_q_lens, pk, pv, pbt, pcl, s.scale)
         times.append(time.perf_counter() - t0)
-    return float(np.median(times)), threads
+    return float(np.median(times)), len(times), threads
 
 
 def main():
@@ -290,13 +292,14 @@ def main():
                                   "flops_per_launch": ab["prefill_flops"]}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same step ...")
-        t_cpu, threads = cpu_baseline(s)
+        t_cpu, runs, threads = cpu_baseline(s)
         result["cpu_baseline"] = {
             "value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"the whole step ({s.name}: append + decode of all {nseq} sequences"
-                      f"{' + prefill chunk' if has_prefill else ''}), numpy float64, median of 3;"
-                      f" {t_cpu:.2f} s per step on {os.cpu_count()} host CPUs",
+                      f"{' + prefill chunk' if has_prefill else ''}), numpy float64, median of {runs} runs"
+                      f" ({runs * t_cpu:.0f} s of CPU work); {t_cpu:.2f} s per step; BLAS pool of"
+                      f" {threads} threads, the per-sequence loop single-threaded; {os.cpu_count()} host CPUs",
         }
     pkv.kv_pool_destroy(pool)
     print(json.dumps(result), flush=True)
