@@ -164,12 +164,15 @@ pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* 
                                          int max_blocks_per_seq, float scale, void* stream);
 
 /* ---- kernel timing (measurement support, not part of the attention path) ----
- * While enabled, every kernel the library enqueues is bracketed by a pair of
- * HIP events on the same stream (events are created by pkv_timing_enable,
- * never inside the calls). pkv_timing_read waits for the recorded events and
- * returns, for one kernel kind, the number of launches recorded and their
- * summed duration in milliseconds. Recording stops silently once
- * max_launches launches have been recorded. Not for use under graph capture. */
+ * While enabled, every kernel of the kinds selected by kind_mask (bit k for
+ * pkv_kernel_kind k; 0 selects all) that the library enqueues is bracketed by
+ * a pair of HIP events on the same stream (events are created by
+ * pkv_timing_enable, never inside the calls). Each pair adds a small gap to
+ * the stream, so measure only the kinds needed. pkv_timing_read waits for the
+ * recorded events and returns, for one kernel kind, the number of launches
+ * recorded and their summed duration in milliseconds. Recording stops
+ * silently once max_launches launches have been recorded. Not for use under
+ * graph capture. */
 typedef enum {
     PKV_KERNEL_APPEND = 0,
     PKV_KERNEL_DECODE_PARTITION = 1,
@@ -178,7 +181,7 @@ typedef enum {
     PKV_KERNEL_KINDS = 4
 } pkv_kernel_kind;
 
-pkv_status pkv_timing_enable(int max_launches);
+pkv_status pkv_timing_enable(int max_launches, unsigned int kind_mask);
 pkv_status pkv_timing_disable(void);
 pkv_status pkv_timing_read(pkv_kernel_kind kind, int* launches, double* total_ms);
 

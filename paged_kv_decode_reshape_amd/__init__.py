@@ -53,7 +53,7 @@ _SIGNATURES = {
     "paged_attention_prefill_chunk": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                               c_int, c_float, c_void_p]),
-    "pkv_timing_enable": (c_int, [c_int]),
+    "pkv_timing_enable": (c_int, [c_int, ctypes.c_uint]),
     "pkv_timing_disable": (c_int, []),
     "pkv_timing_read": (c_int, [c_int, _P(c_int), _P(ctypes.c_double)]),
 }
@@ -168,8 +168,11 @@ def paged_attention_prefill_chunk(pool, layer, out, query, cu_q_lens, block_tabl
                                                 float(scale), _stream(stream)))
 
 
-def pkv_timing_enable(max_launches):
-    _check(load().pkv_timing_enable(max_launches))
+def pkv_timing_enable(max_launches, kinds=None):
+    """Record launches of the given kernel kinds (an iterable of KERNEL_*
+    values; None records every kind)."""
+    mask = 0 if kinds is None else sum(1 << int(k) for k in set(kinds))
+    _check(load().pkv_timing_enable(max_launches, mask))
 
 
 def pkv_timing_disable():

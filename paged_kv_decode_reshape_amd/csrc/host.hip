@@ -139,6 +139,7 @@ size_t round16(size_t x) { return (x + 15) / 16 * 16; }
 struct TimingState {
   std::mutex mu;
   bool enabled = false;
+  unsigned int kinds = 0;   // bit k set: launches of kernel kind k are recorded
   int cap = 0;
   int used = 0;
   std::vector<hipEvent_t> start, stop;
@@ -163,7 +164,7 @@ namespace pkv {
 
 void KernelTimer::begin(KernelKind kind, hipStream_t stream) const {
   g_timing_slot = -1;
-  if (!g_timing.enabled) return;
+  if (!g_timing.enabled || !(g_timing.kinds & (1u << (int)kind))) return;
   std::lock_guard<std::mutex> lock(g_timing.mu);
   if (!g_timing.enabled || g_timing.used >= g_timing.cap) return;
   const int slot = g_timing.used++;
@@ -368,8 +369,10 @@ pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* 
   return PKV_OK;
 }
 
-pkv_status pkv_timing_enable(int max_launches) {
+pkv_status pkv_timing_enable(int max_launches, unsigned int kind_mask) {
   if (max_launches <= 0) return fail(PKV_ERR_INVALID_ARG, "max_launches must be positive");
+  const unsigned int all = (1u << PKV_KERNEL_KINDS) - 1u;
+  if (kind_mask & ~all) return fail(PKV_ERR_INVALID_ARG, "kind_mask 0x%x has bits past the kernel kinds", kind_mask);
   std::lock_guard<std::mutex> lock(g_timing.mu);
   destroy_events_locked();
   g_timing.start.resize(max_launches);
@@ -388,6 +391,7 @@ pkv_status pkv_timing_enable(int max_launches) {
   }
   g_timing.cap = max_launches;
   g_timing.used = 0;
+  g_timing.kinds = kind_mask ? kind_mask : all;
   g_timing.enabled = true;
   return PKV_OK;
 }
