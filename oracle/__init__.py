@@ -1,4 +1,5 @@
-"""CPU oracle (test infrastructure only; see paged_attention.py)."""
+"""CPU oracle (test infrastructure only; see paged_attention.py, and fp8.py for
+the 8-bit KV-cache code)."""
 from .paged_attention import (  # noqa: F401
     append,
     attend,
