@@ -16,8 +16,9 @@ used here (the plainest ones, also what MI355X converts natively):
   * quantizing x: y = fp32(x) * fp32(1 / scale), rounded in fp32 (the
     product both sides compute); then y is clamped to [-448, 448] (so
     out-of-range values and infinities saturate), and rounded to the nearest
-    code, ties to even mantissa. NaN stays NaN (code 0x7F, or 0xFF when its
-    sign bit is set); -0 keeps its sign (0x80).
+    code, ties to even mantissa. A NaN input stays NaN: code 0x7F, or 0xFF
+    when the input's sign bit is set (IEEE 754 leaves the sign of a NaN
+    product open, so the input's is the one used); -0 keeps its sign (0x80).
 
 Everything below follows those definitions with plain integer and float64
 arithmetic; no library FP8 type is used.
@@ -46,10 +47,10 @@ def fp8_e4m3_decode(codes) -> np.ndarray:
 
 def fp8_e4m3_encode(x, inv_scale: float = 1.0) -> np.ndarray:
     """Code (uint8) of fp32(x) * fp32(inv_scale), saturated and rounded to nearest even."""
-    y = np.asarray(x, dtype=np.float32) * np.float32(inv_scale)    # the fp32 product
-    y = y.astype(np.float64)
+    x32 = np.asarray(x, dtype=np.float32)
+    y = (x32 * np.float32(inv_scale)).astype(np.float64)           # the fp32 product
     nan = np.isnan(y)
-    neg = np.signbit(y)
+    neg = np.signbit(x32)          # inv_scale > 0: the product's sign, and the NaN's
     a = np.minimum(np.abs(np.where(nan, 0.0, y)), E4M3_MAX)
     # Exponent of the binade holding a; zero and the subnormals share the
     # smallest normal binade's exponent and spacing (2^-9).

@@ -60,7 +60,8 @@ def pin_closed_forms(f8):
     vals = f8.fp8_e4m3_decode(np.array([0x01, 0x08, 0x38, 0x7E, 0x7F, 0x80, 0xB8]))
     assert vals[0] == 2.0 ** -9 and vals[1] == 2.0 ** -6 and vals[2] == 1.0 and vals[3] == 448.0
     assert np.isnan(vals[4]) and vals[5] == 0.0 and np.signbit(vals[5]) and vals[6] == -1.0
-    assert f8.fp8_e4m3_encode(np.array([np.nan], np.float32))[0] == 0x7F
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7F800001], np.uint32).view(np.float32)
+    assert list(f8.fp8_e4m3_encode(nans, 0.125)) == [0x7F, 0xFF, 0x7F]     # a NaN keeps its sign
 
 
 def pin_round_trip_and_order(f8):

@@ -17,8 +17,10 @@ MUTANTS = {
     "round_half_up": ("q = np.round(a / step)", "q = np.floor(a / step + 0.5)"),
     "no_saturation": ("a = np.minimum(np.abs(np.where(nan, 0.0, y)), E4M3_MAX)",
                       "a = np.abs(np.where(nan, 0.0, y))"),
-    "scale_divides": ("y = np.asarray(x, dtype=np.float32) * np.float32(inv_scale)",
-                      "y = np.asarray(x, dtype=np.float32) / np.float32(inv_scale)"),
+    "scale_divides": ("y = (x32 * np.float32(inv_scale)).astype(np.float64)",
+                      "y = (x32 / np.float32(inv_scale)).astype(np.float64)"),
+    "nan_sign_dropped": ("code = np.where(nan, np.where(neg, 0xFF, 0x7F), code)",
+                         "code = np.where(nan, 0x7F, code)"),
     "subnormal_step_wrong": ("sub = (m / 8.0) * 2.0 ** _MIN_NORMAL_EXP", "sub = (m / 8.0) * 2.0 ** (_MIN_NORMAL_EXP - 1)"),
     "no_nan_code": ("return np.where((e == 15) & (m == 7), np.nan, val)", "return val"),
     "sign_dropped": ("code = np.where(neg, 0x80, 0) | code_mag", "code = code_mag"),
