@@ -33,7 +33,8 @@
  *     Every call only enqueues kernels on `stream` (a hipStream_t; NULL = the
  *     null stream), so calls may be captured into a HIP graph.
  *   - Element type: the pool's dtype (PKV_F32 or PKV_BF16) for query, key,
- *     value and out. Integer tensors are int32 except slot_mapping (int64).
+ *     value and out; bf16 for all four with a PKV_FP8_E4M3 pool. Integer
+ *     tensors are int32 except slot_mapping (int64).
  *   - Every pointer must be 16-byte aligned; tensors are dense row-major.
  *   - Errors: a non-zero pkv_status is returned and nothing is enqueued;
  *     pkv_last_error() gives a message (thread-local). Values *inside*
@@ -49,12 +50,27 @@
  * the head dimension is cut into 16-byte vectors so that loads stay wide
  * despite the block-table indirection):
  *   K: [num_blocks][num_kv_heads][head_dim/x][block_size][x], x = 16/elem_bytes
- *      (8 for bf16, 4 for fp32): for a fixed 16-byte slice of the head
- *      dimension, the 16 tokens of a block are consecutive 16-byte vectors.
+ *      (16 for e4m3, 8 for bf16, 4 for fp32): for a fixed 16-byte slice of
+ *      the head dimension, the 16 tokens of a block are consecutive 16-byte
+ *      vectors.
  *   V: [num_blocks][num_kv_heads][block_size][head_dim]: each token's value
  *      row is contiguous.
  *   One (block, kv head) tile of K or V is block_size*head_dim*elem_bytes
  *   contiguous bytes (4 KiB for bf16 at head_dim 128).
+ *
+ * Eight-bit pools (PKV_FP8_E4M3). The pages note that an eight-bit KV cache
+ * costs little in quality and halves the bytes decode streams ("The Serving
+ * Playbook", "Quantized serving"); they fix neither the code nor the scale
+ * granularity. This library stores OCP FP8 E4M3 codes (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; S.1111.111 is NaN; no infinity; largest
+ * magnitude 448) with one fp32 scale per layer for K and one for V (set with
+ * kv_pool_set_fp8_scales; 1.0 by default). A code c stands for
+ * value(c) * scale. reshape_and_cache quantizes each bf16 input x as: y =
+ * fp32(x) * fp32(1/scale) rounded in fp32; y clamped to [-448, 448] (NaN
+ * stays NaN); rounded to the nearest code, ties to even. Attention treats the
+ * pool as holding value(c) * scale exactly (codes widen to bf16 without
+ * rounding; the K scale multiplies the softmax scale, the V scale the
+ * output).
  */
 #ifndef PKV_H
 #define PKV_H
@@ -74,7 +90,7 @@ typedef enum {
     PKV_ERR_WORKSPACE = -4      /* workspace missing or too small */
 } pkv_status;
 
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3 = 2 } pkv_dtype;
 
 /* Opaque handle: geometry plus per-layer K/V pool pointers (host memory only). */
 typedef struct pkv_pool pkv_pool;
@@ -95,14 +111,26 @@ pkv_status kv_pool_create(pkv_pool** out, int num_layers, int num_blocks, int bl
                           int num_kv_heads, int head_dim, pkv_dtype dtype,
                           void* const* k_layers, void* const* v_layers);
 
+/* Per-layer dequantization scales of an e4m3 pool: k_scales and v_scales
+ * are host arrays of num_layers floats (num_layers must equal the pool's),
+ * copied into the handle; later calls with this handle use them. Each scale
+ * must be positive and finite with a finite, nonzero fp32 inverse; otherwise
+ * PKV_ERR_INVALID_ARG and the handle is unchanged. Changing a scale does not
+ * rewrite codes already stored. PKV_ERR_INVALID_ARG for a pool of another
+ * dtype. Not thread-safe against concurrent calls on the same handle. */
+pkv_status kv_pool_set_fp8_scales(pkv_pool* pool, int num_layers, const float* k_scales,
+                                  const float* v_scales);
+
 /* Free the handle (never the device memory). NULL is accepted. */
 pkv_status kv_pool_destroy(pkv_pool* pool);
 
 /* Append: for t < num_tokens with slot s = slot_mapping[t] >= 0, write
  * key[t][h][:] and value[t][h][:] (all KV heads h) into block s / block_size,
  * offset s % block_size of `layer`'s pools, in the layout above. Negative
- * slots are skipped. Values are copied bit for bit.
- *   key, value: [num_tokens][num_kv_heads][head_dim], pool dtype.
+ * slots are skipped. Values are copied bit for bit (e4m3 pools: quantized
+ * with the layer's scales by the rule above).
+ *   key, value: [num_tokens][num_kv_heads][head_dim], pool dtype (bf16 for
+ *     an e4m3 pool).
  *   slot_mapping: int64 [num_tokens].
  * num_tokens == 0 is a no-op. */
 pkv_status reshape_and_cache(const pkv_pool* pool, int layer, const void* key,
@@ -120,8 +148,8 @@ pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_
  *   out[b][i] = sum_t softmax_t(scale * <query[b][i], K_b[t][i/G]>) V_b[t][i/G]
  * with G = num_q_heads / num_kv_heads and K_b/V_b read through
  * block_tables[b][t / block_size]. context_lens[b] == 0 gives a zero row.
- *   out, query: [num_seqs][num_q_heads][head_dim], pool dtype (out is rounded
- *     to nearest even from fp32 accumulators).
+ *   out, query: [num_seqs][num_q_heads][head_dim], pool dtype (bf16 for an
+ *     e4m3 pool; out is rounded to nearest even from fp32 accumulators).
  *   block_tables: int32 [num_seqs][max_blocks_per_seq]; entries past a
  *     sequence's last block are never read.
  *   context_lens: int32 [num_seqs].
@@ -151,11 +179,13 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
  * The chunk's own K/V must already be appended, so the cache holds
  * ctx_s = context_lens[s] >= T_s tokens; chunk row r is at absolute position
  * ctx_s - T_s + r and attends causally to positions 0 .. ctx_s - T_s + r.
- *   out, query: [total_q_tokens][num_q_heads][head_dim], pool dtype.
+ *   out, query: [total_q_tokens][num_q_heads][head_dim], bf16.
  *   cu_q_lens: int32 [num_seqs + 1], cu_q_lens[0] == 0, non-decreasing,
  *     cu_q_lens[num_seqs] == total_q_tokens.
  *   block_tables: int32 [num_seqs][max_blocks_per_seq]; context_lens: int32
- *     [num_seqs]. The contraction runs on bf16 MFMA (PKV_BF16 pools only). */
+ *     [num_seqs]. The contraction runs on bf16 MFMA: PKV_BF16 and
+ *     PKV_FP8_E4M3 pools (e4m3 codes widen to bf16 exactly); an fp32 pool
+ *     gives PKV_ERR_UNSUPPORTED. */
 pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* out,
                                          const void* query, const int32_t* cu_q_lens,
                                          const int32_t* block_tables,

@@ -17,15 +17,16 @@ import ctypes
 import os
 
 __all__ = [
-    "PkvError", "F32", "BF16", "KERNEL_APPEND", "KERNEL_DECODE_PARTITION",
+    "PkvError", "F32", "BF16", "FP8_E4M3", "KERNEL_APPEND", "KERNEL_DECODE_PARTITION",
     "KERNEL_DECODE_REDUCE", "KERNEL_PREFILL", "library_path", "load",
-    "kv_pool_bytes", "kv_pool_create", "kv_pool_destroy", "reshape_and_cache",
+    "kv_pool_bytes", "kv_pool_create", "kv_pool_set_fp8_scales", "kv_pool_destroy",
+    "reshape_and_cache",
     "paged_attention_decode_workspace_bytes", "paged_attention_decode",
     "paged_attention_prefill_chunk", "pkv_timing_enable", "pkv_timing_disable",
     "pkv_timing_read", "pkv_last_error", "EXPORTED_SYMBOLS",
 ]
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 KERNEL_APPEND, KERNEL_DECODE_PARTITION, KERNEL_DECODE_REDUCE, KERNEL_PREFILL = 0, 1, 2, 3
 
 _STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID_ARG", -2: "PKV_ERR_UNSUPPORTED",
@@ -43,6 +44,7 @@ _SIGNATURES = {
     "kv_pool_bytes": (c_int, [c_int, c_int, c_int, c_int, c_int, _P(c_size_t), _P(c_size_t)]),
     "kv_pool_create": (c_int, [_P(c_void_p), c_int, c_int, c_int, c_int, c_int, c_int,
                                _P(c_void_p), _P(c_void_p)]),
+    "kv_pool_set_fp8_scales": (c_int, [c_void_p, c_int, _P(c_float), _P(c_float)]),
     "kv_pool_destroy": (c_int, [c_void_p]),
     "reshape_and_cache": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p]),
     "paged_attention_decode_workspace_bytes": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
@@ -129,6 +131,14 @@ def kv_pool_create(num_layers, num_blocks, block_size, num_kv_heads, head_dim, d
     _check(load().kv_pool_create(ctypes.byref(handle), num_layers, num_blocks, block_size,
                                  num_kv_heads, head_dim, dtype, karr, varr))
     return handle.value
+
+
+def kv_pool_set_fp8_scales(pool, k_scales, v_scales):
+    """k_scales, v_scales: one float per layer of the pool."""
+    k, v = list(k_scales), list(v_scales)
+    if len(k) != len(v):
+        raise ValueError("k_scales and v_scales differ in length")
+    _check(load().kv_pool_set_fp8_scales(pool, len(k), (c_float * len(k))(*k), (c_float * len(v))(*v)))
 
 
 def kv_pool_destroy(pool):

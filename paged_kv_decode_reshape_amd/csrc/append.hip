@@ -14,6 +14,11 @@
 // the token-major input and writes of V rows are contiguous 16-byte runs; K
 // vectors land 256 bytes apart (bf16, D=128) in the pool's K layout
 // [block][head][D/x][16][x].
+//
+// An e4m3 pool takes bf16 rows: a thread reads 32 bytes (16 values) and
+// writes their 16 codes, quantized with the layer's 1/scale (saturating,
+// nearest even). The pages note that an eight-bit KV cache costs little in
+// quality ("The Serving Playbook", "Quantized serving").
 #include "device_common.h"
 #include "kernels.h"
 
@@ -44,6 +49,53 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams prm) {
   st16(reinterpret_cast<T*>(prm.vpool) + tile + (size_t)off * D + (size_t)c * EPV, v);
 }
 
+// 16 bf16 values at p, times inv_scale, as 16 e4m3 codes.
+__device__ __forceinline__ Vec16 quantize16(const uint16_t* p, float inv_scale) {
+  const Vec16 a = ld16(p), b = ld16(p + 8);
+  float f[16];
+  widen<uint16_t>(a, f);
+  widen<uint16_t>(b, f + 8);
+  Vec16 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = f32x2_to_fp8x2<false>(f[4 * i], f[4 * i + 1], inv_scale, 0u);
+    q.w[i] = f32x2_to_fp8x2<true>(f[4 * i + 2], f[4 * i + 3], inv_scale, w);
+  }
+  return q;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_fp8_kernel(AppendParams prm) {
+  constexpr int VPR = D / 16;   // 16-byte code vectors per token row
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long per_token = (long)prm.num_kv_heads * VPR;
+  if (idx >= per_token * prm.num_tokens) return;
+  const int t = (int)(idx / per_token);
+  const int rem = (int)(idx % per_token);
+  const int h = rem / VPR;
+  const int c = rem % VPR;
+  const int64_t slot = prm.slots[t];
+  if (slot < 0) return;
+  const int64_t blk = slot / kBlockSize;
+  const int off = (int)(slot % kBlockSize);
+  const size_t src = ((size_t)t * prm.num_kv_heads + h) * D + (size_t)c * 16;
+  const size_t tile = ((size_t)blk * prm.num_kv_heads + h) * (size_t)kBlockSize * D;
+  const Vec16 k = quantize16(reinterpret_cast<const uint16_t*>(prm.key) + src, prm.k_inv_scale);
+  const Vec16 v = quantize16(reinterpret_cast<const uint16_t*>(prm.value) + src, prm.v_inv_scale);
+  st16(reinterpret_cast<uint8_t*>(prm.kpool) + tile + ((size_t)c * kBlockSize + off) * 16, k);
+  st16(reinterpret_cast<uint8_t*>(prm.vpool) + tile + (size_t)off * D + (size_t)c * 16, v);
+}
+
+template <int D>
+hipError_t launch_append_fp8(const AppendParams& prm, hipStream_t stream, const KernelTimer& timer) {
+  const long threads = (long)prm.num_tokens * prm.num_kv_heads * (D / 16);
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  timer.begin(KernelKind::kAppend, stream);
+  hipLaunchKernelGGL((append_fp8_kernel<D>), dim3(grid), dim3(256), 0, stream, prm);
+  timer.end(KernelKind::kAppend, stream);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_append_t(const AppendParams& prm, hipStream_t stream, const KernelTimer& timer) {
   constexpr int VPR = D / ElemTraits<T>::kPerVec;
@@ -57,9 +109,12 @@ hipError_t launch_append_t(const AppendParams& prm, hipStream_t stream, const Ke
 
 }  // namespace
 
-hipError_t launch_append(const AppendParams& prm, bool bf16, hipStream_t stream,
+hipError_t launch_append(const AppendParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer) {
-  if (bf16) {
+  if (type == PoolType::kFP8) {
+    if (prm.head_dim == 128) return launch_append_fp8<128>(prm, stream, timer);
+    if (prm.head_dim == 64) return launch_append_fp8<64>(prm, stream, timer);
+  } else if (type == PoolType::kBF16) {
     if (prm.head_dim == 128) return launch_append_t<uint16_t, 128>(prm, stream, timer);
     if (prm.head_dim == 64) return launch_append_t<uint16_t, 64>(prm, stream, timer);
   } else {

@@ -66,7 +66,12 @@ struct DecodeShape {
   static constexpr int kVGroup = (kBlocksPerWindow * kVInstPerBlock <= 16)
                                      ? kBlocksPerWindow
                                      : 16 / kVInstPerBlock;            // V blocks loaded at once
-  static_assert(kVecPerRow == 8 || kVecPerRow == 16 || kVecPerRow == 32, "head_dim");
+  // Queries and outputs: IoType<T> (bf16 for an e4m3 pool), kQPerVec vectors
+  // of them per pool vector.
+  using TQ = typename IoType<T>::type;
+  static constexpr int kQVecPerRow = D / ElemTraits<TQ>::kPerVec;
+  static constexpr int kQPerVec = kQVecPerRow / kVecPerRow;
+  static_assert(kVecPerRow == 4 || kVecPerRow == 8 || kVecPerRow == 16 || kVecPerRow == 32, "head_dim");
 };
 
 constexpr int kMaxBalancedSeqs = 4096;   // LDS prefix-sum capacity of the balanced kernels
@@ -81,6 +86,26 @@ __device__ __forceinline__ void dot_vec_bf16(float (&acc)[G], const Vec16& k, co
       acc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[g].w[i]),
                                                __builtin_bit_cast(bf16x2, k.w[i]), acc[g],
                                                false);
+    }
+  }
+}
+
+// 16 e4m3 codes of one key against 16 bf16 query values per head (two vectors,
+// q[0][g] then q[1][g]): codes become exact bf16 pairs for v_dot2_f32_bf16.
+template <int G>
+__device__ __forceinline__ void dot_vec_fp8(float (&acc)[G], const Vec16& k, const Vec16 (&q)[2][G]) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t k01 = fp8x2_to_bf16x2<false>(k.w[w]);
+    const uint32_t k23 = fp8x2_to_bf16x2<true>(k.w[w]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const Vec16& qv = q[w / 2][g];
+      acc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.w[2 * (w % 2)]),
+                                               __builtin_bit_cast(bf16x2, k01), acc[g], false);
+      acc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.w[2 * (w % 2) + 1]),
+                                               __builtin_bit_cast(bf16x2, k23), acc[g], false);
     }
   }
 }
@@ -115,7 +140,7 @@ __device__ __forceinline__ void set_wave_priority(int level) {
 template <typename T, int D, int G>
 struct WaveLds {
   float p[DecodeShape<T, D, G>::kTokensPerWindow][G];   // probabilities of the window
-  Vec16 q[G][DecodeShape<T, D, G>::kVecPerRow];          // the group's query rows
+  Vec16 q[G][DecodeShape<T, D, G>::kQVecPerRow];         // the group's query rows
 };
 
 // Running online-softmax summary of one segment, for G query heads. m is
@@ -135,7 +160,8 @@ struct DecodeArgs {
   const int32_t* block_tables;
   int hkv;
   int max_blocks;
-  float scale_log2;
+  float scale_log2;        // softmax scale * log2(e) (* the K scale of an e4m3 pool)
+  float v_scale;           // e4m3 pools: the layer's V scale; else 1
 };
 
 // Accumulate tokens [tok_begin, tok_end) of (b, h) into a fresh summary.
@@ -154,7 +180,10 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
   constexpr int BPW = S::kBlocksPerWindow;
   constexpr int KG = S::kKGroup;
   constexpr int VB = S::kVGroup;
-  const T* __restrict__ query = static_cast<const T*>(a.query);
+  constexpr int QV = S::kQVecPerRow;
+  constexpr int QPK = S::kQPerVec;
+  using TQ = typename S::TQ;
+  const TQ* __restrict__ query = static_cast<const TQ*>(a.query);
   const T* __restrict__ kpool = static_cast<const T*>(a.kpool);
   const T* __restrict__ vpool = static_cast<const T*>(a.vpool);
 
@@ -173,8 +202,9 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
 
   wave_lds_sync();   // the wave's previous segment may still be reading q / p
   {
-    const T* qbase = query + ((size_t)b * hq + (size_t)h * G) * D;
-    for (int i = lane; i < G * VPR; i += kWave) lds.q[i / VPR][i % VPR] = ld16(qbase + (size_t)i * EPV);
+    const TQ* qbase = query + ((size_t)b * hq + (size_t)h * G) * D;
+    for (int i = lane; i < G * QV; i += kWave)
+      lds.q[i / QV][i % QV] = ld16(qbase + (size_t)i * ElemTraits<TQ>::kPerVec);
   }
 
   const size_t tile = (size_t)kBlockSize * D;           // elements per (block, head) tile
@@ -226,20 +256,31 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
       Vec16 kv[KG];
 #pragma unroll
       for (int c = 0; c < KG; ++c) kv[c] = ld16_stream(kt + (c0 + c) * (kBlockSize * 16));
-      Vec16 qcur[G], qnext[G];
+      // Query vectors (c0 + c) * QPK + j pair with key vector c0 + c.
+      Vec16 qcur[QPK][G], qnext[QPK][G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) qcur[g] = lds.q[g][c0 + qz];
+      for (int j = 0; j < QPK; ++j) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) qcur[j][g] = lds.q[g][c0 * QPK + j + qz];
+      }
 #pragma unroll
       for (int c = 0; c < KG; ++c) {
         if (c + 1 < KG) {
 #pragma unroll
-          for (int g = 0; g < G; ++g) qnext[g] = lds.q[g][c0 + c + 1 + qz];
+          for (int j = 0; j < QPK; ++j) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) qnext[j][g] = lds.q[g][(c0 + c + 1) * QPK + j + qz];
+          }
         }
-        if constexpr (EPV == 8) dot_vec_bf16<G>(acc, kv[c], qcur);
-        else dot_vec_f32<G>(acc, kv[c], qcur);
+        if constexpr (EPV == 16) dot_vec_fp8<G>(acc, kv[c], qcur);
+        else if constexpr (EPV == 8) dot_vec_bf16<G>(acc, kv[c], qcur[0]);
+        else dot_vec_f32<G>(acc, kv[c], qcur[0]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int g = 0; g < G; ++g) qcur[g] = qnext[g];
+        for (int j = 0; j < QPK; ++j) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) qcur[j][g] = qnext[j][g];
+        }
       }
     }
     const bool kvalid = (t0 + lane) < tok_end;
@@ -320,29 +361,36 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
   return st;
 }
 
-// Final rows: out[g] = o[g] / l[g], rounded to T. out_row points at query head 0 of the group.
+// Final rows: out[g] = v_scale * o[g] / l[g], rounded to the output type.
+// out_row points at query head 0 of the group.
 template <typename T, int D, int G>
-__device__ __forceinline__ void write_rows(T* out_row, const Summary<G, ElemTraits<T>::kPerVec>& st) {
+__device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row,
+                                           const Summary<G, ElemTraits<T>::kPerVec>& st, float v_scale) {
+  using TQ = typename IoType<T>::type;
   constexpr int EPV = ElemTraits<T>::kPerVec;
+  constexpr int EPQ = ElemTraits<TQ>::kPerVec;
   constexpr int VPR = D / EPV;
   const int lane = threadIdx.x & 63;
   if (lane < VPR) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float r[EPV];
-      const float inv = 1.0f / st.l[g];
+      const float inv = v_scale / st.l[g];
 #pragma unroll
       for (int e = 0; e < EPV; ++e) r[e] = st.o[g][e] * inv;
-      st16(out_row + (size_t)g * D + (size_t)lane * EPV, narrow<T>(r));
+#pragma unroll
+      for (int j = 0; j < EPV / EPQ; ++j)
+        st16(out_row + (size_t)g * D + (size_t)lane * EPV + j * EPQ, narrow<TQ>(r + j * EPQ));
     }
   }
 }
 
 // Partial summary: (m, l) of head g at ml[g * ml_stride], unnormalized o at o_base + g * o_stride.
+// The partial output is stored times v_scale, so the reduction needs no scale.
 template <typename T, int D, int G>
 __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base,
                                               size_t o_stride,
-                                              const Summary<G, ElemTraits<T>::kPerVec>& st) {
+                                              const Summary<G, ElemTraits<T>::kPerVec>& st, float v_scale) {
   constexpr int EPV = ElemTraits<T>::kPerVec;
   constexpr int VPR = D / EPV;
   const int lane = threadIdx.x & 63;
@@ -352,7 +400,8 @@ __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, floa
       float* wo = o_base + g * o_stride + (size_t)lane * EPV;
 #pragma unroll
       for (int e = 0; e < EPV; e += 4)
-        *reinterpret_cast<float4*>(wo + e) = make_float4(st.o[g][e], st.o[g][e + 1], st.o[g][e + 2], st.o[g][e + 3]);
+        *reinterpret_cast<float4*>(wo + e) = make_float4(st.o[g][e] * v_scale, st.o[g][e + 1] * v_scale,
+                                                         st.o[g][e + 2] * v_scale, st.o[g][e + 3] * v_scale);
     }
   }
   if (lane == 0) {
@@ -372,9 +421,10 @@ constexpr int decode_waves_per_simd() {
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_partition_kernel(
-    T* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
+    typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
-  constexpr int EPV = ElemTraits<T>::kPerVec;
+  using TQ = typename IoType<T>::type;
+  constexpr int EPV = ElemTraits<TQ>::kPerVec;
   __shared__ WaveLds<T, D, G> lds[4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
@@ -390,7 +440,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
 
   const int ctx = context_lens[b];
   const size_t qh0 = (size_t)b * args.hkv * G + (size_t)h * G;
-  T* out_row = out_ptr + qh0 * D;
+  TQ* out_row = out_ptr + qh0 * D;
   if (ctx <= 0) {
     // Defined result for an empty context: a zero row (written by partition 0).
     if (part == 0) {
@@ -404,10 +454,11 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   int done = 0;
   const auto st = run_segment<T, D, G>(args, lds[wave], b, h, tok_begin, tok_end, done, 0);
   if (ctx <= prm.part_tokens) {
-    write_rows<T, D, G>(out_row, st);
+    write_rows<T, D, G>(out_row, st, args.v_scale);
   } else {
     write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + qh0 * prm.max_parts + part, prm.max_parts,
-                           ws_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st);
+                           ws_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st,
+                           args.v_scale);
   }
 }
 
@@ -555,7 +606,7 @@ struct alignas(16) SlotDesc {
 
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_balanced_kernel(
-    T* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
+    typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     SlotDesc* __restrict__ ws_desc, const int32_t* __restrict__ context_lens, DecodeArgs args,
     DecodeParams prm) {
   __shared__ WaveLds<T, D, G> lds[4];
@@ -564,11 +615,12 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   const int total = window_prefix_sum(context_lens, prm.num_seqs, args.hkv, cum, scan_scratch);
 
   // Defined result for empty contexts: zero rows, spread over the workgroups.
-  constexpr int EPV = ElemTraits<T>::kPerVec;
+  using TQ = typename IoType<T>::type;
+  constexpr int EPV = ElemTraits<TQ>::kPerVec;
   const size_t seq_vecs = (size_t)args.hkv * G * D / EPV;
   for (int b = blockIdx.x; b < prm.num_seqs; b += gridDim.x) {
     if (cum[b + 1] != cum[b]) continue;
-    T* o = out_ptr + (size_t)b * seq_vecs * EPV;
+    TQ* o = out_ptr + (size_t)b * seq_vecs * EPV;
     for (size_t i = threadIdx.x; i < seq_vecs; i += blockDim.x) st16(o + i * EPV, zero16());
   }
 
@@ -599,12 +651,12 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
     const auto st = run_segment<T, D, G>(args, lds[wave], b, h, w0 * 64, min(ctx, w1 * 64), done, x1 - x0);
     const size_t qh0 = (size_t)b * args.hkv * G + (size_t)h * G;
     if (w0 == 0 && w1 == nwb) {
-      write_rows<T, D, G>(out_ptr + qh0 * D, st);
+      write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale);
     } else {
       // Slot 0 holds the share's first segment, slot 1 its last one.
       const int slot = (x == x0) ? 0 : 1;
       const size_t base = ((size_t)wid * 2 + slot) * G;
-      write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st);
+      write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st, args.v_scale);
       desc[slot].row = b * args.hkv + h;
       desc[slot].row_start = x - w0;
       desc[slot].w0 = w0;
@@ -703,9 +755,10 @@ __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
 
 template <typename T, int D, int G>
 hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
+  using TQ = typename IoType<T>::type;
   const DecodeArgs args{prm.query, prm.kpool, prm.vpool, prm.block_tables, prm.num_kv_heads,
-                        prm.max_blocks, prm.scale_log2};
-  T* out = static_cast<T*>(prm.out);
+                        prm.max_blocks, prm.scale_log2, prm.v_scale};
+  TQ* out = static_cast<TQ*>(prm.out);
   hipError_t err;
   if (prm.num_waves > 0) {
     timer.begin(KernelKind::kDecodePartition, stream);
@@ -715,7 +768,7 @@ hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const K
     timer.end(KernelKind::kDecodePartition, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     timer.begin(KernelKind::kDecodeReduce, stream);
-    hipLaunchKernelGGL((decode_balanced_reduce_kernel<T, D, G>), dim3((unsigned)((prm.num_waves + 3) / 4)),
+    hipLaunchKernelGGL((decode_balanced_reduce_kernel<TQ, D, G>), dim3((unsigned)((prm.num_waves + 3) / 4)),
                        dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, desc, prm);
     timer.end(KernelKind::kDecodeReduce, stream);
     return hipGetLastError();
@@ -729,7 +782,7 @@ hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const K
   if (prm.max_parts > 1) {
     const long pairs = (long)prm.num_seqs * prm.num_kv_heads * G;
     timer.begin(KernelKind::kDecodeReduce, stream);
-    hipLaunchKernelGGL((decode_reduce_kernel<T, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256),
+    hipLaunchKernelGGL((decode_reduce_kernel<TQ, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256),
                        0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, prm);
     timer.end(KernelKind::kDecodeReduce, stream);
     err = hipGetLastError();
@@ -789,14 +842,20 @@ int decode_balanced_max_seqs() { return kMaxBalancedSeqs; }
 
 size_t decode_balanced_desc_bytes() { return sizeof(SlotDesc); }
 
-int decode_balanced_waves_per_cu(bool bf16, int head_dim, int group) {
-  if (bf16) return head_dim == 128 ? waves_per_cu_t<uint16_t, 128>(group) : waves_per_cu_t<uint16_t, 64>(group);
+int decode_balanced_waves_per_cu(PoolType type, int head_dim, int group) {
+  if (type == PoolType::kFP8)
+    return head_dim == 128 ? waves_per_cu_t<uint8_t, 128>(group) : waves_per_cu_t<uint8_t, 64>(group);
+  if (type == PoolType::kBF16)
+    return head_dim == 128 ? waves_per_cu_t<uint16_t, 128>(group) : waves_per_cu_t<uint16_t, 64>(group);
   return head_dim == 128 ? waves_per_cu_t<float, 128>(group) : waves_per_cu_t<float, 64>(group);
 }
 
-hipError_t launch_decode(const DecodeParams& prm, bool bf16, hipStream_t stream,
+hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer) {
-  if (bf16) {
+  if (type == PoolType::kFP8) {
+    if (prm.head_dim == 128) return launch_decode_t<uint8_t, 128>(prm, stream, timer);
+    if (prm.head_dim == 64) return launch_decode_t<uint8_t, 64>(prm, stream, timer);
+  } else if (type == PoolType::kBF16) {
     if (prm.head_dim == 128) return launch_decode_t<uint16_t, 128>(prm, stream, timer);
     if (prm.head_dim == 64) return launch_decode_t<uint16_t, 64>(prm, stream, timer);
   } else {

@@ -10,10 +10,17 @@ namespace pkv {
 constexpr int kBlockSize = 16;   // tokens per KV block
 constexpr int kWave = 64;        // CDNA wavefront width
 
-// bf16 is carried as raw uint16_t bits; fp32 as float.
+// bf16 is carried as raw uint16_t bits, fp32 as float, and 8-bit KV-cache
+// codes (OCP e4m3, the format gfx950 converts natively) as uint8_t.
 template <typename T> struct ElemTraits;
 template <> struct ElemTraits<float> { static constexpr int kPerVec = 4; };
 template <> struct ElemTraits<uint16_t> { static constexpr int kPerVec = 8; };
+template <> struct ElemTraits<uint8_t> { static constexpr int kPerVec = 16; };
+
+// Tensors passed alongside a pool of T (queries, outputs, new K/V rows): the
+// pool's own type, except that an e4m3 pool works with bf16 tensors.
+template <typename T> struct IoType { using type = T; };
+template <> struct IoType<uint8_t> { using type = uint16_t; };
 
 struct alignas(16) Vec16 { uint32_t w[4]; };
 
@@ -56,6 +63,48 @@ template <> __device__ __forceinline__ void widen<float>(const Vec16& v, float* 
   for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v.w[i]);
 }
 
+// e4m3 codes: 16 per vector, widened exactly (every e4m3 value is an f32).
+typedef float pkv_f32x2 __attribute__((ext_vector_type(2)));
+template <> __device__ __forceinline__ void widen<uint8_t>(const Vec16& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const pkv_f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.w[i], false);
+    const pkv_f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.w[i], true);
+    f[4 * i] = a.x; f[4 * i + 1] = a.y; f[4 * i + 2] = b.x; f[4 * i + 3] = b.y;
+  }
+}
+
+// Two e4m3 codes (bytes 0, 1 of w, or 2, 3 with kHigh) as a bf16 pair, exactly: an
+// e4m3 value has at most 4 significant bits, so its f32 form is a bf16 value
+// whose low 16 bits are zero; the byte permute keeps the high halves.
+template <bool kHigh>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  const pkv_f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHigh);
+  return __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
+}
+
+// e4m3 code pair of (a, b) * inv_scale: the fp32 products are clamped to
+// +-448 (out-of-range values saturate; NaN stays NaN) and rounded to nearest
+// even by the hardware conversion. Returns `old` with its low 16 bits (or its
+// high 16 bits, with kHigh) replaced by the pair, first value in the lower byte.
+__device__ __forceinline__ float e4m3_saturate(float y) {
+  return y != y ? y : fminf(fmaxf(y, -448.0f), 448.0f);
+}
+// The converter gives NaN one code whatever its sign. A NaN input x (the only
+// way to a NaN product, 1/scale being finite and positive) is coded
+// S.1111.111 with S the sign bit of x.
+__device__ __forceinline__ uint32_t e4m3_nan_fix(uint32_t w, float x, int shift) {
+  const uint32_t nan_code = (__float_as_uint(x) >> 31) ? 0xFFu : 0x7Fu;
+  return x != x ? (w & ~(0xFFu << shift)) | (nan_code << shift) : w;
+}
+template <bool kHigh>
+__device__ __forceinline__ uint32_t f32x2_to_fp8x2(float a, float b, float inv_scale, uint32_t old) {
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_saturate(a * inv_scale),
+                                                         e4m3_saturate(b * inv_scale), (int)old, kHigh);
+  w = e4m3_nan_fix(w, a, kHigh ? 16 : 0);
+  return e4m3_nan_fix(w, b, kHigh ? 24 : 8);
+}
+
 // Narrow kPerVec floats into one 16-byte vector of T.
 template <typename T> __device__ __forceinline__ Vec16 narrow(const float* f);
 template <> __device__ __forceinline__ Vec16 narrow<uint16_t>(const float* f) {
@@ -80,6 +129,7 @@ constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowRor4 = 0x124;      // row_ror:4 inside a 16-lane row
 constexpr int kDppRowRor8 = 0x128;      // row_ror:8 == lane ^ 8 inside a 16-lane row
 
 template <int Ctrl>
@@ -129,9 +179,12 @@ __device__ __forceinline__ float wave_max(float x) { return xor32_max(xor16_max(
 __device__ __forceinline__ float wave_sum(float x) { return xor32_sum(xor16_sum(row_sum(x))); }
 
 // Sum over the lanes l, l ^ (1 << k) for every k with (1 << k) >= Stride,
-// i.e. over all lanes that share (l % Stride). Stride in {8, 16, 32, 64}.
+// i.e. over all lanes that share (l % Stride). Stride in {4, 8, 16, 32, 64}.
+// (Stride 4: rotating a 16-lane row by 4 and then by 8 visits l, l+4, l+8, l+12.)
 template <int Stride>
 __device__ __forceinline__ float sum_lanes_above(float x) {
+  static_assert(Stride == 4 || Stride == 8 || Stride == 16 || Stride == 32 || Stride == 64, "stride");
+  if constexpr (Stride <= 4) x += dpp<kDppRowRor4>(x);
   if constexpr (Stride <= 8) x += dpp<kDppRowRor8>(x);
   if constexpr (Stride <= 16) x = xor16_sum(x);
   if constexpr (Stride <= 32) x = xor32_sum(x);

@@ -23,6 +23,8 @@ struct pkv_pool {
   pkv_dtype dtype;
   std::vector<void*> k_layers;
   std::vector<void*> v_layers;
+  std::vector<float> k_scale;   // e4m3 pools: per-layer dequantization scales (1 otherwise)
+  std::vector<float> v_scale;
 };
 
 namespace {
@@ -45,14 +47,18 @@ pkv_status hip_fail(hipError_t err, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-size_t elem_bytes(pkv_dtype dt) { return dt == PKV_BF16 ? 2 : 4; }
+size_t elem_bytes(pkv_dtype dt) { return dt == PKV_FP8_E4M3 ? 1 : dt == PKV_BF16 ? 2 : 4; }
+
+pkv::PoolType pool_type(pkv_dtype dt) {
+  return dt == PKV_FP8_E4M3 ? pkv::PoolType::kFP8 : dt == PKV_BF16 ? pkv::PoolType::kBF16 : pkv::PoolType::kF32;
+}
 
 pkv_status check_geometry(int num_blocks, int block_size, int num_kv_heads, int head_dim,
                           pkv_dtype dtype) {
   if (num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive (got %d)", num_blocks);
   if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be positive (got %d)", num_kv_heads);
   if (block_size <= 0 || head_dim <= 0) return fail(PKV_ERR_INVALID_ARG, "block_size and head_dim must be positive");
-  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_FP8_E4M3) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (block_size != pkv::kPoolBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
   if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
   return PKV_OK;
@@ -225,7 +231,28 @@ pkv_status kv_pool_create(pkv_pool** out, int num_layers, int num_blocks, int bl
   p->dtype = dtype;
   p->k_layers.assign(k_layers, k_layers + num_layers);
   p->v_layers.assign(v_layers, v_layers + num_layers);
+  p->k_scale.assign(num_layers, 1.0f);
+  p->v_scale.assign(num_layers, 1.0f);
   *out = p;
+  return PKV_OK;
+}
+
+pkv_status kv_pool_set_fp8_scales(pkv_pool* pool, int num_layers, const float* k_scales,
+                                  const float* v_scales) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (pool->dtype != PKV_FP8_E4M3) return fail(PKV_ERR_INVALID_ARG, "scales apply to e4m3 pools only");
+  if (num_layers != pool->num_layers)
+    return fail(PKV_ERR_INVALID_ARG, "%d scales given for a pool of %d layers", num_layers, pool->num_layers);
+  if (!k_scales || !v_scales) return fail(PKV_ERR_INVALID_ARG, "k_scales and v_scales must not be NULL");
+  for (int l = 0; l < pool->num_layers; ++l) {
+    const float ks = k_scales[l], vs = v_scales[l];
+    // 1/scale must be a finite, nonzero fp32 number for the append's quantization.
+    if (!(std::isfinite(ks) && std::isfinite(vs) && ks > 0.0f && vs > 0.0f &&
+          std::isfinite(1.0f / ks) && std::isfinite(1.0f / vs) && 1.0f / ks > 0.0f && 1.0f / vs > 0.0f))
+      return fail(PKV_ERR_INVALID_ARG, "layer %d: scales must be positive, finite and have a finite, nonzero inverse", l);
+  }
+  pool->k_scale.assign(k_scales, k_scales + pool->num_layers);
+  pool->v_scale.assign(v_scales, v_scales + pool->num_layers);
   return PKV_OK;
 }
 
@@ -244,12 +271,15 @@ pkv_status reshape_and_cache(const pkv_pool* pool, int layer, const void* key,
   if (!key || !value || !slot_mapping) return fail(PKV_ERR_INVALID_ARG, "key, value and slot_mapping must not be NULL");
   if (!aligned(key, 16) || !aligned(value, 16)) return fail(PKV_ERR_INVALID_ARG, "key/value must be 16-byte aligned");
   if (!aligned(slot_mapping, 8)) return fail(PKV_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
-  const long threads = (long)num_tokens * pool->num_kv_heads * pool->head_dim * elem_bytes(pool->dtype) / 16;
+  // One thread per 16-byte vector of the input rows (per 16 codes of an e4m3 pool).
+  const long threads = (long)num_tokens * pool->num_kv_heads * pool->head_dim /
+                       (pool->dtype == PKV_F32 ? 4 : pool->dtype == PKV_BF16 ? 8 : 16);
   if (threads >= (1L << 32) - 256) return fail(PKV_ERR_UNSUPPORTED, "too many tokens in one call");
   pkv::AppendParams prm{pool->k_layers[layer], pool->v_layers[layer], key, value, slot_mapping,
-                        num_tokens, pool->num_kv_heads, pool->head_dim};
+                        num_tokens, pool->num_kv_heads, pool->head_dim,
+                        1.0f / pool->k_scale[layer], 1.0f / pool->v_scale[layer]};
   (void)hipGetLastError();
-  hipError_t err = pkv::launch_append(prm, pool->dtype == PKV_BF16, (hipStream_t)stream, pkv::KernelTimer{});
+  hipError_t err = pkv::launch_append(prm, pool_type(pool->dtype), (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "reshape_and_cache launch");
   return PKV_OK;
 }
@@ -308,10 +338,10 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
     if (workspace_bytes < need)
       return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
   }
-  const bool bf16 = pool->dtype == PKV_BF16;
+  const pkv::PoolType type = pool_type(pool->dtype);
   int num_waves = 0;
   if (sp.balanced) {
-    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(bf16, pool->head_dim, group);
+    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, group);
     num_waves = (int)std::max(1L, std::min(sp.wave_cap, slots));
   } else {
     const long units = (long)pool->num_kv_heads * num_seqs * sp.max_parts;
@@ -326,9 +356,10 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
   pkv::DecodeParams prm{out, ws_ml, ws_o, ws_desc, query, pool->k_layers[layer], pool->v_layers[layer],
                         block_tables, context_lens, num_seqs, pool->num_kv_heads, group,
                         pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
-                        num_waves, scale * 1.4426950408889634f};
+                        num_waves, scale * 1.4426950408889634f * pool->k_scale[layer],
+                        pool->v_scale[layer]};
   (void)hipGetLastError();
-  hipError_t err = pkv::launch_decode(prm, bf16, (hipStream_t)stream, pkv::KernelTimer{});
+  hipError_t err = pkv::launch_decode(prm, type, (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "paged_attention_decode launch");
   return PKV_OK;
 }
@@ -341,7 +372,8 @@ pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* 
                                          int max_blocks_per_seq, float scale, void* stream) {
   pkv_status st = check_pool_layer(pool, layer);
   if (st != PKV_OK) return st;
-  if (pool->dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill chunks run on bf16 MFMA: bf16 pools only");
+  if (pool->dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill chunks run on bf16 MFMA: bf16 and e4m3 pools only");
   if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs, total_q_tokens and max_q_len must be >= 0");
   if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
@@ -361,9 +393,9 @@ pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* 
   pkv::PrefillParams prm{out, query, pool->k_layers[layer], pool->v_layers[layer], cu_q_lens,
                          block_tables, context_lens, num_seqs, total_q_tokens, max_q_len,
                          pool->num_kv_heads, group, pool->head_dim, max_blocks_per_seq,
-                         scale * 1.4426950408889634f};
+                         scale * 1.4426950408889634f * pool->k_scale[layer], pool->v_scale[layer]};
   (void)hipGetLastError();
-  hipError_t err = pkv::launch_prefill(prm, (hipStream_t)stream, pkv::KernelTimer{});
+  hipError_t err = pkv::launch_prefill(prm, pool_type(pool->dtype), (hipStream_t)stream, pkv::KernelTimer{});
   if (err == hipErrorNotSupported) return fail(PKV_ERR_UNSUPPORTED, "prefill geometry not supported");
   if (err != hipSuccess) return hip_fail(err, "paged_attention_prefill_chunk launch");
   return PKV_OK;

@@ -17,6 +17,9 @@ struct KernelTimer {
   void end(KernelKind kind, hipStream_t stream) const;
 };
 
+// Element type of a pool (the values match pkv_dtype).
+enum class PoolType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
 struct AppendParams {
   void* kpool;
   void* vpool;
@@ -26,6 +29,8 @@ struct AppendParams {
   int num_tokens;
   int num_kv_heads;
   int head_dim;
+  float k_inv_scale;       // e4m3 pools: 1 / the layer's K scale (fp32)
+  float v_inv_scale;       // e4m3 pools: 1 / the layer's V scale (fp32)
 };
 
 struct DecodeParams {
@@ -46,7 +51,8 @@ struct DecodeParams {
   int part_tokens;         // fixed partitions: tokens per partition (multiple of 64)
   int max_parts;           // fixed partitions: partitions of the longest possible sequence
   int num_waves;           // > 0: balanced split over this many wavefronts
-  float scale_log2;        // scale * log2(e)
+  float scale_log2;        // scale * log2(e), times the K scale of an e4m3 pool
+  float v_scale;           // e4m3 pools: the V scale; else 1
 };
 
 struct PrefillParams {
@@ -64,18 +70,19 @@ struct PrefillParams {
   int group;
   int head_dim;
   int max_blocks;
-  float scale_log2;
+  float scale_log2;        // scale * log2(e), times the K scale of an e4m3 pool
+  float v_scale;           // e4m3 pools: the V scale; else 1
 };
 
-hipError_t launch_append(const AppendParams& prm, bool bf16, hipStream_t stream,
+hipError_t launch_append(const AppendParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer);
-hipError_t launch_decode(const DecodeParams& prm, bool bf16, hipStream_t stream,
+hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer);
 // Balanced decode: resident wavefronts per CU of its kernel, the largest
 // batch its in-LDS prefix sum handles, and the size of one slot descriptor.
-int decode_balanced_waves_per_cu(bool bf16, int head_dim, int group);
+int decode_balanced_waves_per_cu(PoolType type, int head_dim, int group);
 int decode_balanced_max_seqs();
 size_t decode_balanced_desc_bytes();
-hipError_t launch_prefill(const PrefillParams& prm, hipStream_t stream, const KernelTimer& timer);
+hipError_t launch_prefill(const PrefillParams& prm, PoolType type, hipStream_t stream, const KernelTimer& timer);
 
 }  // namespace pkv

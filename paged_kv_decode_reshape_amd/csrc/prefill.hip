@@ -84,10 +84,12 @@ union PrefillLds {
   } merge;
 };
 
-template <int D, int G>
+// TP: the pool's element type, bf16 bits (uint16_t) or e4m3 codes (uint8_t);
+// queries, outputs and the LDS tiles are bf16 either way.
+template <int D, int G, typename TP>
 __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G)) void prefill_chunk_kernel(
-    uint16_t* __restrict__ out, const uint16_t* __restrict__ query, const uint16_t* __restrict__ kpool,
-    const uint16_t* __restrict__ vpool, const int32_t* __restrict__ cu_q_lens,
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ query, const TP* __restrict__ kpool,
+    const TP* __restrict__ vpool, const int32_t* __restrict__ cu_q_lens,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     PrefillParams prm) {
   constexpr int RT = prefill_row_subtiles(G);
@@ -182,17 +184,48 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   constexpr bool kAllSlots = NT * PER == NG * kVecs;   // every thread's slots hold a vector
   static_assert(kBlockVecs % kWave == 0, "a wavefront's vectors must share a block");
   const int wave_vec0 = w * kWave;
-  const uint32_t lane_k = (uint32_t)lane * 16u;                                   // K: byte offset of the lane
-  const uint32_t lane_vg = (uint32_t)((lane / VPR) * D + (lane % VPR) * 8) * 2u;  // V in the pool tile
+  // An e4m3 pool is staged 8 codes (8 bytes) per LDS vector and widened to
+  // bf16 (exactly) when stored to LDS. Its K tile is [D/16][16][16]: LDS
+  // vector (c8, token tin) reads 8 bytes at ((c8/2)*16 + tin)*16 + (c8%2)*8.
+  constexpr bool kF8 = sizeof(TP) == 1;
+  constexpr int SW = kF8 ? 2 : 4;                                                  // staged words per vector
+  const uint32_t lane_k = (uint32_t)lane * 16u;                                   // K in LDS (and a bf16 pool)
+  const uint32_t lane_kg = kF8 ? (uint32_t)((((lane >> 5) * 16 + (lane & 15)) * 16) + ((lane >> 4) & 1) * 8)
+                               : lane_k;                                          // K in the pool tile
+  const uint32_t lane_vg = (uint32_t)((lane / VPR) * D + (lane % VPR) * 8) * (uint32_t)sizeof(TP);  // V in the pool tile
   const uint32_t lane_vl = (uint32_t)((lane / VPR) * PrefillLds<D, NWG, NG>::kVStride + (lane % VPR) * 8) * 2u;  // V in LDS
   const int lane_tok = lane / VPR;                                                // V: token offset of the lane
   char* const lds_k = reinterpret_cast<char*>(&lds.tile.k[0][0][0]);
   char* const lds_v = reinterpret_cast<char*>(&lds.tile.v[0][0][0]);
   // A slot whose block is not read keeps its previous contents: stale K rows
   // are masked, and V rows past the range are cleared when stored.
-  Vec16 kreg[PER], vreg[PER];
+  struct Stage { uint32_t w[SW]; };
+  Stage kreg[PER], vreg[PER];
 #pragma unroll
-  for (int u = 0; u < PER; ++u) kreg[u] = vreg[u] = zero16();
+  for (int u = 0; u < PER; ++u) {
+#pragma unroll
+    for (int i = 0; i < SW; ++i) kreg[u].w[i] = vreg[u].w[i] = 0u;
+  }
+  auto ld_stage = [](const char* p) {
+    Stage r;
+    if constexpr (kF8) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      r.w[0] = v.x; r.w[1] = v.y;
+    } else {
+      const Vec16 v = ld16(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.w[i] = v.w[i];
+    }
+    return r;
+  };
+  auto to_bf16 = [](const Stage& r) {
+    if constexpr (kF8) {
+      return make_uint4(fp8x2_to_bf16x2<false>(r.w[0]), fp8x2_to_bf16x2<true>(r.w[0]),
+                        fp8x2_to_bf16x2<false>(r.w[1]), fp8x2_to_bf16x2<true>(r.w[1]));
+    } else {
+      return make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
+    }
+  };
   auto step_ids = [&](int j, int (&ids)[PER]) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -209,12 +242,12 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
       const int qq0 = q0 % kVecs;
       const int key0 = j * NG * kKeyTile + (q0 / kBlockVecs) * kBlockSize;   // first key of the block
       if (key0 < kv_end) {                                 // uniform: blocks past the range are not read
-        const size_t base = ((size_t)ids[u] * blk_stride + head_off) * sizeof(uint16_t);
+        const size_t base = ((size_t)ids[u] * blk_stride + head_off) * sizeof(TP);
         const char* kb = reinterpret_cast<const char*>(kpool) + base;
         const char* vb = reinterpret_cast<const char*>(vpool) + base;
-        kreg[u] = ld16(kb + (uint32_t)(qq0 % kBlockVecs) * 16u + lane_k);
+        kreg[u] = ld_stage(kb + (uint32_t)(qq0 % kBlockVecs) * (uint32_t)(8 * sizeof(TP)) + lane_kg);
         const int tok0 = (qq0 / VPR) % kBlockSize;         // uniform
-        vreg[u] = ld16(vb + (uint32_t)(tok0 * D * 2) + lane_vg);
+        vreg[u] = ld_stage(vb + (uint32_t)(tok0 * D * (int)sizeof(TP)) + lane_vg);
       }
     }
   };
@@ -228,11 +261,13 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
       const int t = q0 / kVecs, qq0 = q0 % kVecs;
       const int key0 = j * NG * kKeyTile + (q0 / kBlockVecs) * kBlockSize;   // first key of the block
       const int tok0 = (qq0 / VPR) % kBlockSize;
-      if (key0 + tok0 + lane_tok >= kv_end) vreg[u] = zero16();
-      *reinterpret_cast<uint4*>(lds_k + (uint32_t)(t * (kKeyTile * D) + qq0 * 8) * 2u + lane_k) =
-          make_uint4(kreg[u].w[0], kreg[u].w[1], kreg[u].w[2], kreg[u].w[3]);
+      if (key0 + tok0 + lane_tok >= kv_end) {
+#pragma unroll
+        for (int i = 0; i < SW; ++i) vreg[u].w[i] = 0u;
+      }
+      *reinterpret_cast<uint4*>(lds_k + (uint32_t)(t * (kKeyTile * D) + qq0 * 8) * 2u + lane_k) = to_bf16(kreg[u]);
       *reinterpret_cast<uint4*>(lds_v + (uint32_t)((t * kKeyTile + qq0 / VPR) * PrefillLds<D, NWG, NG>::kVStride) * 2u +
-                                lane_vl) = make_uint4(vreg[u].w[0], vreg[u].w[1], vreg[u].w[2], vreg[u].w[3]);
+                                lane_vl) = to_bf16(vreg[u]);
     }
   };
 
@@ -384,7 +419,7 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   // ---- normalize and store: lane writes row col, d = 16n + 4*quad .. +4 ----
   if (my_row < T) {
     uint16_t* orow = out + ((size_t)(q_lo + my_row) * hq + qh) * D;
-    const float inv = 1.0f / lt;
+    const float inv = prm.v_scale / lt;
 #pragma unroll
     for (int n = 0; n < NTILES; ++n) {
       float r[4];
@@ -400,40 +435,47 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   }
 }
 
-template <int D, int G>
+template <int D, int G, typename TP>
 hipError_t launch_prefill_dg(const PrefillParams& prm, hipStream_t stream) {
   constexpr int RT = prefill_row_subtiles(G);
   const dim3 grid((unsigned)((prm.max_q_len + kQRows * RT - 1) / (kQRows * RT)), (unsigned)prm.num_kv_heads,
                   (unsigned)prm.num_seqs);
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, G>), grid, dim3(64 * G * RT * prefill_groups(G)), 0, stream,
+  hipLaunchKernelGGL((prefill_chunk_kernel<D, G, TP>), grid, dim3(64 * G * RT * prefill_groups(G)), 0, stream,
                      static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
-                     static_cast<const uint16_t*>(prm.kpool), static_cast<const uint16_t*>(prm.vpool),
+                     static_cast<const TP*>(prm.kpool), static_cast<const TP*>(prm.vpool),
                      prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename TP>
 hipError_t launch_prefill_d(const PrefillParams& prm, hipStream_t stream) {
   switch (prm.group) {
-    case 1: return launch_prefill_dg<D, 1>(prm, stream);
-    case 2: return launch_prefill_dg<D, 2>(prm, stream);
-    case 3: return launch_prefill_dg<D, 3>(prm, stream);
-    case 4: return launch_prefill_dg<D, 4>(prm, stream);
-    case 5: return launch_prefill_dg<D, 5>(prm, stream);
-    case 6: return launch_prefill_dg<D, 6>(prm, stream);
-    case 7: return launch_prefill_dg<D, 7>(prm, stream);
-    case 8: return launch_prefill_dg<D, 8>(prm, stream);
+    case 1: return launch_prefill_dg<D, 1, TP>(prm, stream);
+    case 2: return launch_prefill_dg<D, 2, TP>(prm, stream);
+    case 3: return launch_prefill_dg<D, 3, TP>(prm, stream);
+    case 4: return launch_prefill_dg<D, 4, TP>(prm, stream);
+    case 5: return launch_prefill_dg<D, 5, TP>(prm, stream);
+    case 6: return launch_prefill_dg<D, 6, TP>(prm, stream);
+    case 7: return launch_prefill_dg<D, 7, TP>(prm, stream);
+    case 8: return launch_prefill_dg<D, 8, TP>(prm, stream);
     default: return hipErrorNotSupported;
   }
 }
 
+template <typename TP>
+hipError_t launch_prefill_t(const PrefillParams& prm, hipStream_t stream) {
+  return prm.head_dim == 128 ? launch_prefill_d<128, TP>(prm, stream) : launch_prefill_d<64, TP>(prm, stream);
+}
+
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& prm, hipStream_t stream, const KernelTimer& timer) {
+hipError_t launch_prefill(const PrefillParams& prm, PoolType type, hipStream_t stream, const KernelTimer& timer) {
   if (prm.group < 1 || prm.group > kMaxGroup) return hipErrorNotSupported;
   if (prm.head_dim != 64 && prm.head_dim != 128) return hipErrorNotSupported;
+  if (type != PoolType::kBF16 && type != PoolType::kFP8) return hipErrorNotSupported;
   timer.begin(KernelKind::kPrefill, stream);
-  const hipError_t err = prm.head_dim == 128 ? launch_prefill_d<128>(prm, stream) : launch_prefill_d<64>(prm, stream);
+  const hipError_t err = type == PoolType::kFP8 ? launch_prefill_t<uint8_t>(prm, stream)
+                                                : launch_prefill_t<uint16_t>(prm, stream);
   timer.end(KernelKind::kPrefill, stream);
   return err;
 }

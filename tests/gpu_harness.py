@@ -15,9 +15,11 @@ import paged_kv_decode_reshape_amd as pkv
 from paged_kv_decode_reshape_amd import workloads as W
 
 DEV = "cuda:0"
-PKV_DT = {"bf16": pkv.BF16, "f32": pkv.F32}
+PKV_DT = {"bf16": pkv.BF16, "f32": pkv.F32, "fp8": pkv.FP8_E4M3}
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
-POISON_BITS = {"bf16": 0xFFFF, "f32": 0xFFFFFFFF}   # NaN patterns for never-written slots
+POISON_BITS = {"bf16": 0xFFFF, "f32": 0xFFFFFFFF, "fp8": 0xFF}   # NaN patterns for never-written slots
+POOL_BYTES = {"bf16": 2, "f32": 4, "fp8": 1}
+X = {"bf16": 8, "f32": 4, "fp8": 16}     # elements per 16-byte K vector
 
 
 def to_device(values: W.Values) -> torch.Tensor:
@@ -39,26 +41,38 @@ def to_f32(t: torch.Tensor) -> np.ndarray:
 def raw_bits(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.uint8:
+        return t.detach().cpu().numpy()
     return t.detach().view(torch.int32).cpu().numpy().view(np.uint32)
 
 
 class DevicePool:
-    """One layer of K/V pool in HBM, wrapped in a library pool handle."""
+    """K/V pools in HBM (one pair per layer), wrapped in a library pool handle.
 
-    def __init__(self, step: W.Step, num_layers: int = 1):
+    ``kv="fp8"`` makes an e4m3 pool for a bf16 step, with per-layer scales
+    ``k_scales`` / ``v_scales`` (lists, one per layer)."""
+
+    def __init__(self, step: W.Step, num_layers: int = 1, kv: str | None = None,
+                 k_scales=None, v_scales=None):
         self.step = step
         s = step
+        self.kv = s.dtype if kv is None else kv
+        assert self.kv == s.dtype or (self.kv == "fp8" and s.dtype == "bf16")
         self.elems = s.num_blocks * s.num_kv_heads * s.block_size * s.head_dim
         kb, vb = pkv.kv_pool_bytes(s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim,
-                                   PKV_DT[s.dtype])
-        assert kb == vb == self.elems * (2 if s.dtype == "bf16" else 4)
+                                   PKV_DT[self.kv])
+        assert kb == vb == self.elems * POOL_BYTES[self.kv]
         self.k = [self._poisoned() for _ in range(num_layers)]
         self.v = [self._poisoned() for _ in range(num_layers)]
         self.handle = pkv.kv_pool_create(num_layers, s.num_blocks, s.block_size, s.num_kv_heads,
-                                         s.head_dim, PKV_DT[s.dtype], self.k, self.v)
+                                         s.head_dim, PKV_DT[self.kv], self.k, self.v)
+        if k_scales is not None:
+            pkv.kv_pool_set_fp8_scales(self.handle, k_scales, v_scales)
 
     def _poisoned(self) -> torch.Tensor:
-        if self.step.dtype == "bf16":
+        if self.kv == "fp8":
+            return torch.full((self.elems,), 0xFF, dtype=torch.uint8, device=DEV)
+        if self.kv == "bf16":
             t = torch.full((self.elems,), -1, dtype=torch.int16, device=DEV)
             return t.view(torch.bfloat16)
         t = torch.full((self.elems,), -1, dtype=torch.int32, device=DEV)
@@ -125,7 +139,7 @@ class DevicePool:
     def decode_pool(self, layer: int = 0):
         """(K, V) as [num_blocks, block_size, Hkv, D] raw bit arrays."""
         s = self.step
-        x = 8 if s.dtype == "bf16" else 4
+        x = X[self.kv]
         nb, hkv, d, bs = s.num_blocks, s.num_kv_heads, s.head_dim, s.block_size
         k = raw_bits(self.k[layer]).reshape(nb, hkv, d // x, bs, x)
         k = k.transpose(0, 3, 1, 2, 4).reshape(nb, bs, hkv, d)

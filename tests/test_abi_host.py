@@ -91,3 +91,27 @@ def test_workspace_sizing_and_check():
                        512, None, nb)[0] == -4
     finally:
         pkv.kv_pool_destroy(h)
+
+
+def test_fp8_pool_bytes_and_scales():
+    assert pkv.kv_pool_bytes(10, 16, 8, 128, pkv.FP8_E4M3) == (10 * 8 * 16 * 128,) * 2
+    h = pkv.kv_pool_create(2, 4, 16, 1, 64, pkv.FP8_E4M3, [256, 512], [768, 1024])
+    try:
+        pkv.kv_pool_set_fp8_scales(h, [0.5, 2.0], [1.0, 0.01])
+        assert _status(pkv.kv_pool_set_fp8_scales, h, [1.0], [1.0])[0] == -1            # count
+        for bad in (0.0, -1.0, float("inf"), float("nan"), 1e-39):                      # 1e-39: 1/x overflows
+            st, msg = _status(pkv.kv_pool_set_fp8_scales, h, [1.0, bad], [1.0, 1.0])
+            assert st == -1 and "layer 1" in msg
+            assert _status(pkv.kv_pool_set_fp8_scales, h, [1.0, 1.0], [bad, 1.0])[0] == -1
+        # an e4m3 pool takes prefill chunks (bf16 MFMA on widened codes): only the
+        # NULL query below is rejected, not the dtype
+        st, msg = _status(pkv.paged_attention_prefill_chunk, h, 0, 16, None, 16, 16, 16, 1, 4, 4,
+                          4, 1, 1.0)
+        assert st == -1 and "NULL" in msg
+    finally:
+        pkv.kv_pool_destroy(h)
+    hb = pkv.kv_pool_create(1, 4, 16, 1, 64, pkv.BF16, [256], [512])
+    try:
+        assert _status(pkv.kv_pool_set_fp8_scales, hb, [1.0], [1.0])[0] == -1         # not an e4m3 pool
+    finally:
+        pkv.kv_pool_destroy(hb)
