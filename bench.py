@@ -9,7 +9,11 @@ pool (one library "layer" each, >= 2 GiB in total) so the 256 MB Infinity
 Cache cannot serve repeated reads.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4|5]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4|5] [--kv-dtype bf16|fp8]
+
+--kv-dtype fp8 keeps the same bf16 step (queries, new K/V rows, outputs) but
+stores the cache as e4m3 codes with per-layer scales: the append quantizes,
+attention reads one byte per cached element.
 """
 from __future__ import annotations
 
@@ -28,7 +32,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, AMD's published figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (no sparsity)
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partition_llama8b_b256_counters.txt")
+COUNTERS_FILES = {
+    "bf16": os.path.join(ROOT, "profiles", "decode_partition_llama8b_b256_counters.txt"),
+    "fp8": os.path.join(ROOT, "profiles", "decode_partition_llama8b_b256_fp8_counters.txt"),
+}
+FP8_SCALE = 1.0 / 80     # K and V scale of every layer of an e4m3 pool (N(0,1) inputs)
 KERNEL_SOURCES = ["decode.hip", "device_common.h", "kernels.h"]
 
 
@@ -55,34 +63,37 @@ def make_step(config: int):
     raise SystemExit(f"--config {config}: the bench runs configs 3, 4 or 5 (1 and 2 are parity cases)")
 
 
-def algorithmic_bytes(step):
-    """Bytes a perfect implementation moves (each byte once)."""
+def algorithmic_bytes(step, kv_dtype: str = "bf16"):
+    """Bytes a perfect implementation moves (each byte once). e: bytes of a
+    query/output/new-row element; ekv: bytes of a cached element."""
     e = 2 if step.dtype == "bf16" else 4
+    ekv = 1 if kv_dtype == "fp8" else e
     hkv, hq, d = step.num_kv_heads, step.num_q_heads, step.head_dim
     _, dec_ctx = step.decode_inputs()
     b = len(dec_ctx)
-    decode_kv = int(dec_ctx.astype(np.int64).sum()) * hkv * d * 2 * e
+    decode_kv = int(dec_ctx.astype(np.int64).sum()) * hkv * d * 2 * ekv
     decode_qo = 2 * b * hq * d * e
     n_new = len(step.new_slots)
-    append = 4 * n_new * hkv * d * e                    # read new K,V + write them
+    append = 2 * n_new * hkv * d * (e + ekv)            # read new K,V + write them
     out = {"decode_kv": decode_kv, "decode_qo": decode_qo, "append": append}
     if step.cu_q_lens is not None:
         _, pctx = step.prefill_inputs()
         qlens = np.diff(step.cu_q_lens)
-        kv = int(pctx.astype(np.int64).sum()) * hkv * d * 2 * e
+        kv = int(pctx.astype(np.int64).sum()) * hkv * d * 2 * ekv
         out["prefill_bytes"] = kv + 2 * int(qlens.sum()) * hq * d * e
         pairs = sum(int(np.sum(c - t + np.arange(t) + 1)) for c, t in zip(pctx, qlens))
         out["prefill_flops"] = 4 * hq * d * pairs
     return out
 
 
-def read_traffic(achieved_launch_bytes: int):
+def read_traffic(kv_dtype: str):
     """HBM bytes per partition-kernel launch from committed rocprofv3 counters,
     if they were taken on the current kernel source; else None."""
-    if not os.path.exists(COUNTERS_FILE):
+    path = COUNTERS_FILES[kv_dtype]
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(COUNTERS_FILE):
+    for line in open(path):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
@@ -94,11 +105,13 @@ def read_traffic(achieved_launch_bytes: int):
         return None
 
 
-def cpu_baseline(step, min_seconds: float = 10.0, max_reps: int = 30):
-    """The oracle, as it stands, on the same workload: append + decode (+ prefill),
-    repeated until about ``min_seconds`` of CPU work (at least 3 runs) and timed
-    per run; returns the median seconds per step, the runs and the threads."""
+def cpu_baseline(step, kv_dtype: str = "bf16", min_seconds: float = 10.0, max_reps: int = 30):
+    """The oracle, as it stands, on the same workload: append (with e4m3
+    quantization for an fp8 cache) + decode (+ prefill), repeated until about
+    ``min_seconds`` of CPU work (at least 3 runs) and timed per run; returns the
+    median seconds per step, the runs and the threads."""
     import oracle
+    from oracle import fp8 as f8
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -107,14 +120,20 @@ def cpu_baseline(step, min_seconds: float = 10.0, max_reps: int = 30):
     s = step
     pk = oracle.new_pool(s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim, np.float32)
     pv = oracle.new_pool(s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim, np.float32)
-    oracle.append(pk, pv, s.cached_key.f32, s.cached_value.f32, s.cached_slots)
+    if kv_dtype == "fp8":
+        def stored(x):
+            return f8.quantize_dequantize(x, FP8_SCALE)
+    else:
+        def stored(x):
+            return x
+    oracle.append(pk, pv, stored(s.cached_key.f32), stored(s.cached_value.f32), s.cached_slots)
     nk, nv, q = s.new_key.f32, s.new_value.f32, s.decode_query.f32
     bt, cl = s.decode_inputs()
     pq = s.prefill_query.f32 if s.prefill_query is not None else None
     times = []
     while len(times) < 3 or (sum(times) < min_seconds and len(times) < max_reps):
         t0 = time.perf_counter()
-        oracle.append(pk, pv, nk, nv, s.new_slots)
+        oracle.append(pk, pv, stored(nk), stored(nv), s.new_slots)
         oracle.paged_decode(q, pk, pv, bt, cl, s.scale)
         if pq is not None:
             pbt, pcl = s.prefill_inputs()
@@ -131,6 +150,8 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto, >= 2 GiB)")
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="cache storage: bf16 (the workload's dtype) or e4m3 codes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warmup, copy this many MiB device-to-device once (a plain copy "
@@ -157,9 +178,14 @@ def main():
     s = step
     log(f"workload {s.name}: generated in {time.time() - t0:.1f}s; "
         f"{len(s.decode_seqs)} decode seqs, tokens {int(s.context_lens.sum())}, info {s.info}")
-    ab = algorithmic_bytes(s)
-    e = 2 if s.dtype == "bf16" else 4
+    kvd = args.kv_dtype
+    if kvd == "fp8" and s.dtype != "bf16":
+        raise SystemExit("--kv-dtype fp8 needs a bf16 workload")
+    ab = algorithmic_bytes(s, kvd)
     tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
+    pool_dt = torch.uint8 if kvd == "fp8" else tdt
+    pool_e = 1 if kvd == "fp8" else (2 if s.dtype == "bf16" else 4)
+    dt_code = pkv.FP8_E4M3 if kvd == "fp8" else (pkv.BF16 if s.dtype == "bf16" else pkv.F32)
 
     def dev_vals(v):
         if v.dtype == "bf16":
@@ -170,14 +196,14 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(dev)
 
     # ---- pools: R replicas = R library layers ----
-    kb, _ = pkv.kv_pool_bytes(s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim,
-                              pkv.BF16 if s.dtype == "bf16" else pkv.F32)
+    kb, _ = pkv.kv_pool_bytes(s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim, dt_code)
     reps = args.replicas or max(2, math.ceil(2 * 2**30 / (2 * kb)))
-    k_layers = [torch.empty(kb // e, dtype=tdt, device=dev) for _ in range(reps)]
-    v_layers = [torch.empty(kb // e, dtype=tdt, device=dev) for _ in range(reps)]
-    dt_code = pkv.BF16 if s.dtype == "bf16" else pkv.F32
+    k_layers = [torch.empty(kb // pool_e, dtype=pool_dt, device=dev) for _ in range(reps)]
+    v_layers = [torch.empty(kb // pool_e, dtype=pool_dt, device=dev) for _ in range(reps)]
     pool = pkv.kv_pool_create(reps, s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim,
                               dt_code, k_layers, v_layers)
+    if kvd == "fp8":
+        pkv.kv_pool_set_fp8_scales(pool, [FP8_SCALE] * reps, [FP8_SCALE] * reps)
     stream = torch.cuda.current_stream(dev)
     pkv.reshape_and_cache(pool, 0, dev_vals(s.cached_key), dev_vals(s.cached_value),
                           dev_int(s.cached_slots, torch.int64), len(s.cached_slots), stream)
@@ -282,6 +308,7 @@ def main():
             "head_dim": s.head_dim, "block_size": s.block_size,
             "context_tokens": int(cl.sum()),
             "partition_size": part if part else "auto",
+            "kv_cache_dtype": "fp8_e4m3" if kvd == "fp8" else s.dtype,
             "pool_replicas": reps,
             "parallelism": "single GPU",
         },
@@ -300,7 +327,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic(part_bytes),
+            "traffic": read_traffic(kvd),
             "algorithmic_bytes_per_launch": part_bytes,
         },
     }
@@ -311,11 +338,11 @@ def main():
                                   "flops_per_launch": ab["prefill_flops"]}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same step ...")
-        t_cpu, runs, threads = cpu_baseline(s)
+        t_cpu, runs, threads = cpu_baseline(s, kvd)
         result["cpu_baseline"] = {
             "value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole step ({s.name}: append + decode of all {nseq} sequences"
+            "sample": f"the whole step ({s.name}{', e4m3 cache' if kvd == 'fp8' else ''}: append + decode of all {nseq} sequences"
                       f"{' + prefill chunk' if has_prefill else ''}), numpy float64, median of {runs} runs"
                       f" ({runs * t_cpu:.0f} s of CPU work); {t_cpu:.2f} s per step; BLAS pool of"
                       f" {threads} threads, the per-sequence loop single-threaded; {os.cpu_count()} host CPUs",

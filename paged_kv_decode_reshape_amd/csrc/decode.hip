@@ -48,6 +48,8 @@
 //     100-160 us and shortens the launch by about 6%.
 //   * fixed partitions of P tokens: one wavefront per (b, h, partition),
 //     partitions dispatched in descending index order (long sequences first).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -58,14 +60,21 @@ namespace {
 template <typename T, int D, int G>
 struct DecodeShape {
   static constexpr int kEpv = ElemTraits<T>::kPerVec;   // elements per 16-byte vector
-  static constexpr int kVecPerRow = D / kEpv;           // vectors per token row (K or V)
-  static constexpr int kVInstPerBlock = kBlockSize * kVecPerRow / kWave;
+  static constexpr int kVecPerRow = D / kEpv;           // 16-byte vectors per token row (K)
   static constexpr int kTokensPerWindow = 64;
   static constexpr int kBlocksPerWindow = kTokensPerWindow / kBlockSize;
   static constexpr int kKGroup = kVecPerRow < 16 ? kVecPerRow : 16;   // K vectors loaded at once
-  static constexpr int kVGroup = (kBlocksPerWindow * kVInstPerBlock <= 16)
+  // The slice of a V row a lane owns: 16 bytes, or 8 codes of an e4m3 pool,
+  // so that the fp32 output accumulators stay at 8 per head (as for bf16)
+  // instead of 16.
+  using VVec = typename std::conditional<sizeof(T) == 1, Vec8, Vec16>::type;
+  static constexpr int kVBytes = (int)sizeof(VVec);
+  static constexpr int kVEpv = kVBytes / (int)sizeof(T);   // elements per V slice
+  static constexpr int kVVecPerRow = D / kVEpv;             // V slices per token row
+  static constexpr int kVInstPerBlock = kBlockSize * kVVecPerRow / kWave;
+  static constexpr int kVGroup = (kBlocksPerWindow * kVInstPerBlock * kVBytes <= 256)
                                      ? kBlocksPerWindow
-                                     : 16 / kVInstPerBlock;            // V blocks loaded at once
+                                     : 256 / (kVInstPerBlock * kVBytes);   // V blocks loaded at once
   // Queries and outputs: IoType<T> (bf16 for an e4m3 pool), kQPerVec vectors
   // of them per pool vector.
   using TQ = typename IoType<T>::type;
@@ -90,21 +99,22 @@ __device__ __forceinline__ void dot_vec_bf16(float (&acc)[G], const Vec16& k, co
   }
 }
 
-// 16 e4m3 codes of one key against 16 bf16 query values per head (two vectors,
-// q[0][g] then q[1][g]): codes become exact bf16 pairs for v_dot2_f32_bf16.
+// Codes 8*half .. 8*half+7 of one e4m3 key vector against 8 bf16 query values
+// per head: codes become exact bf16 pairs for v_dot2_f32_bf16. half is a
+// compile-time constant after unrolling.
 template <int G>
-__device__ __forceinline__ void dot_vec_fp8(float (&acc)[G], const Vec16& k, const Vec16 (&q)[2][G]) {
+__device__ __forceinline__ void dot_half_fp8(float (&acc)[G], const Vec16& k, int half, const Vec16 (&q)[G]) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t k01 = fp8x2_to_bf16x2<false>(k.w[w]);
-    const uint32_t k23 = fp8x2_to_bf16x2<true>(k.w[w]);
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t kw = k.w[2 * half + w];
+    const uint32_t k01 = fp8x2_to_bf16x2<false>(kw);
+    const uint32_t k23 = fp8x2_to_bf16x2<true>(kw);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const Vec16& qv = q[w / 2][g];
-      acc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.w[2 * (w % 2)]),
+      acc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[g].w[2 * w]),
                                                __builtin_bit_cast(bf16x2, k01), acc[g], false);
-      acc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv.w[2 * (w % 2) + 1]),
+      acc[g] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q[g].w[2 * w + 1]),
                                                __builtin_bit_cast(bf16x2, k23), acc[g], false);
     }
   }
@@ -135,6 +145,9 @@ __device__ __forceinline__ void set_wave_priority(int level) {
   else if (level == 1) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
 }
+
+template <typename T> __device__ __forceinline__ void widen_v(const Vec16& v, float* f) { widen<T>(v, f); }
+template <typename T> __device__ __forceinline__ void widen_v(const Vec8& v, float* f) { widen(v, f); }
 
 // Per-wave scratch in LDS.
 template <typename T, int D, int G>
@@ -169,12 +182,15 @@ struct DecodeArgs {
 // priority from the fraction of its share already done (3 in the first
 // quarter .. 0 in the last), where done counts the share's windows so far.
 template <typename T, int D, int G>
-__device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
+__device__ __forceinline__ Summary<G, DecodeShape<T, D, G>::kVEpv> run_segment(
     const DecodeArgs& a, WaveLds<T, D, G>& lds, int b, int h, int tok_begin, int tok_end,
     int& done, int share) {
   using S = DecodeShape<T, D, G>;
-  constexpr int EPV = S::kEpv;
-  constexpr int VPR = S::kVecPerRow;
+  constexpr int KEPV = S::kEpv;           // elements per K vector
+  constexpr int EPV = S::kVEpv;           // V slice elements (output accumulators per head)
+  constexpr int VPR = S::kVecPerRow;      // K vectors per row
+  constexpr int VVPR = S::kVVecPerRow;    // V slices per row
+  using VVec = typename S::VVec;
   constexpr int NVI = S::kVInstPerBlock;
   constexpr int TPW = S::kTokensPerWindow;
   constexpr int BPW = S::kBlocksPerWindow;
@@ -212,8 +228,8 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
   const size_t blk_stride = (size_t)a.hkv * tile;
   const int row = lane >> 4;                            // block of the window for this lane's K token
   const int tin = lane & 15;                            // token within that block
-  const int vvec = lane % VPR;                          // head-dim slice this lane owns for V
-  const int vtok0 = lane / VPR;                         // first token (within a block) it reads for V
+  const int vvec = lane % VVPR;                         // head-dim slice this lane owns for V
+  const int vtok0 = lane / VVPR;                        // first token (within a block) it reads for V
   const uint32_t voff = (uint32_t)(vtok0 * D + vvec * EPV) * (uint32_t)sizeof(T);
 
   Summary<G, EPV> st;
@@ -226,67 +242,57 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
   }
   wave_lds_sync();
 
-#pragma unroll 1
-  for (int w = 0; w < nwin; ++w) {
-    if (share > 0) set_wave_priority(3 - (4 * done) / share);
-    ++done;
-    const int t0 = tok_begin + w * TPW;
+  // ---- the steps of one 64-token window ----
+  // Block ids of window w (refreshing the 64-id register every 16 windows),
+  // and kb, the block of this lane's K token. kb is selected from the
+  // values themselves, not by indexing bid, which would put bid in memory.
+  auto window_bids = [&](int w, int (&bid)[BPW], int& kb) __attribute__((always_inline)) {
     const int lb = 4 * w;                               // first local block of the window
     if (lb > 0 && (lb & 63) == 0) ids = bt[min(lb + lane, nblk - 1)];
-    int bid[BPW];
+    int sel = 0;
 #pragma unroll
-    for (int r = 0; r < BPW; ++r) bid[r] = __builtin_amdgcn_readlane(ids, min(lb + r, nblk - 1) & 63);
-    int kb = bid[0];
-#pragma unroll
-    for (int r = 1; r < BPW; ++r) kb = (row == r) ? bid[r] : kb;
-
-    // ---- q.K for this lane's token ----
-    // K loads: lane = token; one instruction reads 4 x 256 contiguous bytes;
-    // at most 16 vectors (64 VGPRs) are loaded at once. Query slices come from
-    // LDS one vector ahead of their use; the scheduling barriers stop the
-    // compiler from hoisting all G*VPR reads at once.
+    for (int r = 0; r < BPW; ++r) {
+      const int v = __builtin_amdgcn_readlane(ids, min(lb + r, nblk - 1) & 63);
+      bid[r] = v;
+      sel = (row == r) ? v : sel;
+    }
+    kb = sel;
+  };
+  // K loads: lane = token; one instruction reads 4 x 256 contiguous bytes.
+  auto load_k = [&](int kb, int c0, Vec16 (&kv)[KG]) __attribute__((always_inline)) {
     const char* kt = reinterpret_cast<const char*>(kpool + (size_t)kb * blk_stride + head_off) +
                      (uint32_t)tin * 16u;
+#pragma unroll
+    for (int c = 0; c < KG; ++c) kv[c] = ld16_stream(kt + (c0 + c) * (kBlockSize * 16));
+  };
+  // q.K over key vectors c0 .. c0 + KG - 1. Query vector u (of this group)
+  // pairs with part u % QPK of key vector u / QPK (an e4m3 key vector spans
+  // two bf16 query vectors). Query slices come from LDS one vector ahead of
+  // their use; the scheduling barriers stop the compiler from hoisting all
+  // G*VPR reads at once.
+  auto qk_group = [&](float (&acc)[G], const Vec16 (&kv)[KG], int c0) __attribute__((always_inline)) {
     const int qz = opaque_zero();
-    float acc[G];
+    Vec16 qcur[G], qnext[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+    for (int g = 0; g < G; ++g) qcur[g] = lds.q[g][c0 * QPK + qz];
 #pragma unroll
-    for (int c0 = 0; c0 < VPR; c0 += KG) {
-      Vec16 kv[KG];
+    for (int u = 0; u < KG * QPK; ++u) {
+      if (u + 1 < KG * QPK) {
 #pragma unroll
-      for (int c = 0; c < KG; ++c) kv[c] = ld16_stream(kt + (c0 + c) * (kBlockSize * 16));
-      // Query vectors (c0 + c) * QPK + j pair with key vector c0 + c.
-      Vec16 qcur[QPK][G], qnext[QPK][G];
-#pragma unroll
-      for (int j = 0; j < QPK; ++j) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) qcur[j][g] = lds.q[g][c0 * QPK + j + qz];
+        for (int g = 0; g < G; ++g) qnext[g] = lds.q[g][c0 * QPK + u + 1 + qz];
       }
+      if constexpr (KEPV == 16) dot_half_fp8<G>(acc, kv[u / QPK], u % QPK, qcur);
+      else if constexpr (KEPV == 8) dot_vec_bf16<G>(acc, kv[u], qcur);
+      else dot_vec_f32<G>(acc, kv[u], qcur);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < KG; ++c) {
-        if (c + 1 < KG) {
-#pragma unroll
-          for (int j = 0; j < QPK; ++j) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) qnext[j][g] = lds.q[g][(c0 + c + 1) * QPK + j + qz];
-          }
-        }
-        if constexpr (EPV == 16) dot_vec_fp8<G>(acc, kv[c], qcur);
-        else if constexpr (EPV == 8) dot_vec_bf16<G>(acc, kv[c], qcur[0]);
-        else dot_vec_f32<G>(acc, kv[c], qcur[0]);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < QPK; ++j) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) qcur[j][g] = qnext[j][g];
-        }
-      }
+      for (int g = 0; g < G; ++g) qcur[g] = qnext[g];
     }
+  };
+  // Online softmax over the window: the window maximum per query head is
+  // reduced across the wave; probabilities go to LDS.
+  auto softmax_window = [&](const float (&acc)[G], int t0) __attribute__((always_inline)) {
     const bool kvalid = (t0 + lane) < tok_end;
-    __builtin_amdgcn_sched_barrier(0);   // phase boundary: q.K | softmax
-
-    // ---- online softmax over the window ----
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float s = kvalid ? acc[g] * a.scale_log2 : -INFINITY;
@@ -301,51 +307,77 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
       lds.p[lane][g] = p;
     }
     wave_lds_sync();
-    __builtin_amdgcn_sched_barrier(0);   // phase boundary: softmax | P.V
-
-    // ---- P.V ----
-    // V loads: one instruction reads consecutive token rows; address = wave-
-    // uniform block base + this lane's 32-bit byte offset. They are issued
-    // after q.K so K and V never hold registers at the same time, at most 16
-    // vectors at once.
-    const bool partial = (t0 + TPW > tok_end);
+  };
+  // V loads of window blocks r0 .. r0 + VB - 1: one instruction reads
+  // consecutive token rows; address = wave-uniform block base + this lane's
+  // 32-bit byte offset.
+  auto load_v = [&](const int (&bid)[BPW], int r0, VVec (&vv)[VB][NVI]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r0 = 0; r0 < BPW; r0 += VB) {
-      Vec16 vv[VB][NVI];
+    for (int r = 0; r < VB; ++r) {
+      const char* vt = reinterpret_cast<const char*>(vpool + (size_t)bid[r0 + r] * blk_stride + head_off);
 #pragma unroll
-      for (int r = 0; r < VB; ++r) {
-        const char* vt = reinterpret_cast<const char*>(vpool + (size_t)bid[r0 + r] * blk_stride + head_off);
-#pragma unroll
-        for (int i = 0; i < NVI; ++i) vv[r][i] = ld16_stream(vt + voff + i * ((kWave / VPR) * D * (int)sizeof(T)));
-      }
-      if (partial) {
-        // Last, partial window: tokens past the end may hold anything (even
-        // NaN) and carry p = 0, so their V rows are zeroed before the products.
-#pragma unroll
-        for (int r = 0; r < VB; ++r) {
-#pragma unroll
-          for (int i = 0; i < NVI; ++i) {
-            if (t0 + (r0 + r) * kBlockSize + vtok0 + i * (kWave / VPR) >= tok_end) vv[r][i] = zero16();
-          }
-        }
-      }
+      for (int i = 0; i < NVI; ++i)
+        vv[r][i] = ld_stream(vt + voff + i * ((kWave / VVPR) * D * (int)sizeof(T)), VVec{});
+    }
+  };
+  // P.V for those blocks.
+  auto pv_blocks = [&](VVec (&vv)[VB][NVI], int r0, int t0) __attribute__((always_inline)) {
+    if (t0 + TPW > tok_end) {
+      // Last, partial window: tokens past the end may hold anything (even
+      // NaN) and carry p = 0, so their V rows are zeroed before the products.
 #pragma unroll
       for (int r = 0; r < VB; ++r) {
 #pragma unroll
         for (int i = 0; i < NVI; ++i) {
-          const int tb = vtok0 + i * (kWave / VPR);
-          float pv[G];
-#pragma unroll
-          for (int g = 0; g < G; ++g) pv[g] = lds.p[(r0 + r) * kBlockSize + tb][g];
-          float vf[EPV];
-          widen<T>(vv[r][i], vf);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) st.o[g][e] = fmaf(pv[g], vf[e], st.o[g][e]);
-          }
+          if (t0 + (r0 + r) * kBlockSize + vtok0 + i * (kWave / VVPR) >= tok_end) set_zero(vv[r][i]);
         }
       }
+    }
+#pragma unroll
+    for (int r = 0; r < VB; ++r) {
+#pragma unroll
+      for (int i = 0; i < NVI; ++i) {
+        const int tb = vtok0 + i * (kWave / VVPR);
+        float pv[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) pv[g] = lds.p[(r0 + r) * kBlockSize + tb][g];
+        float vf[EPV];
+        widen_v<T>(vv[r][i], vf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) st.o[g][e] = fmaf(pv[g], vf[e], st.o[g][e]);
+        }
+      }
+    }
+  };
+
+  // K and V are loaded in turn, at most 64 VGPRs of each at once, so they
+  // never hold registers at the same time.
+#pragma unroll 1
+  for (int w = 0; w < nwin; ++w) {
+    if (share > 0) set_wave_priority(3 - (4 * done) / share);
+    ++done;
+    const int t0 = tok_begin + w * TPW;
+    int bid[BPW], kb;
+    window_bids(w, bid, kb);
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+#pragma unroll
+    for (int c0 = 0; c0 < VPR; c0 += KG) {
+      Vec16 kv[KG];
+      load_k(kb, c0, kv);
+      qk_group(acc, kv, c0);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // phase boundary: q.K | softmax
+    softmax_window(acc, t0);
+    __builtin_amdgcn_sched_barrier(0);   // phase boundary: softmax | P.V
+#pragma unroll
+    for (int r0 = 0; r0 < BPW; r0 += VB) {
+      VVec vv[VB][NVI];
+      load_v(bid, r0, vv);
+      pv_blocks(vv, r0, t0);
     }
     wave_lds_sync();
   }
@@ -356,7 +388,7 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
   for (int g = 0; g < G; ++g) {
     st.l[g] = wave_sum(st.l[g]);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) st.o[g][e] = sum_lanes_above<VPR>(st.o[g][e]);
+    for (int e = 0; e < EPV; ++e) st.o[g][e] = sum_lanes_above<VVPR>(st.o[g][e]);
   }
   return st;
 }
@@ -365,9 +397,9 @@ __device__ __forceinline__ Summary<G, ElemTraits<T>::kPerVec> run_segment(
 // out_row points at query head 0 of the group.
 template <typename T, int D, int G>
 __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row,
-                                           const Summary<G, ElemTraits<T>::kPerVec>& st, float v_scale) {
+                                           const Summary<G, DecodeShape<T, D, G>::kVEpv>& st, float v_scale) {
   using TQ = typename IoType<T>::type;
-  constexpr int EPV = ElemTraits<T>::kPerVec;
+  constexpr int EPV = DecodeShape<T, D, G>::kVEpv;
   constexpr int EPQ = ElemTraits<TQ>::kPerVec;
   constexpr int VPR = D / EPV;
   const int lane = threadIdx.x & 63;
@@ -390,8 +422,8 @@ __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row,
 template <typename T, int D, int G>
 __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base,
                                               size_t o_stride,
-                                              const Summary<G, ElemTraits<T>::kPerVec>& st, float v_scale) {
-  constexpr int EPV = ElemTraits<T>::kPerVec;
+                                              const Summary<G, DecodeShape<T, D, G>::kVEpv>& st, float v_scale) {
+  constexpr int EPV = DecodeShape<T, D, G>::kVEpv;
   constexpr int VPR = D / EPV;
   const int lane = threadIdx.x & 63;
   if (lane < VPR) {
@@ -412,7 +444,9 @@ __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, floa
 
 template <typename T, int D, int G>
 constexpr int decode_waves_per_simd() {
-  // bf16 q.K + P.V for up to 4 heads fits 168 VGPRs (3 waves per SIMD).
+  // bf16 q.K + P.V for up to 4 heads fits 168 VGPRs (3 waves per SIMD), and
+  // so does e4m3 (8-code V slices) for up to 4 heads.
+  if (sizeof(T) == 1) return G <= 4 ? 3 : 2;
   return (sizeof(T) == 2 && (G == 4 || G == 1)) ? 3 : 2;
 }
 

@@ -42,6 +42,19 @@ __device__ __forceinline__ void st16(void* p, const Vec16& v) {
 }
 __device__ __forceinline__ Vec16 zero16() { return Vec16{{0u, 0u, 0u, 0u}}; }
 
+// 8-byte vectors (8 e4m3 codes), streamed like ld16_stream.
+struct alignas(8) Vec8 { uint32_t w[2]; };
+__device__ __forceinline__ Vec8 ld8_stream(const void* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return Vec8{{v.x, v.y}};
+}
+__device__ __forceinline__ Vec8 zero8() { return Vec8{{0u, 0u}}; }
+__device__ __forceinline__ Vec16 ld_stream(const void* p, Vec16) { return ld16_stream(p); }
+__device__ __forceinline__ Vec8 ld_stream(const void* p, Vec8) { return ld8_stream(p); }
+__device__ __forceinline__ void set_zero(Vec16& v) { v = zero16(); }
+__device__ __forceinline__ void set_zero(Vec8& v) { v = zero8(); }
+
 // bf16 <-> fp32. Widening is exact; narrowing rounds to nearest, ties to even.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -68,6 +81,16 @@ typedef float pkv_f32x2 __attribute__((ext_vector_type(2)));
 template <> __device__ __forceinline__ void widen<uint8_t>(const Vec16& v, float* f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const pkv_f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.w[i], false);
+    const pkv_f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.w[i], true);
+    f[4 * i] = a.x; f[4 * i + 1] = a.y; f[4 * i + 2] = b.x; f[4 * i + 3] = b.y;
+  }
+}
+
+// 8 e4m3 codes widened exactly.
+__device__ __forceinline__ void widen(const Vec8& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
     const pkv_f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.w[i], false);
     const pkv_f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v.w[i], true);
     f[4 * i] = a.x; f[4 * i + 1] = a.y; f[4 * i + 2] = b.x; f[4 * i + 3] = b.y;
