@@ -442,12 +442,316 @@ __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, floa
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core segments (bf16 and e4m3 pools).
+//
+// The same segment on v_mfma_f32_16x16x32_bf16, with the G query heads of
+// the group as the 16 MFMA columns (heads past G are zero queries whose
+// results are never written). Per 64-token window (4 blocks):
+//   * S^T = K Q^T: block r is one 16-token MFMA tile; lane (quad, col) loads
+//     its A fragment -- 8 head-dim values of token col -- straight from the
+//     pool, 1 KiB contiguous per wave instruction (an e4m3 16-code vector
+//     feeds two k-steps and is widened to bf16 exactly). Lane (quad, col)
+//     then holds the scores of tokens 16r + 4*quad + i for head col.
+//   * online softmax per head: the window maximum is an in-lane maximum and
+//     two lane swaps; the running maximum moves only when the window's
+//     exceeds it by more than 2^8 (weights stay below 256, and the common
+//     factor cancels in the final division), so most windows skip the rescale.
+//   * O^T += V^T P^T: those scores are the lane's B fragment of P^T for a
+//     fixed ordering of the tokens (split into bf16 high and remainder parts,
+//     ~17 bits per weight). V^T comes from 32-token halves of the window
+//     staged in the wave's LDS in their natural layout and read back with
+//     gfx950's transposing LDS read (ds_read_b64_tr_b16); tokens past the
+//     segment are staged as zeros.
+// A wave keeps one window's K and V loads (16 + 16 KiB for bf16 at D=128)
+// in flight, and the VALU work per token is a fraction of the lane-per-token
+// path's.
+// ---------------------------------------------------------------------------
+typedef __bf16 mf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float mf_f32x4 __attribute__((ext_vector_type(4)));
+typedef short mf_i16x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct MfmaWaveLds {
+  // Half a window of V (32 tokens), bf16; rows padded by 16 bytes, which
+  // spreads the transposed reads over the banks (at most 2-way conflicts)
+  // and keeps three 4-wave workgroups of the balanced kernel within the LDS.
+  static constexpr int kStride = D + 8;
+  alignas(16) uint16_t v[32][kStride];
+};
+
+// Running summary of head col (every lane of the column holds the same m;
+// l is a per-lane partial until the end of the segment). o: lane (quad, col)
+// holds O^T[16n + 4*quad + i][col].
+template <int D>
+struct MfmaSummary {
+  float m;
+  float l;
+  mf_f32x4 o[D / 16];
+};
+
+__device__ __forceinline__ mf_bf16x8 mf_as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(mf_bf16x8, make_uint4(a, b, c, d));
+}
+__device__ __forceinline__ uint32_t mf_pack_bf16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, b2));
+}
+// Codes 0..7 (kHigh: 8..15) of an e4m3 vector as 8 exact bf16 values.
+template <bool kHigh>
+__device__ __forceinline__ mf_bf16x8 mf_fp8_half(const Vec16& v) {
+  const uint32_t w0 = v.w[kHigh ? 2 : 0], w1 = v.w[kHigh ? 3 : 1];
+  return mf_as_bf16x8(fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+                      fp8x2_to_bf16x2<true>(w1));
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, MfmaWaveLds<D>& lds, int b, int h,
+                                                            int tok_begin, int tok_end, int& done, int share) {
+  static_assert(sizeof(T) <= 2, "matrix-core segments take bf16 or e4m3 pools");
+  static_assert(G <= 16, "the group's heads are the 16 MFMA columns");
+  constexpr bool kF8 = sizeof(T) == 1;
+  constexpr int KS = D / 32;                          // k-steps over the head dim
+  constexpr int KL = kF8 ? KS / 2 : KS;               // K loads per block (16 bytes each)
+  constexpr int NT = D / 16;                          // output tiles over the head dim
+  constexpr int VPRB = D * (int)sizeof(T) / 16;       // 16-byte vectors per V row in the pool
+  constexpr int RPI = kWave / VPRB;                   // V rows per load instruction
+  constexpr int VLD = 32 / RPI;                       // V load instructions per half window
+  constexpr int TPW = 64;
+  static_assert(kBlockSize % RPI == 0, "a V load instruction stays inside one block");
+
+  const int lane = threadIdx.x & 63;
+  const int quad = lane >> 4, col = lane & 15;
+  const int nwin = (tok_end - tok_begin + TPW - 1) / TPW;
+  const int lb_begin = tok_begin / kBlockSize;
+  const int nblk = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;
+  // Block ids of the segment, 64 per register, clamped to its last block so
+  // that every address formed below is in bounds.
+  const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin;
+  int ids = bt[min(lane, nblk - 1)];
+
+  // Q^T fragments (B operand): lane (quad, col) holds 8 values of head col
+  // at the head-dim positions its K fragment holds for each k-step.
+  mf_bf16x8 qf[KS];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.query) +
+                           ((size_t)b * a.hkv * G + (size_t)h * G + min(col, G - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int d0 = kF8 ? 64 * (s / 2) + 16 * quad + 8 * (s % 2) : 32 * s + 8 * quad;
+      const Vec16 v = col < G ? ld16(qrow + d0) : zero16();
+      qf[s] = mf_as_bf16x8(v.w[0], v.w[1], v.w[2], v.w[3]);
+    }
+  }
+
+  const size_t tile_bytes = (size_t)kBlockSize * D * sizeof(T);
+  const size_t blk_bytes = (size_t)a.hkv * tile_bytes;
+  const char* kbase = static_cast<const char*>(a.kpool) + (size_t)h * tile_bytes;
+  const char* vbase = static_cast<const char*>(a.vpool) + (size_t)h * tile_bytes;
+  const uint32_t k_lane = (uint32_t)((quad * kBlockSize + col) * 16);   // vector (4j + quad) of token col
+  const int v_row = lane / VPRB, v_vec = lane % VPRB;
+  const uint32_t v_lane = (uint32_t)(v_row * D * (int)sizeof(T) + v_vec * 16);
+  const int vkey = 4 * quad + (col >> 2), vcol = 4 * (col & 3);   // transposed V read of this lane
+
+  MfmaSummary<D> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) st.o[n] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 1
+  for (int w = 0; w < nwin; ++w) {
+    if (share > 0) set_wave_priority(3 - (4 * done) / share);
+    ++done;
+    const int t0 = tok_begin + w * TPW;
+    const int lb = 4 * w;
+    if (lb > 0 && (lb & 63) == 0) ids = bt[min(lb + lane, nblk - 1)];
+    int bid[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bid[r] = __builtin_amdgcn_readlane(ids, min(lb + r, nblk - 1) & 63);
+
+    // ---- loads: the window's K fragments and V rows ----
+    Vec16 kr[4][KL];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const char* kt = kbase + (size_t)bid[r] * blk_bytes;
+#pragma unroll
+      for (int j = 0; j < KL; ++j) kr[r][j] = ld16_stream(kt + j * (4 * kBlockSize * 16) + k_lane);
+    }
+    Vec16 vr[2][VLD];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int u = 0; u < VLD; ++u) {
+        const int row0 = u * RPI;                       // first row of the instruction in the half
+        const char* vt = vbase + (size_t)bid[2 * kk + row0 / kBlockSize] * blk_bytes;
+        vr[kk][u] = ld16_stream(vt + (row0 % kBlockSize) * D * (int)sizeof(T) + v_lane);
+      }
+    }
+
+    // ---- S^T = K Q^T: s4[r][i] = score of token 16r + 4*quad + i, head col ----
+    mf_f32x4 s4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s4[r] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        if constexpr (kF8) {
+          s4[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mf_fp8_half<false>(kr[r][j]), qf[2 * j], s4[r], 0, 0, 0);
+          s4[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mf_fp8_half<true>(kr[r][j]), qf[2 * j + 1], s4[r], 0, 0, 0);
+        } else {
+          s4[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              mf_as_bf16x8(kr[r][j].w[0], kr[r][j].w[1], kr[r][j].w[2], kr[r][j].w[3]), qf[j], s4[r], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- scale, mask past the segment, window maximum per head ----
+    const bool full = t0 + TPW <= tok_end;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = s4[r][i] * a.scale_log2;
+        if (!full && t0 + 16 * r + 4 * quad + i >= tok_end) v = -INFINITY;
+        s4[r][i] = v;
+        mt = fmaxf(mt, v);
+      }
+    }
+    mt = xor32_max(xor16_max(mt));
+    const bool grow = mt > st.m + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float alpha = grow ? fast_exp2(st.m - mt) : 1.f;
+      st.m = grow ? mt : st.m;
+      st.l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.o[n][i] *= alpha;
+      }
+    }
+
+    // ---- P^T fragments: k-index j of lane (quad, col) in half kk is token
+    //      32kk + 16*(j/4) + 4*quad + j%4 of the window ----
+    mf_bf16x8 phi[2], plo[2];
+    float ls = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float p0 = fast_exp2(s4[2 * kk + j / 4][j % 4] - st.m);
+        const float p1 = fast_exp2(s4[2 * kk + j / 4][j % 4 + 1] - st.m);
+        ls += p0 + p1;
+        const uint32_t hb = mf_pack_bf16x2(p0, p1);
+        hw[j / 2] = hb;
+        lw[j / 2] = mf_pack_bf16x2(p0 - __uint_as_float(hb << 16), p1 - __uint_as_float(hb & 0xffff0000u));
+      }
+      phi[kk] = mf_as_bf16x8(hw[0], hw[1], hw[2], hw[3]);
+      plo[kk] = mf_as_bf16x8(lw[0], lw[1], lw[2], lw[3]);
+    }
+    st.l += ls;
+
+    // ---- O^T += V^T P^T, one 32-token half at a time through LDS ----
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      wave_lds_sync();   // the previous half's transposed reads are issued
+#pragma unroll
+      for (int u = 0; u < VLD; ++u) {
+        const int tr = u * RPI + v_row;                 // row of the half
+        Vec16 v = vr[kk][u];
+        if (!full && t0 + 32 * kk + tr >= tok_end) v = zero16();
+        if constexpr (kF8) {
+          const mf_bf16x8 lo = mf_fp8_half<false>(v), hi = mf_fp8_half<true>(v);
+          *reinterpret_cast<mf_bf16x8*>(&lds.v[tr][v_vec * 16]) = lo;
+          *reinterpret_cast<mf_bf16x8*>(&lds.v[tr][v_vec * 16 + 8]) = hi;
+        } else {
+          *reinterpret_cast<uint4*>(&lds.v[tr][v_vec * 8]) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+        }
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const mf_i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) mf_i16x4*)&lds.v[vkey][16 * n + vcol]);
+        const mf_i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) mf_i16x4*)&lds.v[16 + vkey][16 * n + vcol]);
+        const uint2 u0 = __builtin_bit_cast(uint2, a0), u1 = __builtin_bit_cast(uint2, a1);
+        const mf_bf16x8 vf = mf_as_bf16x8(u0.x, u0.y, u1.x, u1.y);
+        st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[kk], st.o[n], 0, 0, 0);
+        st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[kk], st.o[n], 0, 0, 0);
+      }
+    }
+  }
+  wave_lds_sync();
+  st.l = xor32_sum(xor16_sum(st.l));
+  return st;
+}
+
+// Final rows from a matrix-core summary: lane (quad, col < G) writes head
+// col, d = 16n + 4*quad .. +4.
+template <typename T, int D, int G>
+__device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row, const MfmaSummary<D>& st,
+                                           float v_scale) {
+  const int lane = threadIdx.x & 63;
+  const int quad = lane >> 4, col = lane & 15;
+  if (col < G) {
+    const float inv = v_scale / st.l;
+    uint16_t* row = reinterpret_cast<uint16_t*>(out_row) + (size_t)col * D;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const mf_f32x4 o = st.o[n];
+      *reinterpret_cast<uint2*>(row + 16 * n + 4 * quad) =
+          make_uint2(f32_to_bf16_bits(o[0] * inv) | (f32_to_bf16_bits(o[1] * inv) << 16),
+                     f32_to_bf16_bits(o[2] * inv) | (f32_to_bf16_bits(o[3] * inv) << 16));
+    }
+  }
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base, size_t o_stride,
+                                              const MfmaSummary<D>& st, float v_scale) {
+  const int lane = threadIdx.x & 63;
+  const int quad = lane >> 4, col = lane & 15;
+  if (col < G) {
+    float* wo = o_base + (size_t)col * o_stride;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const mf_f32x4 o = st.o[n];
+      *reinterpret_cast<float4*>(wo + 16 * n + 4 * quad) =
+          make_float4(o[0] * v_scale, o[1] * v_scale, o[2] * v_scale, o[3] * v_scale);
+    }
+    if (quad == 0) ml[(size_t)col * ml_stride] = make_float2(st.m, st.l);
+  }
+}
+
+// Which segment engine a pool type uses: the matrix cores for bf16 and e4m3
+// pools, the lane-per-token VALU path for fp32.
+template <typename T>
+struct UsesMfma {
+  static constexpr bool value = sizeof(T) <= 2;
+};
+template <typename T, int D, int G>
+using SegLds = typename std::conditional<UsesMfma<T>::value, MfmaWaveLds<D>, WaveLds<T, D, G>>::type;
+
+template <typename T, int D, int G>
+__device__ __forceinline__ auto run_seg(const DecodeArgs& a, SegLds<T, D, G>& lds, int b, int h, int tok_begin,
+                                        int tok_end, int& done, int share) {
+  if constexpr (UsesMfma<T>::value) {
+    return run_segment_mfma<T, D, G>(a, lds, b, h, tok_begin, tok_end, done, share);
+  } else {
+    return run_segment<T, D, G>(a, lds, b, h, tok_begin, tok_end, done, share);
+  }
+}
+
 template <typename T, int D, int G>
 constexpr int decode_waves_per_simd() {
-  // bf16 q.K + P.V for up to 4 heads fits 168 VGPRs (3 waves per SIMD), and
-  // so does e4m3 (8-code V slices) for up to 4 heads.
-  if (sizeof(T) == 1) return G <= 4 ? 3 : 2;
-  return (sizeof(T) == 2 && (G == 4 || G == 1)) ? 3 : 2;
+  // Matrix-core segments (bf16, e4m3) fit 168 VGPRs: three waves per SIMD,
+  // which the gather needs to keep enough loads in flight. fp32
+  // lane-per-token segments: two.
+  return sizeof(T) <= 2 ? 3 : 2;
 }
 
 // ---------------------------------------------------------------------------
@@ -459,7 +763,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
     const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
   using TQ = typename IoType<T>::type;
   constexpr int EPV = ElemTraits<TQ>::kPerVec;
-  __shared__ WaveLds<T, D, G> lds[4];
+  __shared__ SegLds<T, D, G> lds[4];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   // Unit numbering: KV head fastest, then sequence, then partition in
@@ -486,7 +790,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   if (tok_begin >= ctx) return;
   const int tok_end = min(ctx, tok_begin + prm.part_tokens);
   int done = 0;
-  const auto st = run_segment<T, D, G>(args, lds[wave], b, h, tok_begin, tok_end, done, 0);
+  const auto st = run_seg<T, D, G>(args, lds[wave], b, h, tok_begin, tok_end, done, 0);
   if (ctx <= prm.part_tokens) {
     write_rows<T, D, G>(out_row, st, args.v_scale);
   } else {
@@ -643,7 +947,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     SlotDesc* __restrict__ ws_desc, const int32_t* __restrict__ context_lens, DecodeArgs args,
     DecodeParams prm) {
-  __shared__ WaveLds<T, D, G> lds[4];
+  __shared__ SegLds<T, D, G> lds[4];
   __shared__ int cum[kMaxBalancedSeqs + 1];
   __shared__ int scan_scratch[256];
   const int total = window_prefix_sum(context_lens, prm.num_seqs, args.hkv, cum, scan_scratch);
@@ -682,7 +986,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
     const int h = r / nwb;
     const int w0 = r % nwb;
     const int w1 = min(nwb, w0 + (x1 - x));
-    const auto st = run_segment<T, D, G>(args, lds[wave], b, h, w0 * 64, min(ctx, w1 * 64), done, x1 - x0);
+    const auto st = run_seg<T, D, G>(args, lds[wave], b, h, w0 * 64, min(ctx, w1 * 64), done, x1 - x0);
     const size_t qh0 = (size_t)b * args.hkv * G + (size_t)h * G;
     if (w0 == 0 && w1 == nwb) {
       write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale);
