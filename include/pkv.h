@@ -174,6 +174,34 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
                                   int partition_size, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* Decode with several query rows per sequence (speculative verification of
+ * queries_per_seq - 1 draft tokens plus one, or a short chunk): sequence b's
+ * queries_per_seq = T new tokens are already appended, so its cache holds
+ * ctx = context_lens[b] >= T tokens, and query row j sits at position
+ * ctx - T + j and attends causally to keys 0 .. ctx - T + j. This is the
+ * prefill-chunk computation with equal chunk lengths (the pages treat decode
+ * and chunked prefill as one rule over a query length: "Inference
+ * Engineering, Part 2", "Prefill, decode, and the KV cache"; "The Serving
+ * Playbook", "Chunked prefill"), run with the decode kernels' KV-axis split.
+ *   out, query: [num_seqs][queries_per_seq][num_q_heads][head_dim], bf16
+ *     (the rows of one sequence are consecutive tokens).
+ *   block_tables, context_lens, partition_size, workspace: as for
+ *     paged_attention_decode; the workspace size comes from
+ *     paged_attention_decode_multi_workspace_bytes. context_lens[b] == 0 gives
+ *     zero rows; 0 < context_lens[b] < queries_per_seq is a caller error.
+ * bf16 and e4m3 pools; queries_per_seq x (num_q_heads / num_kv_heads) <= 16
+ * (the rows of one KV head share one matrix-core tile), else
+ * PKV_ERR_UNSUPPORTED. queries_per_seq == 1 is paged_attention_decode. */
+pkv_status paged_attention_decode_multi_workspace_bytes(const pkv_pool* pool, int num_seqs,
+                                                        int queries_per_seq, int num_q_heads,
+                                                        int max_blocks_per_seq, int partition_size,
+                                                        size_t* bytes);
+pkv_status paged_attention_decode_multi(const pkv_pool* pool, int layer, void* out, const void* query,
+                                        int queries_per_seq, const int32_t* block_tables,
+                                        const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                        int max_blocks_per_seq, float scale, int partition_size,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Prefill-chunk attention: sequence s owns query rows
  * cu_q_lens[s] .. cu_q_lens[s+1]-1 (T_s = its chunk length, T_s <= max_q_len).
  * The chunk's own K/V must already be appended, so the cache holds

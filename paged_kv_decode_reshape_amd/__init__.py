@@ -22,6 +22,7 @@ __all__ = [
     "kv_pool_bytes", "kv_pool_create", "kv_pool_set_fp8_scales", "kv_pool_destroy",
     "reshape_and_cache",
     "paged_attention_decode_workspace_bytes", "paged_attention_decode",
+    "paged_attention_decode_multi_workspace_bytes", "paged_attention_decode_multi",
     "paged_attention_prefill_chunk", "pkv_timing_enable", "pkv_timing_disable",
     "pkv_timing_read", "pkv_last_error", "EXPORTED_SYMBOLS",
 ]
@@ -52,6 +53,11 @@ _SIGNATURES = {
     "paged_attention_decode": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_int, c_int, c_int, c_float, c_int, c_void_p, c_size_t,
                                        c_void_p]),
+    "paged_attention_decode_multi_workspace_bytes": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                                             _P(c_size_t)]),
+    "paged_attention_decode_multi": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p,
+                                             c_void_p, c_int, c_int, c_int, c_float, c_int, c_void_p,
+                                             c_size_t, c_void_p]),
     "paged_attention_prefill_chunk": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                               c_int, c_float, c_void_p]),
@@ -166,6 +172,25 @@ def paged_attention_decode(pool, layer, out, query, block_tables, context_lens, 
                                          _ptr(context_lens), num_seqs, num_q_heads,
                                          max_blocks_per_seq, float(scale), partition_size,
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def paged_attention_decode_multi_workspace_bytes(pool, num_seqs, queries_per_seq, num_q_heads,
+                                                 max_blocks_per_seq, partition_size=0):
+    out = c_size_t()
+    _check(load().paged_attention_decode_multi_workspace_bytes(pool, num_seqs, queries_per_seq,
+                                                               num_q_heads, max_blocks_per_seq,
+                                                               partition_size, ctypes.byref(out)))
+    return out.value
+
+
+def paged_attention_decode_multi(pool, layer, out, query, queries_per_seq, block_tables, context_lens,
+                                 num_seqs, num_q_heads, max_blocks_per_seq, scale, partition_size=0,
+                                 workspace=None, workspace_bytes=0, stream=None):
+    _check(load().paged_attention_decode_multi(pool, layer, _ptr(out), _ptr(query), queries_per_seq,
+                                               _ptr(block_tables), _ptr(context_lens), num_seqs,
+                                               num_q_heads, max_blocks_per_seq, float(scale),
+                                               partition_size, _ptr(workspace), workspace_bytes,
+                                               _stream(stream)))
 
 
 def paged_attention_prefill_chunk(pool, layer, out, query, cu_q_lens, block_tables,

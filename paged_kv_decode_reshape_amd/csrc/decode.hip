@@ -175,6 +175,7 @@ struct DecodeArgs {
   int max_blocks;
   float scale_log2;        // softmax scale * log2(e) (* the K scale of an e4m3 pool)
   float v_scale;           // e4m3 pools: the layer's V scale; else 1
+  int nq;                  // query rows per sequence (1 for plain decode)
 };
 
 // Accumulate tokens [tok_begin, tok_end) of (b, h) into a fresh summary.
@@ -183,8 +184,9 @@ struct DecodeArgs {
 // quarter .. 0 in the last), where done counts the share's windows so far.
 template <typename T, int D, int G>
 __device__ __forceinline__ Summary<G, DecodeShape<T, D, G>::kVEpv> run_segment(
-    const DecodeArgs& a, WaveLds<T, D, G>& lds, int b, int h, int tok_begin, int tok_end,
+    const DecodeArgs& a, WaveLds<T, D, G>& lds, int b, int h, int tok_begin, int tok_end, int ctx,
     int& done, int share) {
+  (void)ctx;   // one query row per sequence: its last key is ctx - 1 >= tok_end - 1
   using S = DecodeShape<T, D, G>;
   constexpr int KEPV = S::kEpv;           // elements per K vector
   constexpr int EPV = S::kVEpv;           // V slice elements (output accumulators per head)
@@ -397,7 +399,8 @@ __device__ __forceinline__ Summary<G, DecodeShape<T, D, G>::kVEpv> run_segment(
 // out_row points at query head 0 of the group.
 template <typename T, int D, int G>
 __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row,
-                                           const Summary<G, DecodeShape<T, D, G>::kVEpv>& st, float v_scale) {
+                                           const Summary<G, DecodeShape<T, D, G>::kVEpv>& st, float v_scale,
+                                           int /*nq: 1*/, int /*hq*/) {
   using TQ = typename IoType<T>::type;
   constexpr int EPV = DecodeShape<T, D, G>::kVEpv;
   constexpr int EPQ = ElemTraits<TQ>::kPerVec;
@@ -422,7 +425,8 @@ __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row,
 template <typename T, int D, int G>
 __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base,
                                               size_t o_stride,
-                                              const Summary<G, DecodeShape<T, D, G>::kVEpv>& st, float v_scale) {
+                                              const Summary<G, DecodeShape<T, D, G>::kVEpv>& st, float v_scale,
+                                              int /*nq: 1*/, int /*pj*/) {
   constexpr int EPV = DecodeShape<T, D, G>::kVEpv;
   constexpr int VPR = D / EPV;
   const int lane = threadIdx.x & 63;
@@ -506,9 +510,12 @@ __device__ __forceinline__ mf_bf16x8 mf_fp8_half(const Vec16& v) {
                       fp8x2_to_bf16x2<true>(w1));
 }
 
-template <typename T, int D, int G>
+// MQ: several query rows per sequence (a.nq); otherwise one.
+template <typename T, int D, int G, bool MQ>
 __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, MfmaWaveLds<D>& lds, int b, int h,
-                                                            int tok_begin, int tok_end, int& done, int share) {
+                                                            int tok_begin, int tok_end, int ctx, int& done,
+                                                            int share) {
+  const int nq = MQ ? a.nq : 1;
   static_assert(sizeof(T) <= 2, "matrix-core segments take bf16 or e4m3 pools");
   static_assert(G <= 16, "the group's heads are the 16 MFMA columns");
   constexpr bool kF8 = sizeof(T) == 1;
@@ -531,16 +538,24 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin;
   int ids = bt[min(lane, nblk - 1)];
 
-  // Q^T fragments (B operand): lane (quad, col) holds 8 values of head col
-  // at the head-dim positions its K fragment holds for each k-step.
+  // Column col is query row j = col / G of the sequence, head g = col % G of
+  // the group (columns past nq * G are zero queries, never written). Row j
+  // sits at position ctx - nq + j and sees keys up to it.
+  const int ncol = nq * G;
+  const int qj = min(col, ncol - 1) / G, qg = min(col, ncol - 1) % G;
+  const int lim = min(tok_end, ctx - nq + qj + 1);       // keys [t, lim) are visible to the column
+  const int lim_all = min(tok_end, ctx - nq + 1);        // ... and [t, lim_all) to every row
+  // Q^T fragments (B operand): lane (quad, col) holds 8 values of its column's
+  // query at the head-dim positions its K fragment holds for each k-step.
   mf_bf16x8 qf[KS];
   {
+    const int hq = a.hkv * G;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.query) +
-                           ((size_t)b * a.hkv * G + (size_t)h * G + min(col, G - 1)) * D;
+                           (((size_t)b * nq + qj) * hq + (size_t)h * G + qg) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int d0 = kF8 ? 64 * (s / 2) + 16 * quad + 8 * (s % 2) : 32 * s + 8 * quad;
-      const Vec16 v = col < G ? ld16(qrow + d0) : zero16();
+      const Vec16 v = col < ncol ? ld16(qrow + d0) : zero16();
       qf[s] = mf_as_bf16x8(v.w[0], v.w[1], v.w[2], v.w[3]);
     }
   }
@@ -607,15 +622,18 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
       }
     }
 
-    // ---- scale, mask past the segment, window maximum per head ----
-    const bool full = t0 + TPW <= tok_end;
+    // ---- scale, mask past the segment and past each row's position, window
+    //      maximum per column ----
+    const bool full = t0 + TPW <= tok_end;              // no V row past the segment
+    const bool open = t0 + TPW <= lim_all;              // every row sees the whole window
     float mt = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = s4[r][i] * a.scale_log2;
-        if (!full && t0 + 16 * r + 4 * quad + i >= tok_end) v = -INFINITY;
+        const int t = t0 + 16 * r + 4 * quad + i;
+        if (!open && t >= lim) v = -INFINITY;
         s4[r][i] = v;
         mt = fmaxf(mt, v);
       }
@@ -634,7 +652,9 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
     }
 
     // ---- P^T fragments: k-index j of lane (quad, col) in half kk is token
-    //      32kk + 16*(j/4) + 4*quad + j%4 of the window ----
+    //      32kk + 16*(j/4) + 4*quad + j%4 of the window. A row that has seen
+    //      no visible key yet keeps m = -inf and gets zero weights. ----
+    const float msub = st.m == -INFINITY ? 0.f : st.m;
     mf_bf16x8 phi[2], plo[2];
     float ls = 0.f;
 #pragma unroll
@@ -642,8 +662,8 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
       uint32_t hw[4], lw[4];
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const float p0 = fast_exp2(s4[2 * kk + j / 4][j % 4] - st.m);
-        const float p1 = fast_exp2(s4[2 * kk + j / 4][j % 4 + 1] - st.m);
+        const float p0 = fast_exp2(s4[2 * kk + j / 4][j % 4] - msub);
+        const float p1 = fast_exp2(s4[2 * kk + j / 4][j % 4 + 1] - msub);
         ls += p0 + p1;
         const uint32_t hb = mf_pack_bf16x2(p0, p1);
         hw[j / 2] = hb;
@@ -690,16 +710,17 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
   return st;
 }
 
-// Final rows from a matrix-core summary: lane (quad, col < G) writes head
-// col, d = 16n + 4*quad .. +4.
+// Final rows from a matrix-core summary: lane (quad, col < nq * G) writes
+// query row col / G, head col % G of the group, d = 16n + 4*quad .. +4.
+// out_row points at row 0, head 0 of the group; rows are hq heads apart.
 template <typename T, int D, int G>
 __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row, const MfmaSummary<D>& st,
-                                           float v_scale) {
+                                           float v_scale, int nq, int hq) {
   const int lane = threadIdx.x & 63;
   const int quad = lane >> 4, col = lane & 15;
-  if (col < G) {
+  if (col < nq * G) {
     const float inv = v_scale / st.l;
-    uint16_t* row = reinterpret_cast<uint16_t*>(out_row) + (size_t)col * D;
+    uint16_t* row = reinterpret_cast<uint16_t*>(out_row) + ((size_t)(col / G) * hq + col % G) * D;
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
       const mf_f32x4 o = st.o[n];
@@ -710,20 +731,22 @@ __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row, co
   }
 }
 
+// Partial summary of column col = (row j, head g) at index j * pj + g.
 template <typename T, int D, int G>
 __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base, size_t o_stride,
-                                              const MfmaSummary<D>& st, float v_scale) {
+                                              const MfmaSummary<D>& st, float v_scale, int nq, int pj) {
   const int lane = threadIdx.x & 63;
   const int quad = lane >> 4, col = lane & 15;
-  if (col < G) {
-    float* wo = o_base + (size_t)col * o_stride;
+  if (col < nq * G) {
+    const size_t idx = (size_t)(col / G) * pj + col % G;
+    float* wo = o_base + idx * o_stride;
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
       const mf_f32x4 o = st.o[n];
       *reinterpret_cast<float4*>(wo + 16 * n + 4 * quad) =
           make_float4(o[0] * v_scale, o[1] * v_scale, o[2] * v_scale, o[3] * v_scale);
     }
-    if (quad == 0) ml[(size_t)col * ml_stride] = make_float2(st.m, st.l);
+    if (quad == 0) ml[idx * ml_stride] = make_float2(st.m, st.l);
   }
 }
 
@@ -736,13 +759,13 @@ struct UsesMfma {
 template <typename T, int D, int G>
 using SegLds = typename std::conditional<UsesMfma<T>::value, MfmaWaveLds<D>, WaveLds<T, D, G>>::type;
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool MQ>
 __device__ __forceinline__ auto run_seg(const DecodeArgs& a, SegLds<T, D, G>& lds, int b, int h, int tok_begin,
-                                        int tok_end, int& done, int share) {
+                                        int tok_end, int ctx, int& done, int share) {
   if constexpr (UsesMfma<T>::value) {
-    return run_segment_mfma<T, D, G>(a, lds, b, h, tok_begin, tok_end, done, share);
+    return run_segment_mfma<T, D, G, MQ>(a, lds, b, h, tok_begin, tok_end, ctx, done, share);
   } else {
-    return run_segment<T, D, G>(a, lds, b, h, tok_begin, tok_end, done, share);
+    return run_segment<T, D, G>(a, lds, b, h, tok_begin, tok_end, ctx, done, share);
   }
 }
 
@@ -757,13 +780,14 @@ constexpr int decode_waves_per_simd() {
 // ---------------------------------------------------------------------------
 // Fixed partitions: one wavefront per (b, h, partition).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool MQ>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_partition_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
   using TQ = typename IoType<T>::type;
   constexpr int EPV = ElemTraits<TQ>::kPerVec;
   __shared__ SegLds<T, D, G> lds[4];
+  const int nq = MQ ? args.nq : 1;   // query rows per sequence
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
   // Unit numbering: KV head fastest, then sequence, then partition in
@@ -777,12 +801,17 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   const int part = prm.max_parts - 1 - (int)prev;
 
   const int ctx = context_lens[b];
-  const size_t qh0 = (size_t)b * args.hkv * G + (size_t)h * G;
+  const int hq = args.hkv * G;
+  // Output (and partial) rows of query row j, head g: qh0 + j * hq + g.
+  const size_t qh0 = (size_t)b * nq * hq + (size_t)h * G;
   TQ* out_row = out_ptr + qh0 * D;
   if (ctx <= 0) {
-    // Defined result for an empty context: a zero row (written by partition 0).
+    // Defined result for an empty context: zero rows (written by partition 0).
     if (part == 0) {
-      for (int i = lane; i < G * D / EPV; i += kWave) st16(out_row + (size_t)i * EPV, zero16());
+      for (int j = 0; j < nq; ++j) {
+        for (int i = lane; i < G * D / EPV; i += kWave)
+          st16(out_row + (size_t)j * hq * D + (size_t)i * EPV, zero16());
+      }
     }
     return;
   }
@@ -790,13 +819,13 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   if (tok_begin >= ctx) return;
   const int tok_end = min(ctx, tok_begin + prm.part_tokens);
   int done = 0;
-  const auto st = run_seg<T, D, G>(args, lds[wave], b, h, tok_begin, tok_end, done, 0);
+  const auto st = run_seg<T, D, G, MQ>(args, lds[wave], b, h, tok_begin, tok_end, ctx, done, 0);
   if (ctx <= prm.part_tokens) {
-    write_rows<T, D, G>(out_row, st, args.v_scale);
+    write_rows<T, D, G>(out_row, st, args.v_scale, nq, hq);
   } else {
     write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + qh0 * prm.max_parts + part, prm.max_parts,
                            ws_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st,
-                           args.v_scale);
+                           args.v_scale, nq, hq);
   }
 }
 
@@ -843,9 +872,9 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int lane = threadIdx.x & 63;
   const int f = lane % kSlices, ph = lane / kSlices;
   const long pair = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hq = prm.num_kv_heads * prm.group;
-  if (pair >= (long)prm.num_seqs * hq) return;
-  const int b = (int)(pair / hq);
+  const int rows = prm.q_per_seq * prm.num_kv_heads * prm.group;   // output rows per sequence
+  if (pair >= (long)prm.num_seqs * rows) return;
+  const int b = (int)(pair / rows);
   const int ctx = context_lens[b];
   const int nparts = (ctx + prm.part_tokens - 1) / prm.part_tokens;
   if (nparts <= 1) return;
@@ -942,7 +971,7 @@ struct alignas(16) SlotDesc {
   int pad[2];
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool MQ>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_balanced_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     SlotDesc* __restrict__ ws_desc, const int32_t* __restrict__ context_lens, DecodeArgs args,
@@ -950,12 +979,13 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   __shared__ SegLds<T, D, G> lds[4];
   __shared__ int cum[kMaxBalancedSeqs + 1];
   __shared__ int scan_scratch[256];
+  const int nq = MQ ? args.nq : 1;   // query rows per sequence
   const int total = window_prefix_sum(context_lens, prm.num_seqs, args.hkv, cum, scan_scratch);
 
   // Defined result for empty contexts: zero rows, spread over the workgroups.
   using TQ = typename IoType<T>::type;
   constexpr int EPV = ElemTraits<TQ>::kPerVec;
-  const size_t seq_vecs = (size_t)args.hkv * G * D / EPV;
+  const size_t seq_vecs = (size_t)nq * args.hkv * G * D / EPV;
   for (int b = blockIdx.x; b < prm.num_seqs; b += gridDim.x) {
     if (cum[b + 1] != cum[b]) continue;
     TQ* o = out_ptr + (size_t)b * seq_vecs * EPV;
@@ -986,15 +1016,18 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
     const int h = r / nwb;
     const int w0 = r % nwb;
     const int w1 = min(nwb, w0 + (x1 - x));
-    const auto st = run_seg<T, D, G>(args, lds[wave], b, h, w0 * 64, min(ctx, w1 * 64), done, x1 - x0);
-    const size_t qh0 = (size_t)b * args.hkv * G + (size_t)h * G;
+    const auto st = run_seg<T, D, G, MQ>(args, lds[wave], b, h, w0 * 64, min(ctx, w1 * 64), ctx, done, x1 - x0);
+    const int hq = args.hkv * G;
+    const size_t qh0 = (size_t)b * nq * hq + (size_t)h * G;
     if (w0 == 0 && w1 == nwb) {
-      write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale);
+      write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, nq, hq);
     } else {
       // Slot 0 holds the share's first segment, slot 1 its last one.
       const int slot = (x == x0) ? 0 : 1;
-      const size_t base = ((size_t)wid * 2 + slot) * G;
-      write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st, args.v_scale);
+      // A slot holds nq * G summary rows, column (row j, head g) at j * G + g.
+      const size_t base = ((size_t)wid * 2 + slot) * nq * G;
+      write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st, args.v_scale,
+                             nq, G);
       desc[slot].row = b * args.hkv + h;
       desc[slot].row_start = x - w0;
       desc[slot].w0 = w0;
@@ -1037,12 +1070,14 @@ __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
     if (d.row < 0 || d.w0 != 0) continue;
     const int total = d.total;
     const long last = share_of((long)d.row_start + d.row_windows - 1, nw, total);
-
+    const int nq = prm.q_per_seq;
+    for (int qr = 0; qr < nq; ++qr) {   // the sequence's query rows, one after another
     // Lane slice f = lane + 64 j covers head f / (D/4), dims 4 (f % (D/4)) .. +4.
     float m[NF], l[NF];
     float4 acc[NF];
     {
-      const size_t row0 = ((size_t)wid * 2 + slot) * G;   // the first piece, always non-empty
+      // The first piece: it holds key 0, which every query row sees.
+      const size_t row0 = (((size_t)wid * 2 + slot) * nq + qr) * G;
 #pragma unroll
       for (int j = 0; j < NF; ++j) {
         const int f = min(lane + kWave * j, kSlices - 1);
@@ -1060,7 +1095,7 @@ __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
       for (int u = 0; u < kPieces; ++u) {
         const long i = min(i0 + u, last);
         live[u] = (i0 + u <= last) && share_begin(i, nw, total) != share_begin(i + 1, nw, total);
-        const size_t rowi = (size_t)i * 2 * G;             // slot 0 of wave i
+        const size_t rowi = ((size_t)i * 2 * nq + qr) * G;   // slot 0 of wave i, row qr
 #pragma unroll
         for (int j = 0; j < NF; ++j) {
           const int f = min(lane + kWave * j, kSlices - 1);
@@ -1082,26 +1117,28 @@ __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
         }
       }
     }
-    T* out = out_ptr + (size_t)d.row * G * D;
+    const int b = d.row / prm.num_kv_heads, h = d.row % prm.num_kv_heads;
+    T* out = out_ptr + (((size_t)b * nq + qr) * prm.num_kv_heads * G + (size_t)h * G) * D;
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
       const int f = lane + kWave * j;
       if (f < kSlices) store_row4<T>(out + (size_t)f * 4, acc[j], 1.0f / l[j]);
     }
+    }
   }
 }
 
-template <typename T, int D, int G>
-hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
+template <typename T, int D, int G, bool MQ>
+hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
   using TQ = typename IoType<T>::type;
   const DecodeArgs args{prm.query, prm.kpool, prm.vpool, prm.block_tables, prm.num_kv_heads,
-                        prm.max_blocks, prm.scale_log2, prm.v_scale};
+                        prm.max_blocks, prm.scale_log2, prm.v_scale, prm.q_per_seq};
   TQ* out = static_cast<TQ*>(prm.out);
   hipError_t err;
   if (prm.num_waves > 0) {
     timer.begin(KernelKind::kDecodePartition, stream);
     SlotDesc* desc = static_cast<SlotDesc*>(prm.ws_desc);
-    hipLaunchKernelGGL((decode_balanced_kernel<T, D, G>), dim3((unsigned)((prm.num_waves + 3) / 4)),
+    hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ>), dim3((unsigned)((prm.num_waves + 3) / 4)),
                        dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
     timer.end(KernelKind::kDecodePartition, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1113,12 +1150,12 @@ hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const K
   }
   const long units = (long)prm.num_kv_heads * prm.num_seqs * prm.max_parts;
   timer.begin(KernelKind::kDecodePartition, stream);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G>), dim3((unsigned)((units + 3) / 4)), dim3(256),
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ>), dim3((unsigned)((units + 3) / 4)), dim3(256),
                      0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
   timer.end(KernelKind::kDecodePartition, stream);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (prm.max_parts > 1) {
-    const long pairs = (long)prm.num_seqs * prm.num_kv_heads * G;
+    const long pairs = (long)prm.num_seqs * prm.q_per_seq * prm.num_kv_heads * G;
     timer.begin(KernelKind::kDecodeReduce, stream);
     hipLaunchKernelGGL((decode_reduce_kernel<TQ, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256),
                        0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, prm);
@@ -1128,12 +1165,23 @@ hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const K
   return err;
 }
 
+// Several query rows per sequence run on the matrix cores only.
 template <typename T, int D, int G>
+hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
+  if constexpr (UsesMfma<T>::value) {
+    if (prm.q_per_seq > 1) return launch_decode_tgm<T, D, G, true>(prm, stream, timer);
+  } else {
+    if (prm.q_per_seq > 1) return hipErrorNotSupported;
+  }
+  return launch_decode_tgm<T, D, G, false>(prm, stream, timer);
+}
+
+template <typename T, int D, int G, bool MQ>
 int balanced_waves_per_cu() {
   static int cached = 0;
   if (cached == 0) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ>, 256, 0) !=
             hipSuccess ||
         blocks <= 0) {
       (void)hipGetLastError();
@@ -1159,19 +1207,27 @@ hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream, const Ke
   }
 }
 
-template <typename T, int D>
-int waves_per_cu_t(int group) {
+template <typename T, int D, bool MQ>
+int waves_per_cu_tm(int group) {
   switch (group) {
-    case 1: return balanced_waves_per_cu<T, D, 1>();
-    case 2: return balanced_waves_per_cu<T, D, 2>();
-    case 3: return balanced_waves_per_cu<T, D, 3>();
-    case 4: return balanced_waves_per_cu<T, D, 4>();
-    case 5: return balanced_waves_per_cu<T, D, 5>();
-    case 6: return balanced_waves_per_cu<T, D, 6>();
-    case 7: return balanced_waves_per_cu<T, D, 7>();
-    case 8: return balanced_waves_per_cu<T, D, 8>();
+    case 1: return balanced_waves_per_cu<T, D, 1, MQ>();
+    case 2: return balanced_waves_per_cu<T, D, 2, MQ>();
+    case 3: return balanced_waves_per_cu<T, D, 3, MQ>();
+    case 4: return balanced_waves_per_cu<T, D, 4, MQ>();
+    case 5: return balanced_waves_per_cu<T, D, 5, MQ>();
+    case 6: return balanced_waves_per_cu<T, D, 6, MQ>();
+    case 7: return balanced_waves_per_cu<T, D, 7, MQ>();
+    case 8: return balanced_waves_per_cu<T, D, 8, MQ>();
     default: return 8;
   }
+}
+
+template <typename T, int D>
+int waves_per_cu_t(int group, bool multi) {
+  if constexpr (UsesMfma<T>::value) {
+    if (multi) return waves_per_cu_tm<T, D, true>(group);
+  }
+  return waves_per_cu_tm<T, D, false>(group);
 }
 
 }  // namespace
@@ -1180,12 +1236,12 @@ int decode_balanced_max_seqs() { return kMaxBalancedSeqs; }
 
 size_t decode_balanced_desc_bytes() { return sizeof(SlotDesc); }
 
-int decode_balanced_waves_per_cu(PoolType type, int head_dim, int group) {
+int decode_balanced_waves_per_cu(PoolType type, int head_dim, int group, bool multi) {
   if (type == PoolType::kFP8)
-    return head_dim == 128 ? waves_per_cu_t<uint8_t, 128>(group) : waves_per_cu_t<uint8_t, 64>(group);
+    return head_dim == 128 ? waves_per_cu_t<uint8_t, 128>(group, multi) : waves_per_cu_t<uint8_t, 64>(group, multi);
   if (type == PoolType::kBF16)
-    return head_dim == 128 ? waves_per_cu_t<uint16_t, 128>(group) : waves_per_cu_t<uint16_t, 64>(group);
-  return head_dim == 128 ? waves_per_cu_t<float, 128>(group) : waves_per_cu_t<float, 64>(group);
+    return head_dim == 128 ? waves_per_cu_t<uint16_t, 128>(group, multi) : waves_per_cu_t<uint16_t, 64>(group, multi);
+  return head_dim == 128 ? waves_per_cu_t<float, 128>(group, false) : waves_per_cu_t<float, 64>(group, false);
 }
 
 hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,

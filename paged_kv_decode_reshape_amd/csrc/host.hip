@@ -284,39 +284,50 @@ pkv_status reshape_and_cache(const pkv_pool* pool, int layer, const void* key,
   return PKV_OK;
 }
 
-pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_seqs,
-                                                  int num_q_heads, int max_blocks_per_seq,
-                                                  int partition_size, size_t* bytes) {
+}  // extern "C"
+
+namespace {
+
+constexpr int kMfmaColumns = 16;   // query rows x heads of a group that one matrix-core segment holds
+
+pkv_status decode_workspace(const pkv_pool* pool, int num_seqs, int q_per_seq, int num_q_heads,
+                            int max_blocks_per_seq, int partition_size, size_t* bytes) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
   if (!bytes) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
-  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
-    return fail(PKV_ERR_INVALID_ARG, "num_seqs >= 0, num_q_heads > 0 and max_blocks_per_seq > 0 required");
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0 || q_per_seq <= 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "num_seqs >= 0, queries_per_seq > 0, num_q_heads > 0 and max_blocks_per_seq > 0 required");
   if (num_q_heads % pool->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
                 num_q_heads, pool->num_kv_heads);
   DecodeSplit sp;
   pkv_status st = decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
   if (st != PKV_OK) return st;
-  const size_t rows = decode_summary_rows(sp, num_seqs, num_q_heads, num_q_heads / pool->num_kv_heads);
+  const size_t rows = decode_summary_rows(sp, num_seqs, num_q_heads, num_q_heads / pool->num_kv_heads) *
+                      (size_t)q_per_seq;
   *bytes = rows == 0 ? 0 : round16(rows * 2 * sizeof(float)) + rows * pool->head_dim * sizeof(float);
   if (sp.balanced) *bytes += (size_t)sp.wave_cap * 2 * pkv::decode_balanced_desc_bytes();
   return PKV_OK;
 }
 
-pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
-                                  const void* query, const int32_t* block_tables,
-                                  const int32_t* context_lens, int num_seqs,
-                                  int num_q_heads, int max_blocks_per_seq, float scale,
-                                  int partition_size, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* query, int q_per_seq,
+                      const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                      int num_q_heads, int max_blocks_per_seq, float scale, int partition_size,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   pkv_status st = check_pool_layer(pool, layer);
   if (st != PKV_OK) return st;
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (q_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "queries_per_seq must be positive (got %d)", q_per_seq);
   if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 num_q_heads, pool->num_kv_heads);
   const int group = num_q_heads / pool->num_kv_heads;
   if (group > 8) return fail(PKV_ERR_UNSUPPORTED, "%d query heads per KV head unsupported (1..8)", group);
+  if (q_per_seq > 1 && pool->dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "several queries per sequence run on the matrix cores: bf16 and e4m3 pools only");
+  if (q_per_seq * group > kMfmaColumns)
+    return fail(PKV_ERR_UNSUPPORTED, "queries_per_seq (%d) x query heads per KV head (%d) must be <= %d",
+                q_per_seq, group, kMfmaColumns);
   if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
   if (num_seqs == 0) return PKV_OK;
@@ -329,8 +340,7 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
   st = decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
   if (st != PKV_OK) return st;
   size_t need = 0;
-  st = paged_attention_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
-                                              partition_size, &need);
+  st = decode_workspace(pool, num_seqs, q_per_seq, num_q_heads, max_blocks_per_seq, partition_size, &need);
   if (st != PKV_OK) return st;
   if (need > 0) {
     if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
@@ -341,13 +351,13 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
   const pkv::PoolType type = pool_type(pool->dtype);
   int num_waves = 0;
   if (sp.balanced) {
-    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, group);
+    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, group, q_per_seq > 1);
     num_waves = (int)std::max(1L, std::min(sp.wave_cap, slots));
   } else {
     const long units = (long)pool->num_kv_heads * num_seqs * sp.max_parts;
     if ((units + 3) / 4 >= (1L << 24)) return fail(PKV_ERR_UNSUPPORTED, "too many work units in one call");
   }
-  const size_t rows = decode_summary_rows(sp, num_seqs, num_q_heads, group);
+  const size_t rows = decode_summary_rows(sp, num_seqs, num_q_heads, group) * (size_t)q_per_seq;
   float* ws_ml = static_cast<float*>(workspace);
   float* ws_o = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round16(rows * 2 * sizeof(float)))
                          : nullptr;
@@ -357,11 +367,49 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
                         block_tables, context_lens, num_seqs, pool->num_kv_heads, group,
                         pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
                         num_waves, scale * 1.4426950408889634f * pool->k_scale[layer],
-                        pool->v_scale[layer]};
+                        pool->v_scale[layer], q_per_seq};
   (void)hipGetLastError();
   hipError_t err = pkv::launch_decode(prm, type, (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "paged_attention_decode launch");
   return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_seqs,
+                                                  int num_q_heads, int max_blocks_per_seq,
+                                                  int partition_size, size_t* bytes) {
+  return decode_workspace(pool, num_seqs, 1, num_q_heads, max_blocks_per_seq, partition_size, bytes);
+}
+
+pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
+                                  const void* query, const int32_t* block_tables,
+                                  const int32_t* context_lens, int num_seqs,
+                                  int num_q_heads, int max_blocks_per_seq, float scale,
+                                  int partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_run(pool, layer, out, query, 1, block_tables, context_lens, num_seqs, num_q_heads,
+                    max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+pkv_status paged_attention_decode_multi_workspace_bytes(const pkv_pool* pool, int num_seqs,
+                                                        int queries_per_seq, int num_q_heads,
+                                                        int max_blocks_per_seq, int partition_size,
+                                                        size_t* bytes) {
+  return decode_workspace(pool, num_seqs, queries_per_seq, num_q_heads, max_blocks_per_seq, partition_size,
+                          bytes);
+}
+
+pkv_status paged_attention_decode_multi(const pkv_pool* pool, int layer, void* out, const void* query,
+                                        int queries_per_seq, const int32_t* block_tables,
+                                        const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                        int max_blocks_per_seq, float scale, int partition_size,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_run(pool, layer, out, query, queries_per_seq, block_tables, context_lens, num_seqs,
+                    num_q_heads, max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes,
+                    stream);
 }
 
 pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* out,

@@ -35,8 +35,8 @@ struct AppendParams {
 
 struct DecodeParams {
   void* out;
-  float* ws_ml;            // float2 [B][Hq][max_parts]: (max in base 2, normalizer)
-  float* ws_o;             // float  [B][Hq][max_parts][D]: unnormalized partial output
+  float* ws_ml;            // float2 [B*q_per_seq][Hq][max_parts]: (max in base 2, normalizer)
+  float* ws_o;             // float  [B*q_per_seq][Hq][max_parts][D]: unnormalized partial output
   void* ws_desc;           // balanced split: two slot descriptors per wave
   const void* query;
   const void* kpool;
@@ -53,6 +53,7 @@ struct DecodeParams {
   int num_waves;           // > 0: balanced split over this many wavefronts
   float scale_log2;        // scale * log2(e), times the K scale of an e4m3 pool
   float v_scale;           // e4m3 pools: the V scale; else 1
+  int q_per_seq;           // query rows per sequence, at positions ctx - q_per_seq .. ctx - 1
 };
 
 struct PrefillParams {
@@ -78,9 +79,10 @@ hipError_t launch_append(const AppendParams& prm, PoolType type, hipStream_t str
                          const KernelTimer& timer);
 hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer);
-// Balanced decode: resident wavefronts per CU of its kernel, the largest
-// batch its in-LDS prefix sum handles, and the size of one slot descriptor.
-int decode_balanced_waves_per_cu(PoolType type, int head_dim, int group);
+// Balanced decode: resident wavefronts per CU of its kernel (multi: the
+// several-query-rows variant), the largest batch its in-LDS prefix sum
+// handles, and the size of one slot descriptor.
+int decode_balanced_waves_per_cu(PoolType type, int head_dim, int group, bool multi);
 int decode_balanced_max_seqs();
 size_t decode_balanced_desc_bytes();
 hipError_t launch_prefill(const PrefillParams& prm, PoolType type, hipStream_t stream, const KernelTimer& timer);

@@ -123,6 +123,23 @@ class DevicePool:
                                    s.scale if scale is None else scale, part, ws, wsb)
         return out
 
+    def decode_multi(self, q_per_seq: int, partition_size: int | None = None, layer: int = 0):
+        """Several query rows per sequence: the step's prefill chunks, all of
+        length q_per_seq, through paged_attention_decode_multi."""
+        s = self.step
+        bt, cl = s.prefill_inputs()
+        assert np.all(np.diff(s.cu_q_lens) == q_per_seq)
+        q = to_device(s.prefill_query)
+        nseq = len(cl)
+        out = torch.empty((nseq * q_per_seq, s.num_q_heads, s.head_dim), dtype=TORCH_DT[s.dtype], device=DEV)
+        part = s.partition_size if partition_size is None else partition_size
+        wsb = pkv.paged_attention_decode_multi_workspace_bytes(self.handle, nseq, q_per_seq, s.num_q_heads,
+                                                               bt.shape[1], part)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+        pkv.paged_attention_decode_multi(self.handle, layer, out, q, q_per_seq, int_tensor(bt), int_tensor(cl),
+                                         nseq, s.num_q_heads, bt.shape[1], s.scale, part, ws, wsb)
+        return out
+
     def prefill(self, layer: int = 0):
         s = self.step
         bt, cl = s.prefill_inputs()

@@ -115,3 +115,26 @@ def test_fp8_pool_bytes_and_scales():
         assert _status(pkv.kv_pool_set_fp8_scales, hb, [1.0], [1.0])[0] == -1         # not an e4m3 pool
     finally:
         pkv.kv_pool_destroy(hb)
+
+
+def test_multi_query_decode_checks():
+    h = pkv.kv_pool_create(1, 4096, 16, 8, 128, pkv.BF16, [256], [512])
+    hf = pkv.kv_pool_create(1, 64, 16, 8, 128, pkv.F32, [256], [512])
+    try:
+        # workspace: summary rows scale with the query rows per sequence
+        one = pkv.paged_attention_decode_multi_workspace_bytes(h, 3, 1, 32, 128, 512)
+        assert one == pkv.paged_attention_decode_workspace_bytes(h, 3, 32, 128, 512)
+        rows = 3 * 32 * 4 * 4
+        assert pkv.paged_attention_decode_multi_workspace_bytes(h, 3, 4, 32, 128, 512) == \
+            ((rows * 8 + 15) // 16) * 16 + rows * 128 * 4
+        assert _status(pkv.paged_attention_decode_multi_workspace_bytes, h, 3, 0, 32, 128, 512)[0] == -1
+        # rows x heads per KV head must fit the 16 matrix-core columns
+        assert _status(pkv.paged_attention_decode_multi, h, 0, 16, 16, 5, 16, 16, 1, 32, 4, 1.0)[0] == -2
+        assert _status(pkv.paged_attention_decode_multi, h, 0, 16, 16, 0, 16, 16, 1, 32, 4, 1.0)[0] == -1
+        # fp32 pools take one query row per sequence only
+        st, msg = _status(pkv.paged_attention_decode_multi, hf, 0, 16, 16, 2, 16, 16, 1, 32, 4, 1.0)
+        assert st == -2 and "bf16" in msg
+        pkv.paged_attention_decode_multi(h, 0, 16, 16, 4, 16, 16, 0, 32, 4, 1.0)   # no sequences: no-op
+    finally:
+        pkv.kv_pool_destroy(h)
+        pkv.kv_pool_destroy(hf)
