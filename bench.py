@@ -14,6 +14,10 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 --kv-dtype fp8 keeps the same bf16 step (queries, new K/V rows, outputs) but
 stores the cache as e4m3 codes with per-layer scales: the append quantizes,
 attention reads one byte per cached element.
+
+--queries-per-seq T (T > 1) gives every decoding sequence T query rows (a
+speculative-verification step: the last T tokens of each sequence are this
+step's, appended first) and runs paged_attention_decode_multi.
 """
 from __future__ import annotations
 
@@ -63,7 +67,25 @@ def make_step(config: int):
     raise SystemExit(f"--config {config}: the bench runs configs 3, 4 or 5 (1 and 2 are parity cases)")
 
 
-def algorithmic_bytes(step, kv_dtype: str = "bf16"):
+def multi_query_inputs(step, t: int, seed: int = 11):
+    """T query rows and T new K/V rows (the last T positions) per decoding
+    sequence, seeded N(0, 1) rounded to bf16, and their slots."""
+    from paged_kv_decode_reshape_amd import workloads as W
+    rng = np.random.default_rng(seed)
+    bt, cl = step.decode_inputs()
+    hq, hkv, d = step.num_q_heads, step.num_kv_heads, step.head_dim
+    slots = []
+    for b in range(len(cl)):
+        pos = np.arange(int(cl[b]) - t, int(cl[b]))
+        slots.append(bt[b, pos // step.block_size].astype(np.int64) * step.block_size + pos % step.block_size)
+    n = len(cl) * t
+    q = W.make_values(rng.standard_normal((n, hq, d), dtype=np.float32), step.dtype)
+    k = W.make_values(rng.standard_normal((n, hkv, d), dtype=np.float32), step.dtype)
+    v = W.make_values(rng.standard_normal((n, hkv, d), dtype=np.float32), step.dtype)
+    return q, k, v, np.concatenate(slots)
+
+
+def algorithmic_bytes(step, kv_dtype: str = "bf16", q_per_seq: int = 1):
     """Bytes a perfect implementation moves (each byte once). e: bytes of a
     query/output/new-row element; ekv: bytes of a cached element."""
     e = 2 if step.dtype == "bf16" else 4
@@ -72,8 +94,8 @@ def algorithmic_bytes(step, kv_dtype: str = "bf16"):
     _, dec_ctx = step.decode_inputs()
     b = len(dec_ctx)
     decode_kv = int(dec_ctx.astype(np.int64).sum()) * hkv * d * 2 * ekv
-    decode_qo = 2 * b * hq * d * e
-    n_new = len(step.new_slots)
+    decode_qo = 2 * b * q_per_seq * hq * d * e
+    n_new = len(step.new_slots) if q_per_seq == 1 else b * q_per_seq
     append = 2 * n_new * hkv * d * (e + ekv)            # read new K,V + write them
     out = {"decode_kv": decode_kv, "decode_qo": decode_qo, "append": append}
     if step.cu_q_lens is not None:
@@ -105,7 +127,7 @@ def read_traffic(kv_dtype: str):
         return None
 
 
-def cpu_baseline(step, kv_dtype: str = "bf16", min_seconds: float = 10.0, max_reps: int = 30):
+def cpu_baseline(step, kv_dtype: str = "bf16", multi=None, min_seconds: float = 10.0, max_reps: int = 30):
     """The oracle, as it stands, on the same workload: append (with e4m3
     quantization for an fp8 cache) + decode (+ prefill), repeated until about
     ``min_seconds`` of CPU work (at least 3 runs) and timed per run; returns the
@@ -128,13 +150,21 @@ def cpu_baseline(step, kv_dtype: str = "bf16", min_seconds: float = 10.0, max_re
             return x
     oracle.append(pk, pv, stored(s.cached_key.f32), stored(s.cached_value.f32), s.cached_slots)
     nk, nv, q = s.new_key.f32, s.new_value.f32, s.decode_query.f32
+    new_slots = s.new_slots
     bt, cl = s.decode_inputs()
+    if multi is not None:     # (T, query, new keys, new values, their slots)
+        t, mq, mk, mv, new_slots = multi
+        nk, nv, q = mk.f32, mv.f32, mq.f32
+        cu = np.arange(len(cl) + 1, dtype=np.int64) * t
     pq = s.prefill_query.f32 if s.prefill_query is not None else None
     times = []
     while len(times) < 3 or (sum(times) < min_seconds and len(times) < max_reps):
         t0 = time.perf_counter()
-        oracle.append(pk, pv, stored(nk), stored(nv), s.new_slots)
-        oracle.paged_decode(q, pk, pv, bt, cl, s.scale)
+        oracle.append(pk, pv, stored(nk), stored(nv), new_slots)
+        if multi is None:
+            oracle.paged_decode(q, pk, pv, bt, cl, s.scale)
+        else:
+            oracle.paged_prefill_chunk(q, cu, pk, pv, bt, cl, s.scale)
         if pq is not None:
             pbt, pcl = s.prefill_inputs()
             oracle.paged_prefill_chunk(pq, s.cu_q_lens, pk, pv, pbt, pcl, s.scale)
@@ -152,6 +182,8 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
                     help="cache storage: bf16 (the workload's dtype) or e4m3 codes")
+    ap.add_argument("--queries-per-seq", type=int, default=1,
+                    help="query rows per decoding sequence (> 1: speculative-verification step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warmup, copy this many MiB device-to-device once (a plain copy "
@@ -181,7 +213,10 @@ def main():
     kvd = args.kv_dtype
     if kvd == "fp8" and s.dtype != "bf16":
         raise SystemExit("--kv-dtype fp8 needs a bf16 workload")
-    ab = algorithmic_bytes(s, kvd)
+    tq = args.queries_per_seq
+    if tq < 1:
+        raise SystemExit("--queries-per-seq must be >= 1")
+    ab = algorithmic_bytes(s, kvd, tq)
     tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     pool_dt = torch.uint8 if kvd == "fp8" else tdt
     pool_e = 1 if kvd == "fp8" else (2 if s.dtype == "bf16" else 4)
@@ -210,16 +245,23 @@ def main():
     for r in range(1, reps):
         k_layers[r].copy_(k_layers[0])
         v_layers[r].copy_(v_layers[0])
-    new_k, new_v = dev_vals(s.new_key), dev_vals(s.new_value)
-    new_slots = dev_int(s.new_slots, torch.int64)
-    n_new = len(s.new_slots)
     bt, cl = s.decode_inputs()
     bt_d, cl_d = dev_int(bt), dev_int(cl)
-    q_d = dev_vals(s.decode_query)
     nseq = len(cl)
-    out = torch.empty((nseq, s.num_q_heads, s.head_dim), dtype=tdt, device=dev)
+    multi = None
+    if tq > 1:
+        multi = (tq,) + multi_query_inputs(s, tq)
+        _, mq, mk, mv, mslots = multi
+        new_k, new_v, new_slots, n_new = dev_vals(mk), dev_vals(mv), dev_int(mslots, torch.int64), len(mslots)
+        q_d = dev_vals(mq)
+    else:
+        new_k, new_v = dev_vals(s.new_key), dev_vals(s.new_value)
+        new_slots = dev_int(s.new_slots, torch.int64)
+        n_new = len(s.new_slots)
+        q_d = dev_vals(s.decode_query)
+    out = torch.empty((nseq * tq, s.num_q_heads, s.head_dim), dtype=tdt, device=dev)
     part = s.partition_size if args.partition_size is None else args.partition_size
-    wsb = pkv.paged_attention_decode_workspace_bytes(pool, nseq, s.num_q_heads, bt.shape[1], part)
+    wsb = pkv.paged_attention_decode_multi_workspace_bytes(pool, nseq, tq, s.num_q_heads, bt.shape[1], part)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     has_prefill = s.cu_q_lens is not None
     if has_prefill:
@@ -235,8 +277,12 @@ def main():
     def one_step(i):
         layer = i % reps
         pkv.reshape_and_cache(pool, layer, new_k, new_v, new_slots, n_new, stream)
-        pkv.paged_attention_decode(pool, layer, out, q_d, bt_d, cl_d, nseq, s.num_q_heads,
-                                   bt.shape[1], s.scale, part, ws, wsb, stream)
+        if tq == 1:
+            pkv.paged_attention_decode(pool, layer, out, q_d, bt_d, cl_d, nseq, s.num_q_heads,
+                                       bt.shape[1], s.scale, part, ws, wsb, stream)
+        else:
+            pkv.paged_attention_decode_multi(pool, layer, out, q_d, tq, bt_d, cl_d, nseq, s.num_q_heads,
+                                             bt.shape[1], s.scale, part, ws, wsb, stream)
         if has_prefill:
             pkv.paged_attention_prefill_chunk(pool, layer, pout, pq_d, cu_d, pbt_d, pcl_d,
                                               len(pcl), ptotal, pmax, s.num_q_heads,
@@ -302,13 +348,14 @@ def main():
         "dtype": s.dtype,
         "data": "synthetic (seeded N(0,1) values, lognormal lengths, churned block tables)",
         "config": {
-            "workload": s.name,
+            "workload": s.name if tq == 1 else f"{s.name}_q{tq}",
             "batch": nseq,
             "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
             "head_dim": s.head_dim, "block_size": s.block_size,
             "context_tokens": int(cl.sum()),
             "partition_size": part if part else "auto",
             "kv_cache_dtype": "fp8_e4m3" if kvd == "fp8" else s.dtype,
+            "queries_per_seq": tq,
             "pool_replicas": reps,
             "parallelism": "single GPU",
         },
@@ -327,7 +374,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic(kvd),
+            "traffic": read_traffic(kvd) if tq == 1 else None,
             "algorithmic_bytes_per_launch": part_bytes,
         },
     }
@@ -338,11 +385,12 @@ def main():
                                   "flops_per_launch": ab["prefill_flops"]}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the same step ...")
-        t_cpu, runs, threads = cpu_baseline(s, kvd)
+        t_cpu, runs, threads = cpu_baseline(s, kvd, multi)
         result["cpu_baseline"] = {
             "value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"the whole step ({s.name}{', e4m3 cache' if kvd == 'fp8' else ''}: append + decode of all {nseq} sequences"
+            "sample": f"the whole step ({s.name}{', e4m3 cache' if kvd == 'fp8' else ''}"
+                      f"{f', {tq} query rows per sequence' if tq > 1 else ''}: append + decode of all {nseq} sequences"
                       f"{' + prefill chunk' if has_prefill else ''}), numpy float64, median of {runs} runs"
                       f" ({runs * t_cpu:.0f} s of CPU work); {t_cpu:.2f} s per step; BLAS pool of"
                       f" {threads} threads, the per-sequence loop single-threaded; {os.cpu_count()} host CPUs",

@@ -1043,9 +1043,10 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   }
 }
 
-// One wavefront per partition wave i: for each split (b, h) row whose first
-// piece (w0 == 0) wave i holds, combine the pieces held by waves i..last with
-// the online-softmax rule, per query head:
+// One wavefront per (partition wave i, query row of the sequence; grid y):
+// for each split (b, h) row whose first piece (w0 == 0) wave i holds, combine
+// the pieces held by waves i..last with the online-softmax rule, per query
+// head:
 //   M = max m,  L = sum 2^(m - M) l,  out = sum 2^(m - M) o / L.
 // Pieces after the first sit in slot 0 of each later wave with a non-empty
 // share, so the piece list follows from the share arithmetic and the loads of
@@ -1071,7 +1072,8 @@ __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
     const int total = d.total;
     const long last = share_of((long)d.row_start + d.row_windows - 1, nw, total);
     const int nq = prm.q_per_seq;
-    for (int qr = 0; qr < nq; ++qr) {   // the sequence's query rows, one after another
+    const int qr = blockIdx.y;            // query row of the sequence (grid y: one per row)
+    {
     // Lane slice f = lane + 64 j covers head f / (D/4), dims 4 (f % (D/4)) .. +4.
     float m[NF], l[NF];
     float4 acc[NF];
@@ -1143,8 +1145,9 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
     timer.end(KernelKind::kDecodePartition, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     timer.begin(KernelKind::kDecodeReduce, stream);
-    hipLaunchKernelGGL((decode_balanced_reduce_kernel<TQ, D, G>), dim3((unsigned)((prm.num_waves + 3) / 4)),
-                       dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, desc, prm);
+    hipLaunchKernelGGL((decode_balanced_reduce_kernel<TQ, D, G>),
+                       dim3((unsigned)((prm.num_waves + 3) / 4), (unsigned)prm.q_per_seq), dim3(256), 0, stream,
+                       out, prm.ws_ml, prm.ws_o, desc, prm);
     timer.end(KernelKind::kDecodeReduce, stream);
     return hipGetLastError();
   }
