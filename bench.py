@@ -184,6 +184,8 @@ def main():
                     help="cache storage: bf16 (the workload's dtype) or e4m3 codes")
     ap.add_argument("--queries-per-seq", type=int, default=1,
                     help="query rows per decoding sequence (> 1: speculative-verification step)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each step in a HIP graph (torch.cuda.CUDAGraph) and time the replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warmup, copy this many MiB device-to-device once (a plain copy "
@@ -276,6 +278,7 @@ def main():
 
     def one_step(i):
         layer = i % reps
+        stream = torch.cuda.current_stream(dev)     # the capture stream while a graph is recorded
         pkv.reshape_and_cache(pool, layer, new_k, new_v, new_slots, n_new, stream)
         if tq == 1:
             pkv.paged_attention_decode(pool, layer, out, q_d, bt_d, cl_d, nseq, s.num_q_heads,
@@ -304,15 +307,35 @@ def main():
     kinds_all = (("append", pkv.KERNEL_APPEND), ("partition", pkv.KERNEL_DECODE_PARTITION),
                  ("reduce", pkv.KERNEL_DECODE_REDUCE), ("prefill", pkv.KERNEL_PREFILL))
     timed_kinds = [pkv.KERNEL_DECODE_PARTITION] + ([pkv.KERNEL_PREFILL] if has_prefill else [])
-    pkv.pkv_timing_enable(2 * args.steps + 8, timed_kinds)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.steps):
-        one_step(args.warmup + i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    kt = {name: pkv.pkv_timing_read(kind) for name, kind in kinds_all if kind in timed_kinds}
-    pkv.pkv_timing_disable()
+    if args.graph:
+        # One captured step per pool replica; step i replays graph i % reps.
+        # Kernel durations then come from the separate eager pass below.
+        graphs = []
+        for r in range(reps):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                one_step(r)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % reps].replay()
+        torch.cuda.synchronize()
+        timed_kinds = []
+        kt = {}
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % reps].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+    else:
+        pkv.pkv_timing_enable(2 * args.steps + 8, timed_kinds)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(args.steps):
+            one_step(args.warmup + i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        kt = {name: pkv.pkv_timing_read(kind) for name, kind in kinds_all if kind in timed_kinds}
+        pkv.pkv_timing_disable()
     # The other kernels' durations, from a separate untimed pass with events on
     # every kernel.
     n_break = min(args.steps, 20)
@@ -362,9 +385,11 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
         "us_per_layer_step": round(ms_per_step * 1e3, 2),
         "kernel_us": {k: round(v, 2) for k, v in avg_us.items()},
-        "kernel_us_source": "partition" + (" and prefill" if has_prefill else "") +
-                            ": HIP events in the timed region; the others: a separate "
+        "kernel_us_source": ("all kernels: a separate eager pass of " if args.graph else
+                             "partition" + (" and prefill" if has_prefill else "") +
+                             ": HIP events in the timed region; the others: a separate ") +
                             f"{n_break}-step pass with events on every kernel",
+        "graph": bool(args.graph),
         "decode_attention_gbs": round(part_bytes / (decode_us * 1e-6) / 1e9, 1) if decode_us else None,
         "algorithmic_bytes": ab,
         "roofline": {
