@@ -6,6 +6,7 @@ from .paged_attention import (  # noqa: F401
     attend_split,
     blocks_for,
     combine,
+    copy_blocks,
     gather,
     kv_cache_bytes,
     new_pool,

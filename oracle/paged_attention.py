@@ -89,6 +89,16 @@ def append(pool_k: np.ndarray, pool_v: np.ndarray, key: np.ndarray, value: np.nd
     pool_v[blk, off] = np.asarray(value)[keep]
 
 
+def copy_blocks(pool_k: np.ndarray, pool_v: np.ndarray, pairs) -> None:
+    """Copy-on-write ("LLM 7 - Efficient LLM Serving", 3., "Sharing and
+    Preemption"; "The Serving Playbook", "Sharing is a reference count"): for
+    each (source, destination) pair, the destination block becomes a copy of
+    the source block, all slots and KV heads, in K and in V."""
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        pool_k[dst] = pool_k[src]
+        pool_v[dst] = pool_v[src]
+
+
 def gather(pool: np.ndarray, block_table_row: np.ndarray, ctx: int) -> np.ndarray:
     """Logical positions 0..ctx-1 of one sequence as a contiguous [ctx, Hkv, D] array.
 

@@ -303,4 +303,32 @@ def pin_last_block_waste_bound(orc):
             assert 0 <= nb * bs - ctx <= bs - 1
 
 
+def pin_copy_on_write_fork(orc):
+    """Two sequences share a 40-token prompt (blocks 3, 7 full and block 5
+    holding 8 tokens); at the fork the partly filled block 5 is copied into
+    block 9 for the second sequence, and each appends its own 6 tokens. Each
+    sequence's gathered cache must equal an unshared cache built for it alone,
+    and the shared prompt's source blocks must still hold the prompt."""
+    rng = np.random.default_rng(21)
+    bs, hkv, d = 16, 2, 8
+    prompt_k, prompt_v = rng.standard_normal((2, 40, hkv, d))
+    tails = rng.standard_normal((2, 2, 6, hkv, d))            # [seq][k/v][token]
+    pk = orc.new_pool(12, bs, hkv, d)
+    pv = orc.new_pool(12, bs, hkv, d)
+    shared = [3, 7, 5]
+    slots = np.array([shared[p // bs] * bs + p % bs for p in range(40)])
+    orc.append(pk, pv, prompt_k, prompt_v, slots)
+    orc.copy_blocks(pk, pv, [[5, 9]])
+    tables = [np.array([3, 7, 5]), np.array([3, 7, 9])]
+    for sq in range(2):
+        pos = np.arange(40, 46)
+        orc.append(pk, pv, tails[sq, 0], tails[sq, 1], tables[sq][pos // bs] * bs + pos % bs)
+    for sq in range(2):
+        want_k = np.concatenate([prompt_k, tails[sq, 0]])
+        want_v = np.concatenate([prompt_v, tails[sq, 1]])
+        assert np.array_equal(orc.gather(pk, tables[sq], 46), want_k)
+        assert np.array_equal(orc.gather(pv, tables[sq], 46), want_v)
+    assert np.array_equal(orc.gather(pk, np.array([3, 7]), 32), prompt_k[:32])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

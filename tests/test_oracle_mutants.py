@@ -28,6 +28,9 @@ MUTANTS = {
     "kv_bytes_no_factor_two": ("return 2 * layers", "return layers"),
     "blocks_floor": ("return (int(ctx) + block_size - 1) // block_size", "return int(ctx) // block_size"),
     "negative_slots_written": ("keep = slots >= 0", "keep = slots >= -1"),
+    "copy_reversed": ("pool_k[dst] = pool_k[src]\n        pool_v[dst] = pool_v[src]",
+                      "pool_k[src] = pool_k[dst]\n        pool_v[src] = pool_v[dst]"),
+    "copy_k_only": ("pool_v[dst] = pool_v[src]", "pass"),
 }
 
 
