@@ -137,6 +137,18 @@ pkv_status reshape_and_cache(const pkv_pool* pool, int layer, const void* key,
                              const void* value, const int64_t* slot_mapping,
                              int num_tokens, void* stream);
 
+/* Copy-on-write: when sequences that share a block diverge, the shared block
+ * is duplicated into a private one ("LLM 7 - Efficient LLM Serving", 3. KV
+ * Cache and PagedAttention, "Sharing and Preemption"; "The Serving
+ * Playbook", "Sharing is a reference count"). For every pair p <
+ * num_pairs, block block_pairs[2p+1] of every layer's K and V pool becomes a
+ * bit-for-bit copy of block block_pairs[2p] (all KV heads, all 16 slots).
+ *   block_pairs: int32 [num_pairs][2] (source, destination), device memory.
+ * Block ids must lie in [0, num_blocks); no destination may appear twice or
+ * also be a source in the same call (the copies would race). num_pairs == 0
+ * is a no-op. Any pool dtype. */
+pkv_status copy_blocks(const pkv_pool* pool, const int32_t* block_pairs, int num_pairs, void* stream);
+
 /* Workspace bytes paged_attention_decode needs for these arguments (0 when no
  * sequence can be split). Depends only on host-side sizes. */
 pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_seqs,

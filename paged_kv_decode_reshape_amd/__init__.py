@@ -20,7 +20,7 @@ __all__ = [
     "PkvError", "F32", "BF16", "FP8_E4M3", "KERNEL_APPEND", "KERNEL_DECODE_PARTITION",
     "KERNEL_DECODE_REDUCE", "KERNEL_PREFILL", "library_path", "load",
     "kv_pool_bytes", "kv_pool_create", "kv_pool_set_fp8_scales", "kv_pool_destroy",
-    "reshape_and_cache",
+    "reshape_and_cache", "copy_blocks",
     "paged_attention_decode_workspace_bytes", "paged_attention_decode",
     "paged_attention_decode_multi_workspace_bytes", "paged_attention_decode_multi",
     "paged_attention_prefill_chunk", "pkv_timing_enable", "pkv_timing_disable",
@@ -48,6 +48,7 @@ _SIGNATURES = {
     "kv_pool_set_fp8_scales": (c_int, [c_void_p, c_int, _P(c_float), _P(c_float)]),
     "kv_pool_destroy": (c_int, [c_void_p]),
     "reshape_and_cache": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_void_p]),
+    "copy_blocks": (c_int, [c_void_p, c_void_p, c_int, c_void_p]),
     "paged_attention_decode_workspace_bytes": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
                                                        _P(c_size_t)]),
     "paged_attention_decode": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -154,6 +155,10 @@ def kv_pool_destroy(pool):
 def reshape_and_cache(pool, layer, key, value, slot_mapping, num_tokens, stream=None):
     _check(load().reshape_and_cache(pool, layer, _ptr(key), _ptr(value), _ptr(slot_mapping),
                                     num_tokens, _stream(stream)))
+
+
+def copy_blocks(pool, block_pairs, num_pairs, stream=None):
+    _check(load().copy_blocks(pool, _ptr(block_pairs), num_pairs, _stream(stream)))
 
 
 def paged_attention_decode_workspace_bytes(pool, num_seqs, num_q_heads, max_blocks_per_seq,

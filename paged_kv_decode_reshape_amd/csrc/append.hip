@@ -107,7 +107,28 @@ hipError_t launch_append_t(const AppendParams& prm, hipStream_t stream, const Ke
   return hipGetLastError();
 }
 
+// Copy-on-write (LLM 7 - Efficient LLM Serving, 3., "Sharing and
+// Preemption"; "The Serving Playbook", "Sharing is a reference count"): when
+// sequences that share a block diverge, the block is duplicated into a
+// private one. A block of a layer's pool holds all KV heads contiguously, so
+// one workgroup copies one (pair, layer, K or V) region with 16-byte vectors.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams prm) {
+  const int pair = blockIdx.x;
+  const int layer = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int32_t src = prm.pairs[2 * pair], dst = prm.pairs[2 * pair + 1];
+  const char* from = static_cast<const char*>(is_v ? prm.v[layer] : prm.k[layer]) + (size_t)src * prm.block_bytes;
+  char* to = static_cast<char*>(is_v ? prm.v[layer] : prm.k[layer]) + (size_t)dst * prm.block_bytes;
+  for (int off = threadIdx.x * 16; off < prm.block_bytes; off += 256 * 16) st16(to + off, ld16(from + off));
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyParams& prm, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)prm.num_pairs, (unsigned)prm.num_layers, 2u), dim3(256), 0,
+                     stream, prm);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const AppendParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer) {

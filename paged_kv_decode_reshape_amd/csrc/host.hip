@@ -378,6 +378,33 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
 
 extern "C" {
 
+pkv_status copy_blocks(const pkv_pool* pool, const int32_t* block_pairs, int num_pairs, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (num_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "num_pairs must be >= 0 (got %d)", num_pairs);
+  if (num_pairs == 0) return PKV_OK;
+  if (!block_pairs) return fail(PKV_ERR_INVALID_ARG, "block_pairs must not be NULL");
+  if (!aligned(block_pairs, 4)) return fail(PKV_ERR_INVALID_ARG, "block_pairs must be 4-byte aligned");
+  if (num_pairs >= (1 << 30)) return fail(PKV_ERR_UNSUPPORTED, "too many pairs in one call");
+  const size_t block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim * elem_bytes(pool->dtype);
+  if (block_bytes % 16 != 0 || block_bytes >= (1u << 31))
+    return fail(PKV_ERR_UNSUPPORTED, "block of %zu bytes unsupported", block_bytes);
+  (void)hipGetLastError();
+  for (int l0 = 0; l0 < pool->num_layers; l0 += pkv::kCopyLayers) {
+    pkv::CopyParams prm{};
+    prm.num_layers = std::min(pkv::kCopyLayers, pool->num_layers - l0);
+    for (int i = 0; i < prm.num_layers; ++i) {
+      prm.k[i] = pool->k_layers[l0 + i];
+      prm.v[i] = pool->v_layers[l0 + i];
+    }
+    prm.pairs = block_pairs;
+    prm.num_pairs = num_pairs;
+    prm.block_bytes = (int)block_bytes;
+    hipError_t err = pkv::launch_copy_blocks(prm, (hipStream_t)stream);
+    if (err != hipSuccess) return hip_fail(err, "copy_blocks launch");
+  }
+  return PKV_OK;
+}
+
 pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_seqs,
                                                   int num_q_heads, int max_blocks_per_seq,
                                                   int partition_size, size_t* bytes) {

@@ -77,6 +77,18 @@ struct PrefillParams {
 
 hipError_t launch_append(const AppendParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer);
+
+// Block copies for copy-on-write: up to kCopyLayers layers per launch.
+constexpr int kCopyLayers = 16;
+struct CopyParams {
+  void* k[kCopyLayers];
+  void* v[kCopyLayers];
+  int num_layers;
+  const int32_t* pairs;    // [num_pairs][2]: (source block, destination block)
+  int num_pairs;
+  int block_bytes;         // bytes of one block of one layer's K (or V) pool, all heads
+};
+hipError_t launch_copy_blocks(const CopyParams& prm, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer);
 // Balanced decode: resident wavefronts per CU of its kernel (multi: the

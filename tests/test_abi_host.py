@@ -138,3 +138,14 @@ def test_multi_query_decode_checks():
     finally:
         pkv.kv_pool_destroy(h)
         pkv.kv_pool_destroy(hf)
+
+
+def test_copy_blocks_checks():
+    h = pkv.kv_pool_create(2, 8, 16, 2, 64, pkv.BF16, [256, 512], [768, 1024])
+    try:
+        pkv.copy_blocks(h, 16, 0)                                  # no pairs: no-op
+        assert _status(pkv.copy_blocks, h, 16, -1)[0] == -1
+        assert _status(pkv.copy_blocks, h, None, 2)[0] == -1
+        assert _status(pkv.copy_blocks, h, 18, 2)[0] == -1         # misaligned pairs
+    finally:
+        pkv.kv_pool_destroy(h)
