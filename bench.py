@@ -18,6 +18,11 @@ attention reads one byte per cached element.
 --queries-per-seq T (T > 1) gives every decoding sequence T query rows (a
 speculative-verification step: the last T tokens of each sequence are this
 step's, appended first) and runs paged_attention_decode_multi.
+
+--config 6 is a parallel-sampling step (32 prompts of 2000 tokens, 8 samples
+each, every sample sharing its prompt's blocks). --shared runs it through
+paged_attention_decode_shared, which reads each prompt's blocks once for its
+8 samples; without it the same step runs through paged_attention_decode.
 """
 from __future__ import annotations
 
@@ -64,7 +69,9 @@ def make_step(config: int):
         return W.long_context()
     if config == 5:
         return W.mixed_chunked_prefill()
-    raise SystemExit(f"--config {config}: the bench runs configs 3, 4 or 5 (1 and 2 are parity cases)")
+    if config == 6:
+        return W.parallel_sampling()
+    raise SystemExit(f"--config {config}: the bench runs configs 3, 4, 5 or 6 (1 and 2 are parity cases)")
 
 
 def multi_query_inputs(step, t: int, seed: int = 11):
@@ -85,15 +92,17 @@ def multi_query_inputs(step, t: int, seed: int = 11):
     return q, k, v, np.concatenate(slots)
 
 
-def algorithmic_bytes(step, kv_dtype: str = "bf16", q_per_seq: int = 1):
+def algorithmic_bytes(step, kv_dtype: str = "bf16", q_per_seq: int = 1, shared: bool = False):
     """Bytes a perfect implementation moves (each byte once). e: bytes of a
-    query/output/new-row element; ekv: bytes of a cached element."""
+    query/output/new-row element; ekv: bytes of a cached element. shared: a
+    prefix shared by a group of sequences is counted once for the group."""
     e = 2 if step.dtype == "bf16" else 4
     ekv = 1 if kv_dtype == "fp8" else e
     hkv, hq, d = step.num_kv_heads, step.num_q_heads, step.head_dim
     _, dec_ctx = step.decode_inputs()
     b = len(dec_ctx)
-    decode_kv = int(dec_ctx.astype(np.int64).sum()) * hkv * d * 2 * ekv
+    tokens = step.info["unique_tokens"] if shared else int(dec_ctx.astype(np.int64).sum())
+    decode_kv = tokens * hkv * d * 2 * ekv
     decode_qo = 2 * b * q_per_seq * hq * d * e
     n_new = len(step.new_slots) if q_per_seq == 1 else b * q_per_seq
     append = 2 * n_new * hkv * d * (e + ekv)            # read new K,V + write them
@@ -184,6 +193,9 @@ def main():
                     help="cache storage: bf16 (the workload's dtype) or e4m3 codes")
     ap.add_argument("--queries-per-seq", type=int, default=1,
                     help="query rows per decoding sequence (> 1: speculative-verification step)")
+    ap.add_argument("--shared", action="store_true",
+                    help="decode through paged_attention_decode_shared with the step's sharing groups "
+                         "(--config 6)")
     ap.add_argument("--graph", action="store_true",
                     help="capture each step in a HIP graph (torch.cuda.CUDAGraph) and time the replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -218,7 +230,10 @@ def main():
     tq = args.queries_per_seq
     if tq < 1:
         raise SystemExit("--queries-per-seq must be >= 1")
-    ab = algorithmic_bytes(s, kvd, tq)
+    shared = bool(args.shared)
+    if shared and ("group_starts" not in s.info or tq != 1):
+        raise SystemExit("--shared needs a workload with sharing groups (--config 6) and one query per sequence")
+    ab = algorithmic_bytes(s, kvd, tq, shared)
     tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float32
     pool_dt = torch.uint8 if kvd == "fp8" else tdt
     pool_e = 1 if kvd == "fp8" else (2 if s.dtype == "bf16" else 4)
@@ -263,7 +278,13 @@ def main():
         q_d = dev_vals(s.decode_query)
     out = torch.empty((nseq * tq, s.num_q_heads, s.head_dim), dtype=tdt, device=dev)
     part = s.partition_size if args.partition_size is None else args.partition_size
-    wsb = pkv.paged_attention_decode_multi_workspace_bytes(pool, nseq, tq, s.num_q_heads, bt.shape[1], part)
+    if shared:
+        gs_d, pl_d = dev_int(s.info["group_starts"]), dev_int(s.info["prefix_lens"])
+        n_groups = len(s.info["prefix_lens"])
+        max_group = int(np.max(np.diff(s.info["group_starts"])))
+        wsb = pkv.paged_attention_decode_shared_workspace_bytes(pool, nseq, s.num_q_heads, bt.shape[1], part)
+    else:
+        wsb = pkv.paged_attention_decode_multi_workspace_bytes(pool, nseq, tq, s.num_q_heads, bt.shape[1], part)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     has_prefill = s.cu_q_lens is not None
     if has_prefill:
@@ -280,7 +301,11 @@ def main():
         layer = i % reps
         stream = torch.cuda.current_stream(dev)     # the capture stream while a graph is recorded
         pkv.reshape_and_cache(pool, layer, new_k, new_v, new_slots, n_new, stream)
-        if tq == 1:
+        if shared:
+            pkv.paged_attention_decode_shared(pool, layer, out, q_d, bt_d, cl_d, gs_d, pl_d, nseq, n_groups,
+                                              max_group, s.num_q_heads, bt.shape[1], s.scale, part, ws, wsb,
+                                              stream)
+        elif tq == 1:
             pkv.paged_attention_decode(pool, layer, out, q_d, bt_d, cl_d, nseq, s.num_q_heads,
                                        bt.shape[1], s.scale, part, ws, wsb, stream)
         else:
@@ -305,8 +330,10 @@ def main():
     # (the decode partition kernel, and the prefill kernel when present); each
     # event pair adds a gap to the stream.
     kinds_all = (("append", pkv.KERNEL_APPEND), ("partition", pkv.KERNEL_DECODE_PARTITION),
-                 ("reduce", pkv.KERNEL_DECODE_REDUCE), ("prefill", pkv.KERNEL_PREFILL))
-    timed_kinds = [pkv.KERNEL_DECODE_PARTITION] + ([pkv.KERNEL_PREFILL] if has_prefill else [])
+                 ("reduce", pkv.KERNEL_DECODE_REDUCE), ("prefill", pkv.KERNEL_PREFILL),
+                 ("prefix", pkv.KERNEL_DECODE_PREFIX))
+    timed_kinds = [pkv.KERNEL_DECODE_PARTITION] + ([pkv.KERNEL_PREFILL] if has_prefill else []) + \
+        ([pkv.KERNEL_DECODE_PREFIX] if shared else [])
     if args.graph:
         # One captured step per pool replica; step i replays graph i % reps.
         # Kernel durations then come from the separate eager pass below.
@@ -355,8 +382,11 @@ def main():
     step_bytes = ab["decode_kv"] + ab["decode_qo"] + ab["append"] + ab.get("prefill_bytes", 0)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     part_bytes = ab["decode_kv"] + ab["decode_qo"]
-    achieved = part_bytes / (avg_us["partition"] * 1e-6) / 1e9 if avg_us["partition"] else 0.0
-    decode_us = avg_us["partition"] + avg_us["reduce"]
+    # With shared prefixes the KV is read by two kernels (the groups' shared
+    # partitions, then each sequence's own): the roofline covers both.
+    read_us = avg_us["partition"] + avg_us["prefix"]
+    achieved = part_bytes / (read_us * 1e-6) / 1e9 if read_us else 0.0
+    decode_us = read_us + avg_us["reduce"]
     result = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) and us per layer-step",
         "value": round(value, 1),
@@ -369,7 +399,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": s.dtype,
-        "data": "synthetic (seeded N(0,1) values, lognormal lengths, churned block tables)",
+        "data": ("synthetic (seeded N(0,1) values, 32 prompts x 8 samples sharing prompt blocks, "
+                 "uniform 1..512 generated tokens)" if "group_starts" in s.info else
+                 "synthetic (seeded N(0,1) values, lognormal lengths, churned block tables)"),
         "config": {
             "workload": s.name if tq == 1 else f"{s.name}_q{tq}",
             "batch": nseq,
@@ -379,6 +411,7 @@ def main():
             "partition_size": part if part else "auto",
             "kv_cache_dtype": "fp8_e4m3" if kvd == "fp8" else s.dtype,
             "queries_per_seq": tq,
+            "shared_prefix_decode": shared,
             "pool_replicas": reps,
             "parallelism": "single GPU",
         },
@@ -393,13 +426,13 @@ def main():
         "decode_attention_gbs": round(part_bytes / (decode_us * 1e-6) / 1e9, 1) if decode_us else None,
         "algorithmic_bytes": ab,
         "roofline": {
-            "kernel": "decode_partition_kernel",
+            "kernel": "decode_prefix_kernel + decode_partition_kernel" if shared else "decode_partition_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic(kvd) if tq == 1 else None,
+            "traffic": read_traffic(kvd) if tq == 1 and not shared and args.config == 3 else None,
             "algorithmic_bytes_per_launch": part_bytes,
         },
     }

@@ -214,6 +214,48 @@ pkv_status paged_attention_decode_multi(const pkv_pool* pool, int layer, void* o
                                         int max_blocks_per_seq, float scale, int partition_size,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode over shared prefixes. Sequences that share their leading tokens
+ * point their block tables at the same physical blocks ("The Serving
+ * Playbook", "Paged KV cache" and "Sharing is a reference count": parallel
+ * sampling, beam search and a common system prompt are all several block
+ * tables over one set of blocks). When such sequences decode in one batch the
+ * shared portion need be read from HBM only once for the batch, not once per
+ * sequence ("The Serving Playbook", "RadixAttention", "The tree changes what
+ * the scheduler should do"). The result is that of paged_attention_decode on
+ * the same arguments (within rounding); only the work is organised
+ * differently: for each group, the whole partitions of partition_size tokens
+ * that lie inside its prefix are read once and multiplied against all
+ * members' query heads together on the matrix cores; every member's remaining
+ * partitions are read on their own; one reduction merges all partitions.
+ *   out, query, block_tables, context_lens, scale: as for
+ *     paged_attention_decode (one query row per sequence).
+ *   group_starts: int32 [num_groups + 1], device memory. Group k is
+ *     sequences group_starts[k] .. group_starts[k+1]-1; group_starts[0] == 0,
+ *     non-decreasing, group_starts[num_groups] == num_seqs (so every sequence
+ *     is in exactly one group; a sequence that shares nothing is a group of
+ *     one with prefix 0). No group may have more than max_group_size members.
+ *   prefix_lens: int32 [num_groups], device memory: group k's first
+ *     prefix_lens[k] tokens sit in the same physical blocks, with the same
+ *     block-table entries, for every member (caller contract). The blocks are
+ *     read through the group's first sequence's table; tokens past that
+ *     sequence's context or a member's context are not treated as shared.
+ *   partition_size: > 0, a multiple of 64, or 0 for 256 tokens. Tokens of a
+ *     prefix past its last whole partition are read per member.
+ *   workspace: at least paged_attention_decode_shared_workspace_bytes(...)
+ *     bytes, 16-byte aligned; contents on entry are ignored.
+ * bf16 and e4m3 pools (the shared products run on bf16 MFMA); an fp32 pool
+ * gives PKV_ERR_UNSUPPORTED. */
+pkv_status paged_attention_decode_shared_workspace_bytes(const pkv_pool* pool, int num_seqs,
+                                                         int num_q_heads, int max_blocks_per_seq,
+                                                         int partition_size, size_t* bytes);
+pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* out, const void* query,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         const int32_t* group_starts, const int32_t* prefix_lens,
+                                         int num_seqs, int num_groups, int max_group_size,
+                                         int num_q_heads, int max_blocks_per_seq, float scale,
+                                         int partition_size, void* workspace, size_t workspace_bytes,
+                                         void* stream);
+
 /* Prefill-chunk attention: sequence s owns query rows
  * cu_q_lens[s] .. cu_q_lens[s+1]-1 (T_s = its chunk length, T_s <= max_q_len).
  * The chunk's own K/V must already be appended, so the cache holds
@@ -248,7 +290,8 @@ typedef enum {
     PKV_KERNEL_DECODE_PARTITION = 1,
     PKV_KERNEL_DECODE_REDUCE = 2,
     PKV_KERNEL_PREFILL = 3,
-    PKV_KERNEL_KINDS = 4
+    PKV_KERNEL_DECODE_PREFIX = 4,   /* shared-prefix partitions of paged_attention_decode_shared */
+    PKV_KERNEL_KINDS = 5
 } pkv_kernel_kind;
 
 pkv_status pkv_timing_enable(int max_launches, unsigned int kind_mask);

@@ -18,17 +18,19 @@ import os
 
 __all__ = [
     "PkvError", "F32", "BF16", "FP8_E4M3", "KERNEL_APPEND", "KERNEL_DECODE_PARTITION",
-    "KERNEL_DECODE_REDUCE", "KERNEL_PREFILL", "library_path", "load",
+    "KERNEL_DECODE_REDUCE", "KERNEL_PREFILL", "KERNEL_DECODE_PREFIX", "library_path", "load",
     "kv_pool_bytes", "kv_pool_create", "kv_pool_set_fp8_scales", "kv_pool_destroy",
     "reshape_and_cache", "copy_blocks",
     "paged_attention_decode_workspace_bytes", "paged_attention_decode",
     "paged_attention_decode_multi_workspace_bytes", "paged_attention_decode_multi",
+    "paged_attention_decode_shared_workspace_bytes", "paged_attention_decode_shared",
     "paged_attention_prefill_chunk", "pkv_timing_enable", "pkv_timing_disable",
     "pkv_timing_read", "pkv_last_error", "EXPORTED_SYMBOLS",
 ]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 KERNEL_APPEND, KERNEL_DECODE_PARTITION, KERNEL_DECODE_REDUCE, KERNEL_PREFILL = 0, 1, 2, 3
+KERNEL_DECODE_PREFIX = 4
 
 _STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID_ARG", -2: "PKV_ERR_UNSUPPORTED",
            -3: "PKV_ERR_HIP", -4: "PKV_ERR_WORKSPACE"}
@@ -59,6 +61,11 @@ _SIGNATURES = {
     "paged_attention_decode_multi": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p,
                                              c_void_p, c_int, c_int, c_int, c_float, c_int, c_void_p,
                                              c_size_t, c_void_p]),
+    "paged_attention_decode_shared_workspace_bytes": (c_int, [c_void_p, c_int, c_int, c_int, c_int,
+                                                              _P(c_size_t)]),
+    "paged_attention_decode_shared": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                              c_float, c_int, c_void_p, c_size_t, c_void_p]),
     "paged_attention_prefill_chunk": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                               c_int, c_float, c_void_p]),
@@ -196,6 +203,27 @@ def paged_attention_decode_multi(pool, layer, out, query, queries_per_seq, block
                                                num_q_heads, max_blocks_per_seq, float(scale),
                                                partition_size, _ptr(workspace), workspace_bytes,
                                                _stream(stream)))
+
+
+def paged_attention_decode_shared_workspace_bytes(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                                                  partition_size=0):
+    out = c_size_t()
+    _check(load().paged_attention_decode_shared_workspace_bytes(pool, num_seqs, num_q_heads,
+                                                                max_blocks_per_seq, partition_size,
+                                                                ctypes.byref(out)))
+    return out.value
+
+
+def paged_attention_decode_shared(pool, layer, out, query, block_tables, context_lens, group_starts,
+                                  prefix_lens, num_seqs, num_groups, max_group_size, num_q_heads,
+                                  max_blocks_per_seq, scale, partition_size=0, workspace=None,
+                                  workspace_bytes=0, stream=None):
+    _check(load().paged_attention_decode_shared(pool, layer, _ptr(out), _ptr(query), _ptr(block_tables),
+                                                _ptr(context_lens), _ptr(group_starts),
+                                                _ptr(prefix_lens), num_seqs, num_groups, max_group_size,
+                                                num_q_heads, max_blocks_per_seq, float(scale),
+                                                partition_size, _ptr(workspace), workspace_bytes,
+                                                _stream(stream)))
 
 
 def paged_attention_prefill_chunk(pool, layer, out, query, cu_q_lens, block_tables,

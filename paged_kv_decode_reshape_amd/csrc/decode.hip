@@ -511,10 +511,12 @@ __device__ __forceinline__ mf_bf16x8 mf_fp8_half(const Vec16& v) {
 }
 
 // MQ: several query rows per sequence (a.nq); otherwise one.
+// qrow0: the query row of column row 0 (b * nq for a sequence's own rows; the
+// first member's row when the columns are sequences sharing a prefix).
 template <typename T, int D, int G, bool MQ>
 __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, MfmaWaveLds<D>& lds, int b, int h,
                                                             int tok_begin, int tok_end, int ctx, int& done,
-                                                            int share) {
+                                                            int share, int qrow0) {
   const int nq = MQ ? a.nq : 1;
   static_assert(sizeof(T) <= 2, "matrix-core segments take bf16 or e4m3 pools");
   static_assert(G <= 16, "the group's heads are the 16 MFMA columns");
@@ -551,7 +553,7 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
   {
     const int hq = a.hkv * G;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.query) +
-                           (((size_t)b * nq + qj) * hq + (size_t)h * G + qg) * D;
+                           (((size_t)qrow0 + qj) * hq + (size_t)h * G + qg) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       const int d0 = kF8 ? 64 * (s / 2) + 16 * quad + 8 * (s % 2) : 32 * s + 8 * quad;
@@ -763,7 +765,8 @@ template <typename T, int D, int G, bool MQ>
 __device__ __forceinline__ auto run_seg(const DecodeArgs& a, SegLds<T, D, G>& lds, int b, int h, int tok_begin,
                                         int tok_end, int ctx, int& done, int share) {
   if constexpr (UsesMfma<T>::value) {
-    return run_segment_mfma<T, D, G, MQ>(a, lds, b, h, tok_begin, tok_end, ctx, done, share);
+    return run_segment_mfma<T, D, G, MQ>(a, lds, b, h, tok_begin, tok_end, ctx, done, share,
+                                         b * (MQ ? a.nq : 1));
   } else {
     return run_segment<T, D, G>(a, lds, b, h, tok_begin, tok_end, ctx, done, share);
   }
@@ -817,16 +820,104 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   }
   const int tok_begin = part * prm.part_tokens;
   if (tok_begin >= ctx) return;
+  // Partitions inside a shared prefix were computed by decode_prefix_kernel.
+  const int shared = prm.shared_parts ? prm.shared_parts[b] : 0;
+  if (part < shared) return;
   const int tok_end = min(ctx, tok_begin + prm.part_tokens);
   int done = 0;
   const auto st = run_seg<T, D, G, MQ>(args, lds[wave], b, h, tok_begin, tok_end, ctx, done, 0);
-  if (ctx <= prm.part_tokens) {
+  if (ctx <= prm.part_tokens && shared == 0) {
     write_rows<T, D, G>(out_row, st, args.v_scale, nq, hq);
   } else {
     write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + qh0 * prm.max_parts + part, prm.max_parts,
                            ws_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st,
                            args.v_scale, nq, hq);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Shared prefixes: sequences whose leading tokens live in the same physical
+// blocks ("The Serving Playbook", "Paged KV cache" and "Sharing is a reference
+// count") read those blocks once for the whole group ("RadixAttention": the
+// shared portion is fetched from HBM once for the batch, not once per
+// sequence). One wavefront per (group, KV head, member tile, partition inside
+// the prefix): its 16 MFMA columns are the G query heads of 16/G members, so
+// each K/V tile is loaded once and multiplied against every member's query.
+// It writes each member's partial summary for that partition in the layout of
+// the fixed-partition split; decode_partition_kernel then skips those
+// partitions and decode_reduce_kernel merges everything.
+// ---------------------------------------------------------------------------
+
+// Members of a group that one wavefront's 16 columns hold.
+__host__ __device__ constexpr int prefix_members_per_wave(int g) { return 16 / g; }
+
+// Largest k with group_starts[k] <= b (group_starts non-decreasing, [0] = 0).
+__device__ __forceinline__ int find_group(const int32_t* __restrict__ gs, int num_groups, int b) {
+  int lo = 0, hi = num_groups;                     // invariant: gs[lo] <= b < gs[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (gs[mid] <= b) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_prefix_kernel(
+    const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
+  __shared__ MfmaWaveLds<D> lds[4];
+  constexpr int MPW = prefix_members_per_wave(G);
+  const int lane = threadIdx.x & 63;
+  // Every sequence learns how many of its leading partitions are shared; the
+  // partition and reduce kernels that follow on the stream read it.
+  for (long b = (long)blockIdx.x * blockDim.x + threadIdx.x; b < prm.num_seqs; b += (long)gridDim.x * blockDim.x) {
+    const int k = find_group(prm.group_starts, prm.num_groups, (int)b);
+    const int plen = min(min(max(prm.prefix_lens[k], 0), max(context_lens[prm.group_starts[k]], 0)),
+                         max(context_lens[b], 0));
+    prm.shared_parts[b] = plen / prm.part_tokens;
+  }
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Unit numbering: member tile fastest, then KV head, group, and partition
+  // (descending, so the long prefixes' late partitions start first). The
+  // member tiles of one (group, head, partition) read the same K/V tiles and
+  // sit in one workgroup, so the second read hits the CU's caches.
+  const long unit = (long)blockIdx.x * 4 + wave;
+  const int mt = (int)(unit % prm.member_tiles);
+  long rest = unit / prm.member_tiles;
+  const int h = (int)(rest % args.hkv);
+  rest /= args.hkv;
+  const int k = (int)(rest % prm.num_groups);
+  const long prev = rest / prm.num_groups;
+  if (prev >= prm.max_parts) return;
+  const int part = prm.max_parts - 1 - (int)prev;
+
+  const int seq0 = prm.group_starts[k];
+  const int members = prm.group_starts[k + 1] - seq0;
+  const int m0 = mt * MPW;
+  if (m0 >= members) return;
+  const int nm = min(MPW, members - m0);
+  // The group's shared partitions: whole partitions inside its prefix and
+  // inside the first member's context, whose table supplies the block ids. A
+  // member with a shorter context recomputes its own partitions past it
+  // (shared_parts above), overwriting these slots later on the stream.
+  const int plen = min(max(prm.prefix_lens[k], 0), max(context_lens[seq0], 0));
+  if (part >= plen / prm.part_tokens) return;
+  const int tok_begin = part * prm.part_tokens;
+  const int tok_end = tok_begin + prm.part_tokens;
+
+  DecodeArgs a = args;
+  a.nq = nm;                   // columns: nm members x G heads
+  int done = 0;
+  // Blocks come from the first member's table (all members hold the same ids
+  // there); with ctx = tok_end + nm no column is masked inside the partition.
+  const MfmaSummary<D> st =
+      run_segment_mfma<T, D, G, true>(a, lds[wave], seq0, h, tok_begin, tok_end, tok_end + nm, done, 0, seq0 + m0);
+  const int hq = args.hkv * G;
+  const size_t qh0 = (size_t)(seq0 + m0) * hq + (size_t)h * G;
+  write_partial<T, D, G>(reinterpret_cast<float2*>(prm.ws_ml) + qh0 * prm.max_parts + part, prm.max_parts,
+                         prm.ws_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st,
+                         args.v_scale, nm, hq);
+  (void)lane;
 }
 
 __device__ __forceinline__ float lane_xor16(float x) { return __shfl_xor(x, 16); }
@@ -877,7 +968,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int b = (int)(pair / rows);
   const int ctx = context_lens[b];
   const int nparts = (ctx + prm.part_tokens - 1) / prm.part_tokens;
-  if (nparts <= 1) return;
+  // A single partition was written out directly unless it came from a shared prefix.
+  if (nparts <= 1 && (prm.shared_parts == nullptr || prm.shared_parts[b] == 0)) return;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + (size_t)pair * prm.max_parts;
   const float4* wo = reinterpret_cast<const float4*>(ws_o) + (size_t)pair * prm.max_parts * kSlices;
 
@@ -1151,13 +1243,24 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
     timer.end(KernelKind::kDecodeReduce, stream);
     return hipGetLastError();
   }
+  if constexpr (UsesMfma<T>::value && !MQ) {
+    if (prm.shared_parts != nullptr) {
+      const long punits = (long)prm.num_kv_heads * prm.member_tiles * prm.num_groups * prm.max_parts;
+      const long pblocks = std::max((punits + 3) / 4, ((long)prm.num_seqs + 255) / 256);
+      timer.begin(KernelKind::kDecodePrefix, stream);
+      hipLaunchKernelGGL((decode_prefix_kernel<T, D, G>), dim3((unsigned)pblocks), dim3(256), 0, stream,
+                         prm.context_lens, args, prm);
+      timer.end(KernelKind::kDecodePrefix, stream);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+  }
   const long units = (long)prm.num_kv_heads * prm.num_seqs * prm.max_parts;
   timer.begin(KernelKind::kDecodePartition, stream);
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ>), dim3((unsigned)((units + 3) / 4)), dim3(256),
                      0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
   timer.end(KernelKind::kDecodePartition, stream);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (prm.max_parts > 1) {
+  if (prm.max_parts > 1 || prm.shared_parts != nullptr) {
     const long pairs = (long)prm.num_seqs * prm.q_per_seq * prm.num_kv_heads * G;
     timer.begin(KernelKind::kDecodeReduce, stream);
     hipLaunchKernelGGL((decode_reduce_kernel<TQ, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256),

@@ -374,9 +374,113 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
   return PKV_OK;
 }
 
+// Shared-prefix decode: fixed partitions (partition_size, or 256 when 0), the
+// summary rows of every (sequence, query head, partition) and one int32 per
+// sequence for the count of its shared partitions.
+constexpr int kSharedDefaultPartition = 256;
+
+pkv_status shared_split(const pkv_pool* pool, int num_seqs, int num_q_heads, int max_blocks_per_seq,
+                        int partition_size, DecodeSplit* sp) {
+  if (partition_size < 0)
+    return fail(PKV_ERR_INVALID_ARG, "partition_size must be >= 0 for shared-prefix decode (got %d)",
+                partition_size);
+  return decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                      partition_size == 0 ? kSharedDefaultPartition : partition_size, sp);
+}
+
+pkv_status shared_workspace(const pkv_pool* pool, int num_seqs, int num_q_heads, int max_blocks_per_seq,
+                            int partition_size, size_t* bytes, size_t* rows_out) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (!bytes) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
+  if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_seqs >= 0, num_q_heads > 0 and max_blocks_per_seq > 0 required");
+  if (num_q_heads % pool->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                num_q_heads, pool->num_kv_heads);
+  DecodeSplit sp;
+  pkv_status st = shared_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
+  if (st != PKV_OK) return st;
+  const size_t rows = (size_t)num_seqs * num_q_heads * sp.max_parts;
+  *bytes = rows == 0 ? 0
+                     : round16(rows * 2 * sizeof(float)) + round16(rows * pool->head_dim * sizeof(float)) +
+                           round16((size_t)num_seqs * sizeof(int32_t));
+  if (rows_out) *rows_out = rows;
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+pkv_status paged_attention_decode_shared_workspace_bytes(const pkv_pool* pool, int num_seqs,
+                                                         int num_q_heads, int max_blocks_per_seq,
+                                                         int partition_size, size_t* bytes) {
+  return shared_workspace(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, bytes, nullptr);
+}
+
+pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* out, const void* query,
+                                         const int32_t* block_tables, const int32_t* context_lens,
+                                         const int32_t* group_starts, const int32_t* prefix_lens,
+                                         int num_seqs, int num_groups, int max_group_size,
+                                         int num_q_heads, int max_blocks_per_seq, float scale,
+                                         int partition_size, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  pkv_status st = check_pool_layer(pool, layer);
+  if (st != PKV_OK) return st;
+  if (pool->dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode runs on the matrix cores: bf16 and e4m3 pools only");
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                num_q_heads, pool->num_kv_heads);
+  const int group = num_q_heads / pool->num_kv_heads;
+  if (group > 8) return fail(PKV_ERR_UNSUPPORTED, "%d query heads per KV head unsupported (1..8)", group);
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  if (num_seqs == 0) return PKV_OK;
+  if (num_groups <= 0 || num_groups > num_seqs)
+    return fail(PKV_ERR_INVALID_ARG, "num_groups must be in [1, num_seqs] (got %d)", num_groups);
+  if (max_group_size <= 0 || max_group_size > num_seqs)
+    return fail(PKV_ERR_INVALID_ARG, "max_group_size must be in [1, num_seqs] (got %d)", max_group_size);
+  if (!out || !query || !block_tables || !context_lens || !group_starts || !prefix_lens)
+    return fail(PKV_ERR_INVALID_ARG,
+                "out, query, block_tables, context_lens, group_starts and prefix_lens must not be NULL");
+  if (!aligned(out, 16) || !aligned(query, 16)) return fail(PKV_ERR_INVALID_ARG, "out/query must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(group_starts, 4) || !aligned(prefix_lens, 4))
+    return fail(PKV_ERR_INVALID_ARG, "block_tables/context_lens/group_starts/prefix_lens must be 4-byte aligned");
+  DecodeSplit sp;
+  st = shared_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
+  if (st != PKV_OK) return st;
+  size_t need = 0, rows = 0;
+  st = shared_workspace(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &need, &rows);
+  if (st != PKV_OK) return st;
+  if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
+  if (!aligned(workspace, 16)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
+  // Members per wavefront: the 16 matrix-core columns hold 16 / G members' heads.
+  const int mpw = kMfmaColumns / group;
+  const long member_tiles = (max_group_size + mpw - 1) / mpw;
+  const long units = (long)pool->num_kv_heads * num_seqs * sp.max_parts;
+  const long punits = (long)pool->num_kv_heads * member_tiles * num_groups * sp.max_parts;
+  if ((units + 3) / 4 >= (1L << 24) || (punits + 3) / 4 >= (1L << 24))
+    return fail(PKV_ERR_UNSUPPORTED, "too many work units in one call");
+  char* ws = static_cast<char*>(workspace);
+  float* ws_ml = reinterpret_cast<float*>(ws);
+  float* ws_o = reinterpret_cast<float*>(ws + round16(rows * 2 * sizeof(float)));
+  int32_t* shared_parts = reinterpret_cast<int32_t*>(ws + round16(rows * 2 * sizeof(float)) +
+                                                     round16(rows * pool->head_dim * sizeof(float)));
+  pkv::DecodeParams prm{out, ws_ml, ws_o, nullptr, query, pool->k_layers[layer], pool->v_layers[layer],
+                        block_tables, context_lens, num_seqs, pool->num_kv_heads, group,
+                        pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
+                        0, scale * 1.4426950408889634f * pool->k_scale[layer],
+                        pool->v_scale[layer], 1, group_starts, prefix_lens, num_groups, (int)member_tiles,
+                        shared_parts};
+  (void)hipGetLastError();
+  hipError_t err = pkv::launch_decode(prm, pool_type(pool->dtype), (hipStream_t)stream, pkv::KernelTimer{});
+  if (err != hipSuccess) return hip_fail(err, "paged_attention_decode_shared launch");
+  return PKV_OK;
+}
 
 pkv_status copy_blocks(const pkv_pool* pool, const int32_t* block_pairs, int num_pairs, void* stream) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");

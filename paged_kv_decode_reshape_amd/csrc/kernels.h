@@ -8,7 +8,7 @@ namespace pkv {
 
 constexpr int kPoolBlockSize = 16;  // tokens per KV block supported by the kernels
 
-enum class KernelKind : int { kAppend = 0, kDecodePartition = 1, kDecodeReduce = 2, kPrefill = 3 };
+enum class KernelKind : int { kAppend = 0, kDecodePartition = 1, kDecodeReduce = 2, kPrefill = 3, kDecodePrefix = 4 };
 
 // Records a pair of HIP events around a launch when kernel timing is enabled
 // (a no-op otherwise). Defined in host.hip.
@@ -54,6 +54,14 @@ struct DecodeParams {
   float scale_log2;        // scale * log2(e), times the K scale of an e4m3 pool
   float v_scale;           // e4m3 pools: the V scale; else 1
   int q_per_seq;           // query rows per sequence, at positions ctx - q_per_seq .. ctx - 1
+  // Shared prefixes (fixed partitions only; all NULL / 0 otherwise). Group k
+  // is sequences [group_starts[k], group_starts[k+1]); its first
+  // prefix_lens[k] tokens sit in the same physical blocks for every member.
+  const int32_t* group_starts;
+  const int32_t* prefix_lens;
+  int num_groups;
+  int member_tiles;        // member tiles per group in the prefix launch (largest group / members per wave)
+  int32_t* shared_parts;   // workspace [num_seqs]: leading partitions of each sequence done by the prefix kernel
 };
 
 struct PrefillParams {

@@ -438,6 +438,100 @@ def custom(name, *, seed, dtype, hq, hkv, d, ctx, q_lens=None, pool_factor=1.25,
                      partition_size=partition_size)
 
 
+def shared_prefix(name, *, seed, dtype, hq, hkv, d, groups, pool_factor=1.25) -> Step:
+    """Decode step whose sequences share prefixes in groups.
+
+    ``groups`` is a list of (prefix_len, [context lengths of the members]).
+    The whole blocks of a group's prefix are allocated once and appear in every
+    member's block table; a partly filled last prefix block is copied into a
+    block of each member's own (the copy-on-write at divergence), holding the
+    same values. Each member's tokens past the prefix are its own, the last
+    one appended this step. Members are consecutive sequences; ``info`` holds
+    ``group_starts`` and ``prefix_lens``. Values of a shared position are
+    drawn once.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bs = BLOCK_SIZE
+    ctx = np.asarray([c for _, members in groups for c in members], dtype=np.int32)
+    starts = np.concatenate([[0], np.cumsum([len(m) for _, m in groups])]).astype(np.int32)
+    plens = np.asarray([p for p, _ in groups], dtype=np.int32)
+    nseq = len(ctx)
+    need = sum(blocks_needed(p, bs) // 1 - (p % bs != 0) for p, _ in groups) + sum(
+        blocks_needed(c, bs) - (p // bs) for p, m in groups for c in m)
+    num_blocks = max(int(math.ceil(pool_factor * need)) + 1, 2)
+    poison = num_blocks - 1
+    order = [int(x) for x in rng.permutation(num_blocks) if x != poison]
+    max_blocks = max(1, blocks_needed(int(ctx.max()) if nseq else 1, bs))
+    tables = np.full((nseq, max_blocks), poison, dtype=np.int32)
+    ck, cv, cslots, nk, nv, nslots = [], [], [], [], [], []
+    pos = 0
+    for k, (plen, members) in enumerate(groups):
+        assert all(c >= plen for c in members), "a member's context must hold the prefix"
+        n_sh = plen // bs                                  # whole shared blocks
+        shared = order[pos:pos + n_sh]
+        pos += n_sh
+        pk, pv = _normal(rng, (plen, hkv, d)), _normal(rng, (plen, hkv, d))
+        s0 = int(starts[k])
+        for i, c in enumerate(members):
+            s = s0 + i
+            own = blocks_needed(c, bs) - n_sh
+            tables[s, :n_sh] = shared
+            tables[s, n_sh:n_sh + own] = order[pos:pos + own]
+            pos += own
+            if c == 0:
+                continue
+            assert c - 1 >= n_sh * bs or len(members) == 1, "the new token must land in an own block"
+            lo = 0 if i == 0 else n_sh * bs                # shared blocks are written by member 0
+            cached = np.arange(lo, c - 1)
+            cslots.append(_slots_for(tables[s], cached, bs))
+            in_prefix = cached[cached < plen]
+            own_pos = cached[cached >= plen]
+            ok, ov = _normal(rng, (len(own_pos), hkv, d)), _normal(rng, (len(own_pos), hkv, d))
+            ck.append(np.concatenate([pk[in_prefix], ok]))
+            cv.append(np.concatenate([pv[in_prefix], ov]))
+            nslots.append(_slots_for(tables[s], np.asarray([c - 1]), bs))
+            if c - 1 < plen:
+                nk.append(pk[c - 1:c])
+                nv.append(pv[c - 1:c])
+            else:
+                nk.append(_normal(rng, (1, hkv, d)))
+                nv.append(_normal(rng, (1, hkv, d)))
+
+    def cat(parts, shape):
+        return np.concatenate(parts) if parts else np.zeros(shape, np.float32)
+
+    dq = _normal(rng, (nseq, hq, d))
+    return Step(
+        name=name, dtype=dtype, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+        block_size=bs, num_blocks=num_blocks, poison_block=poison,
+        context_lens=ctx, block_tables=tables,
+        cached_key=make_values(cat(ck, (0, hkv, d)), dtype),
+        cached_value=make_values(cat(cv, (0, hkv, d)), dtype),
+        cached_slots=np.concatenate(cslots) if cslots else np.zeros(0, np.int64),
+        new_key=make_values(cat(nk, (0, hkv, d)), dtype),
+        new_value=make_values(cat(nv, (0, hkv, d)), dtype),
+        new_slots=np.concatenate(nslots) if nslots else np.zeros(0, np.int64),
+        decode_seqs=np.arange(nseq, dtype=np.int32), decode_query=make_values(dq, dtype),
+        prefill_seqs=np.zeros(0, np.int32), prefill_query=None, cu_q_lens=None,
+        scale=1.0 / math.sqrt(d),
+        info=dict(group_starts=starts, prefix_lens=plens,
+                  shared_tokens=int(sum(p * len(m) for p, m in groups)),
+                  unique_tokens=int(sum(p + sum(c - p for c in m) for p, m in groups))))
+
+
+def parallel_sampling(rep: int = 0, prompts: int = 32, samples: int = 8, prompt_len: int = 2000,
+                      max_new: int = 512) -> Step:
+    """Llama-8B-shaped decode (Hq=32, Hkv=8, D=128, bf16) of ``prompts`` prompts
+    of ``prompt_len`` tokens, each sampled ``samples`` times in parallel: every
+    sample shares its prompt's blocks and has generated a uniform 1..max_new
+    tokens of its own (256 sequences by default)."""
+    rng = _rng(6, rep)
+    groups = [(prompt_len, [prompt_len + int(x) for x in rng.integers(1, max_new, size=samples, endpoint=True)])
+              for _ in range(prompts)]
+    return shared_prefix(f"llama8b_parallel_sampling_{prompts}x{samples}_prompt{prompt_len}",
+                         seed=6000 + rep, dtype="bf16", hq=32, hkv=8, d=128, groups=groups)
+
+
 CONFIGS = {
     1: "tiny_fp32",
     2: "qwen_layer",

@@ -140,6 +140,26 @@ class DevicePool:
                                          nseq, s.num_q_heads, bt.shape[1], s.scale, part, ws, wsb)
         return out
 
+    def decode_shared(self, partition_size: int = 0, groups=None, prefix_lens=None, layer: int = 0):
+        """Decode through paged_attention_decode_shared with the step's sharing
+        groups (``info['group_starts']``, ``info['prefix_lens']``) unless given."""
+        s = self.step
+        bt, cl = s.decode_inputs()
+        gs = s.info["group_starts"] if groups is None else np.asarray(groups, np.int32)
+        pl = s.info["prefix_lens"] if prefix_lens is None else np.asarray(prefix_lens, np.int32)
+        q = to_device(s.decode_query)
+        nseq = len(cl)
+        out = torch.empty((nseq, s.num_q_heads, s.head_dim), dtype=TORCH_DT[s.dtype], device=DEV)
+        wsb = pkv.paged_attention_decode_shared_workspace_bytes(self.handle, nseq, s.num_q_heads,
+                                                                bt.shape[1], partition_size)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+        ng = len(gs) - 1
+        max_group = int(np.max(np.diff(gs))) if ng else 1
+        pkv.paged_attention_decode_shared(self.handle, layer, out, q, int_tensor(bt), int_tensor(cl),
+                                          int_tensor(gs), int_tensor(pl), nseq, ng, max_group,
+                                          s.num_q_heads, bt.shape[1], s.scale, partition_size, ws, wsb)
+        return out
+
     def prefill(self, layer: int = 0):
         s = self.step
         bt, cl = s.prefill_inputs()

@@ -149,3 +149,35 @@ def test_copy_blocks_checks():
         assert _status(pkv.copy_blocks, h, 18, 2)[0] == -1         # misaligned pairs
     finally:
         pkv.kv_pool_destroy(h)
+
+
+def test_shared_prefix_decode_checks():
+    h = pkv.kv_pool_create(1, 4096, 16, 8, 128, pkv.BF16, [256], [512])
+    hf = pkv.kv_pool_create(1, 64, 16, 8, 128, pkv.F32, [256], [512])
+    try:
+        # workspace: summary rows of every (sequence, head, 256-token partition)
+        # plus one int32 per sequence
+        rows = 3 * 32 * 8                                         # 128 blocks = 2048 tokens = 8 partitions
+        want = ((rows * 8 + 15) // 16) * 16 + rows * 128 * 4 + 16
+        assert pkv.paged_attention_decode_shared_workspace_bytes(h, 3, 32, 128, 0) == want
+        assert pkv.paged_attention_decode_shared_workspace_bytes(h, 3, 32, 128, 256) == want
+        assert _status(pkv.paged_attention_decode_shared_workspace_bytes, h, 3, 32, 128, -1)[0] == -1
+        assert _status(pkv.paged_attention_decode_shared_workspace_bytes, h, 3, 32, 128, 100)[0] == -1
+        args = (0, 16, 16, 16, 16, 16, 16)   # layer, out, query, tables, lens, group_starts, prefix_lens
+        # groups and their largest size must be within [1, num_seqs]
+        assert _status(pkv.paged_attention_decode_shared, h, *args, 4, 0, 1, 32, 128, 1.0)[0] == -1
+        assert _status(pkv.paged_attention_decode_shared, h, *args, 4, 5, 1, 32, 128, 1.0)[0] == -1
+        assert _status(pkv.paged_attention_decode_shared, h, *args, 4, 2, 0, 32, 128, 1.0)[0] == -1
+        # the workspace is required
+        assert _status(pkv.paged_attention_decode_shared, h, *args, 4, 2, 2, 32, 128, 1.0)[0] == -4
+        # null group arrays are rejected
+        st, msg = _status(pkv.paged_attention_decode_shared, h, 0, 16, 16, 16, 16, None, 16, 4, 2, 2, 32, 128,
+                          1.0)
+        assert st == -1 and "group_starts" in msg
+        # fp32 pools: the shared products run on the matrix cores
+        st, msg = _status(pkv.paged_attention_decode_shared, hf, *args, 4, 2, 2, 32, 128, 1.0)
+        assert st == -2 and "bf16" in msg
+        pkv.paged_attention_decode_shared(h, *args, 0, 0, 0, 32, 128, 1.0)   # no sequences: no-op
+    finally:
+        pkv.kv_pool_destroy(h)
+        pkv.kv_pool_destroy(hf)
