@@ -223,10 +223,13 @@ pkv_status paged_attention_decode_multi(const pkv_pool* pool, int layer, void* o
  * sequence ("The Serving Playbook", "RadixAttention", "The tree changes what
  * the scheduler should do"). The result is that of paged_attention_decode on
  * the same arguments (within rounding); only the work is organised
- * differently: for each group, the whole partitions of partition_size tokens
- * that lie inside its prefix are read once and multiplied against all
- * members' query heads together on the matrix cores; every member's remaining
- * partitions are read on their own; one reduction merges all partitions.
+ * differently. A group's shared region is its prefix rounded down to whole
+ * 64-token windows; it is cut into pieces of partition_size tokens (the last
+ * one shorter), each read once and multiplied against all members' query
+ * heads together on the matrix cores. Every member's tokens after the shared
+ * region are then read on their own with the balanced split of
+ * paged_attention_decode, and the pieces are merged by the online-softmax
+ * combine.
  *   out, query, block_tables, context_lens, scale: as for
  *     paged_attention_decode (one query row per sequence).
  *   group_starts: int32 [num_groups + 1], device memory. Group k is
@@ -237,14 +240,14 @@ pkv_status paged_attention_decode_multi(const pkv_pool* pool, int layer, void* o
  *   prefix_lens: int32 [num_groups], device memory: group k's first
  *     prefix_lens[k] tokens sit in the same physical blocks, with the same
  *     block-table entries, for every member (caller contract). The blocks are
- *     read through the group's first sequence's table; tokens past that
- *     sequence's context or a member's context are not treated as shared.
- *   partition_size: > 0, a multiple of 64, or 0 for 256 tokens. Tokens of a
- *     prefix past its last whole partition are read per member.
+ *     read through the group's first sequence's table, so the shared region
+ *     never extends past that sequence's context; a member whose context ends
+ *     inside the region uses only the pieces wholly before its context end.
+ *   partition_size: piece size, > 0 and a multiple of 64, or 0 for 512.
  *   workspace: at least paged_attention_decode_shared_workspace_bytes(...)
  *     bytes, 16-byte aligned; contents on entry are ignored.
- * bf16 and e4m3 pools (the shared products run on bf16 MFMA); an fp32 pool
- * gives PKV_ERR_UNSUPPORTED. */
+ * bf16 and e4m3 pools (the shared products run on bf16 MFMA) and at most 4096
+ * sequences; otherwise PKV_ERR_UNSUPPORTED. */
 pkv_status paged_attention_decode_shared_workspace_bytes(const pkv_pool* pool, int num_seqs,
                                                          int num_q_heads, int max_blocks_per_seq,
                                                          int partition_size, size_t* bytes);

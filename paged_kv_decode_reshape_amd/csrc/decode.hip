@@ -820,13 +820,10 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   }
   const int tok_begin = part * prm.part_tokens;
   if (tok_begin >= ctx) return;
-  // Partitions inside a shared prefix were computed by decode_prefix_kernel.
-  const int shared = prm.shared_parts ? prm.shared_parts[b] : 0;
-  if (part < shared) return;
   const int tok_end = min(ctx, tok_begin + prm.part_tokens);
   int done = 0;
   const auto st = run_seg<T, D, G, MQ>(args, lds[wave], b, h, tok_begin, tok_end, ctx, done, 0);
-  if (ctx <= prm.part_tokens && shared == 0) {
+  if (ctx <= prm.part_tokens) {
     write_rows<T, D, G>(out_row, st, args.v_scale, nq, hq);
   } else {
     write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + qh0 * prm.max_parts + part, prm.max_parts,
@@ -861,26 +858,35 @@ __device__ __forceinline__ int find_group(const int32_t* __restrict__ gs, int nu
   return lo;
 }
 
+// Shared region of group k: its prefix, limited to the first member's context
+// (whose table supplies the block ids), rounded down to whole 64-token windows.
+__device__ __forceinline__ int group_shared_tokens(const int32_t* __restrict__ context_lens,
+                                                   const DecodeParams& prm, int k) {
+  const int plen = min(max(prm.prefix_lens[k], 0), max(context_lens[prm.group_starts[k]], 0));
+  return plen / 64 * 64;
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_prefix_kernel(
     const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
   __shared__ MfmaWaveLds<D> lds[4];
   constexpr int MPW = prefix_members_per_wave(G);
-  const int lane = threadIdx.x & 63;
-  // Every sequence learns how many of its leading partitions are shared; the
-  // partition and reduce kernels that follow on the stream read it.
+  const int P = prm.part_tokens;
+  // Every sequence records where its own reading starts; the kernels after
+  // this one on the stream read it. A member whose context ends inside the
+  // group's shared region keeps only the pieces wholly before its context.
   for (long b = (long)blockIdx.x * blockDim.x + threadIdx.x; b < prm.num_seqs; b += (long)gridDim.x * blockDim.x) {
     const int k = find_group(prm.group_starts, prm.num_groups, (int)b);
-    const int plen = min(min(max(prm.prefix_lens[k], 0), max(context_lens[prm.group_starts[k]], 0)),
-                         max(context_lens[b], 0));
-    prm.shared_parts[b] = plen / prm.part_tokens;
+    const int sk = group_shared_tokens(context_lens, prm, k);
+    const int ctx = max(context_lens[b], 0);
+    prm.shared_start[b] = ctx >= sk ? sk : ctx / P * P;
   }
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Unit numbering: member tile fastest, then KV head, group, and partition
-  // (descending, so the long prefixes' late partitions start first). The
-  // member tiles of one (group, head, partition) read the same K/V tiles and
-  // sit in one workgroup, so the second read hits the CU's caches.
+  // Unit numbering: member tile fastest, then KV head, group, and piece
+  // (descending, so the long prefixes' late pieces start first). The member
+  // tiles of one (group, head, piece) read the same K/V tiles and sit in one
+  // workgroup, so the second read hits the CU's caches.
   const long unit = (long)blockIdx.x * 4 + wave;
   const int mt = (int)(unit % prm.member_tiles);
   long rest = unit / prm.member_tiles;
@@ -896,28 +902,23 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   const int m0 = mt * MPW;
   if (m0 >= members) return;
   const int nm = min(MPW, members - m0);
-  // The group's shared partitions: whole partitions inside its prefix and
-  // inside the first member's context, whose table supplies the block ids. A
-  // member with a shorter context recomputes its own partitions past it
-  // (shared_parts above), overwriting these slots later on the stream.
-  const int plen = min(max(prm.prefix_lens[k], 0), max(context_lens[seq0], 0));
-  if (part >= plen / prm.part_tokens) return;
-  const int tok_begin = part * prm.part_tokens;
-  const int tok_end = tok_begin + prm.part_tokens;
+  const int sk = group_shared_tokens(context_lens, prm, k);
+  const int tok_begin = part * P;
+  if (tok_begin >= sk) return;
+  const int tok_end = min(sk, tok_begin + P);
 
   DecodeArgs a = args;
   a.nq = nm;                   // columns: nm members x G heads
   int done = 0;
   // Blocks come from the first member's table (all members hold the same ids
-  // there); with ctx = tok_end + nm no column is masked inside the partition.
+  // there); with ctx = tok_end + nm no column is masked inside the piece.
   const MfmaSummary<D> st =
       run_segment_mfma<T, D, G, true>(a, lds[wave], seq0, h, tok_begin, tok_end, tok_end + nm, done, 0, seq0 + m0);
   const int hq = args.hkv * G;
   const size_t qh0 = (size_t)(seq0 + m0) * hq + (size_t)h * G;
-  write_partial<T, D, G>(reinterpret_cast<float2*>(prm.ws_ml) + qh0 * prm.max_parts + part, prm.max_parts,
-                         prm.ws_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st,
+  write_partial<T, D, G>(reinterpret_cast<float2*>(prm.pre_ml) + qh0 * prm.max_parts + part, prm.max_parts,
+                         prm.pre_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st,
                          args.v_scale, nm, hq);
-  (void)lane;
 }
 
 __device__ __forceinline__ float lane_xor16(float x) { return __shfl_xor(x, 16); }
@@ -968,8 +969,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int b = (int)(pair / rows);
   const int ctx = context_lens[b];
   const int nparts = (ctx + prm.part_tokens - 1) / prm.part_tokens;
-  // A single partition was written out directly unless it came from a shared prefix.
-  if (nparts <= 1 && (prm.shared_parts == nullptr || prm.shared_parts[b] == 0)) return;
+  if (nparts <= 1) return;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + (size_t)pair * prm.max_parts;
   const float4* wo = reinterpret_cast<const float4*>(ws_o) + (size_t)pair * prm.max_parts * kSlices;
 
@@ -1008,14 +1008,23 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
 // Exclusive prefix sum over sequences of their window counts times hkv, in
 // LDS: cum[b] = first global window of sequence b, cum[B] = total windows.
 // All 256 threads of the workgroup must call it. Returns the total.
+// With shared prefixes (start non-NULL) a sequence's windows begin at its
+// token start[b].
+__device__ __forceinline__ int own_tokens(const int32_t* __restrict__ context_lens,
+                                          const int32_t* __restrict__ start, int b) {
+  const int ctx = max(context_lens[b], 0);
+  return start ? ctx - start[b] : ctx;
+}
+
 __device__ __forceinline__ int window_prefix_sum(const int32_t* __restrict__ context_lens,
+                                                 const int32_t* __restrict__ start,
                                                  int num_seqs, int hkv, int* cum, int* scratch) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int per = (num_seqs + 255) / 256;
   const int lo = min(num_seqs, t * per), hi = min(num_seqs, lo + per);
   int sum = 0;
-  for (int b = lo; b < hi; ++b) sum += (max(context_lens[b], 0) + 63) / 64 * hkv;
+  for (int b = lo; b < hi; ++b) sum += (own_tokens(context_lens, start, b) + 63) / 64 * hkv;
   // Inclusive scan inside the wavefront, then across the 4 wavefronts.
   int inc = sum;
 #pragma unroll
@@ -1029,7 +1038,7 @@ __device__ __forceinline__ int window_prefix_sum(const int32_t* __restrict__ con
   for (int w = 0; w < wave; ++w) run += scratch[w];
   for (int b = lo; b < hi; ++b) {
     cum[b] = run;
-    run += (max(context_lens[b], 0) + 63) / 64 * hkv;
+    run += (own_tokens(context_lens, start, b) + 63) / 64 * hkv;
   }
   if (t == 255) cum[num_seqs] = run;
   __syncthreads();
@@ -1063,23 +1072,89 @@ struct alignas(16) SlotDesc {
   int pad[2];
 };
 
-template <typename T, int D, int G, bool MQ>
+// A row finished by one wave, merged with its shared partitions and written:
+// lane (quad, col < G) holds head col of the group, d = 16n + 4*quad .. +4.
+template <typename T, int D, int G>
+__device__ __forceinline__ void write_rows_shared(typename IoType<T>::type* out_row, const MfmaSummary<D>& st,
+                                                  float v_scale, const float* pre_ml, const float* pre_o,
+                                                  size_t qh0, int max_parts, int nsh) {
+  const int lane = threadIdx.x & 63;
+  const int quad = lane >> 4, col = lane & 15;
+  if (col >= G) return;
+  constexpr int NT = D / 16;
+  float m = st.m, l = st.l;
+  float4 acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+    acc[n] = make_float4(st.o[n][0] * v_scale, st.o[n][1] * v_scale, st.o[n][2] * v_scale, st.o[n][3] * v_scale);
+  const size_t row = (qh0 + col) * max_parts;
+  const float2* ml = reinterpret_cast<const float2*>(pre_ml) + row;
+  const float* ob = pre_o + row * D + 4 * quad;
+#pragma unroll 2
+  for (int p = 0; p < nsh; ++p) {
+    const float2 sm = ml[p];
+    const float mn = fmaxf(m, sm.x);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float a = fast_exp2(m - ms), w = fast_exp2(sm.x - ms);
+    m = mn;
+    l = l * a + sm.y * w;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const float4 v = *reinterpret_cast<const float4*>(ob + (size_t)p * D + 16 * n);
+      acc[n] = make_float4(acc[n].x * a + v.x * w, acc[n].y * a + v.y * w, acc[n].z * a + v.z * w,
+                           acc[n].w * a + v.w * w);
+    }
+  }
+  const float inv = 1.0f / l;
+  uint16_t* orow = reinterpret_cast<uint16_t*>(out_row) + (size_t)col * D;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    *reinterpret_cast<uint2*>(orow + 16 * n + 4 * quad) =
+        make_uint2(f32_to_bf16_bits(acc[n].x * inv) | (f32_to_bf16_bits(acc[n].y * inv) << 16),
+                   f32_to_bf16_bits(acc[n].z * inv) | (f32_to_bf16_bits(acc[n].w * inv) << 16));
+  }
+}
+
+// SH: the rows start after their shared partitions (decode_prefix_kernel has
+// run), and every row is merged with those partitions' summaries.
+template <typename T, int D, int G, bool MQ, bool SH>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_balanced_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     SlotDesc* __restrict__ ws_desc, const int32_t* __restrict__ context_lens, DecodeArgs args,
     DecodeParams prm) {
+  static_assert(!SH || (!MQ && UsesMfma<T>::value), "shared prefixes: one query row, matrix-core segments");
   __shared__ SegLds<T, D, G> lds[4];
   __shared__ int cum[kMaxBalancedSeqs + 1];
   __shared__ int scan_scratch[256];
   const int nq = MQ ? args.nq : 1;   // query rows per sequence
-  const int total = window_prefix_sum(context_lens, prm.num_seqs, args.hkv, cum, scan_scratch);
+  const int total = window_prefix_sum(context_lens, SH ? prm.shared_start : nullptr, prm.num_seqs, args.hkv, cum,
+                                      scan_scratch);
 
   // Defined result for empty contexts: zero rows, spread over the workgroups.
+  // With shared prefixes a row with no tokens of its own is its shared
+  // partitions' combination.
   using TQ = typename IoType<T>::type;
   constexpr int EPV = ElemTraits<TQ>::kPerVec;
   const size_t seq_vecs = (size_t)nq * args.hkv * G * D / EPV;
   for (int b = blockIdx.x; b < prm.num_seqs; b += gridDim.x) {
     if (cum[b + 1] != cum[b]) continue;
+    if constexpr (SH) {
+      const int nsh = (prm.shared_start[b] + prm.part_tokens - 1) / prm.part_tokens;
+      if (nsh > 0) {
+        const int hq = args.hkv * G;
+        for (int i = threadIdx.x; i < hq * (D / 4); i += blockDim.x) {
+          const size_t qh = (size_t)b * hq + i / (D / 4);
+          const float2* ml = reinterpret_cast<const float2*>(prm.pre_ml) + qh * prm.max_parts;
+          const float4* o4 = reinterpret_cast<const float4*>(prm.pre_o + qh * prm.max_parts * D) + i % (D / 4);
+          float m = -INFINITY, l = 0.f;
+          float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+          for (int p = 0; p < nsh; ++p) merge_state(m, l, acc, ml[p].x, ml[p].y, o4[(size_t)p * (D / 4)]);
+          store_row4<TQ>(out_ptr + qh * D + (size_t)(i % (D / 4)) * 4, acc, 1.0f / l);
+        }
+        continue;
+      }
+    }
     TQ* o = out_ptr + (size_t)b * seq_vecs * EPV;
     for (size_t i = threadIdx.x; i < seq_vecs; i += blockDim.x) st16(o + i * EPV, zero16());
   }
@@ -1103,16 +1178,28 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
     // Locate (b, h, first window) of x and run to the end of that (b, h) or of the share.
     const int b = find_seq(cum, prm.num_seqs, x);
     const int ctx = context_lens[b];
-    const int nwb = (ctx + 63) / 64;
+    const int t0 = SH ? prm.shared_start[b] : 0;    // the row's own tokens start here
+    const int nsh = SH ? (t0 + prm.part_tokens - 1) / prm.part_tokens : 0;   // shared pieces before them
+    const int nwb = (ctx - t0 + 63) / 64;
     const int r = x - cum[b];
     const int h = r / nwb;
     const int w0 = r % nwb;
     const int w1 = min(nwb, w0 + (x1 - x));
-    const auto st = run_seg<T, D, G, MQ>(args, lds[wave], b, h, w0 * 64, min(ctx, w1 * 64), ctx, done, x1 - x0);
+    const auto st =
+        run_seg<T, D, G, MQ>(args, lds[wave], b, h, t0 + w0 * 64, min(ctx, t0 + w1 * 64), ctx, done, x1 - x0);
     const int hq = args.hkv * G;
     const size_t qh0 = (size_t)b * nq * hq + (size_t)h * G;
     if (w0 == 0 && w1 == nwb) {
-      write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, nq, hq);
+      if constexpr (SH) {
+        if (nsh > 0) {
+          write_rows_shared<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, prm.pre_ml, prm.pre_o, qh0,
+                                     prm.max_parts, nsh);
+        } else {
+          write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, nq, hq);
+        }
+      } else {
+        write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, nq, hq);
+      }
     } else {
       // Slot 0 holds the share's first segment, slot 1 its last one.
       const int slot = (x == x0) ? 0 : 1;
@@ -1212,6 +1299,23 @@ __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
       }
     }
     const int b = d.row / prm.num_kv_heads, h = d.row % prm.num_kv_heads;
+    if (prm.shared_start != nullptr) {
+      // Shared prefixes (one query row): the row's shared partitions, summaries
+      // in the fixed-partition layout with o already times the V scale.
+      const int nsh = (prm.shared_start[b] + prm.part_tokens - 1) / prm.part_tokens;
+      const size_t qh0 = (size_t)b * prm.num_kv_heads * G + (size_t)h * G;
+#pragma unroll 2
+      for (int p = 0; p < nsh; ++p) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const int f = min(lane + kWave * j, kSlices - 1);
+          const size_t qh = qh0 + f / (D / 4);
+          const float2 sm = reinterpret_cast<const float2*>(prm.pre_ml)[qh * prm.max_parts + p];
+          const float4 ov = reinterpret_cast<const float4*>(prm.pre_o + (qh * prm.max_parts + p) * D)[f % (D / 4)];
+          merge_state(m[j], l[j], acc[j], sm.x, sm.y, ov);
+        }
+      }
+    }
     T* out = out_ptr + (((size_t)b * nq + qr) * prm.num_kv_heads * G + (size_t)h * G) * D;
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
@@ -1229,22 +1333,11 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
                         prm.max_blocks, prm.scale_log2, prm.v_scale, prm.q_per_seq};
   TQ* out = static_cast<TQ*>(prm.out);
   hipError_t err;
-  if (prm.num_waves > 0) {
-    timer.begin(KernelKind::kDecodePartition, stream);
-    SlotDesc* desc = static_cast<SlotDesc*>(prm.ws_desc);
-    hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ>), dim3((unsigned)((prm.num_waves + 3) / 4)),
-                       dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
-    timer.end(KernelKind::kDecodePartition, stream);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    timer.begin(KernelKind::kDecodeReduce, stream);
-    hipLaunchKernelGGL((decode_balanced_reduce_kernel<TQ, D, G>),
-                       dim3((unsigned)((prm.num_waves + 3) / 4), (unsigned)prm.q_per_seq), dim3(256), 0, stream,
-                       out, prm.ws_ml, prm.ws_o, desc, prm);
-    timer.end(KernelKind::kDecodeReduce, stream);
-    return hipGetLastError();
-  }
-  if constexpr (UsesMfma<T>::value && !MQ) {
-    if (prm.shared_parts != nullptr) {
+  // Shared prefixes: the groups' shared partitions first (they also record
+  // each sequence's count of shared partitions for the kernels after them).
+  constexpr bool kShareable = UsesMfma<T>::value && !MQ;
+  if constexpr (kShareable) {
+    if (prm.shared_start != nullptr) {
       const long punits = (long)prm.num_kv_heads * prm.member_tiles * prm.num_groups * prm.max_parts;
       const long pblocks = std::max((punits + 3) / 4, ((long)prm.num_seqs + 255) / 256);
       timer.begin(KernelKind::kDecodePrefix, stream);
@@ -1254,13 +1347,38 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
+  if (prm.num_waves > 0) {
+    timer.begin(KernelKind::kDecodePartition, stream);
+    SlotDesc* desc = static_cast<SlotDesc*>(prm.ws_desc);
+    const dim3 grid((unsigned)((prm.num_waves + 3) / 4));
+    if constexpr (kShareable) {
+      if (prm.shared_start != nullptr) {
+        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, true>), grid, dim3(256), 0, stream, out,
+                           prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
+      } else {
+        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false>), grid, dim3(256), 0, stream, out,
+                           prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
+      }
+    } else {
+      hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false>), grid, dim3(256), 0, stream, out,
+                         prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
+    }
+    timer.end(KernelKind::kDecodePartition, stream);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    timer.begin(KernelKind::kDecodeReduce, stream);
+    hipLaunchKernelGGL((decode_balanced_reduce_kernel<TQ, D, G>),
+                       dim3((unsigned)((prm.num_waves + 3) / 4), (unsigned)prm.q_per_seq), dim3(256), 0, stream,
+                       out, prm.ws_ml, prm.ws_o, desc, prm);
+    timer.end(KernelKind::kDecodeReduce, stream);
+    return hipGetLastError();
+  }
   const long units = (long)prm.num_kv_heads * prm.num_seqs * prm.max_parts;
   timer.begin(KernelKind::kDecodePartition, stream);
   hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ>), dim3((unsigned)((units + 3) / 4)), dim3(256),
                      0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
   timer.end(KernelKind::kDecodePartition, stream);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (prm.max_parts > 1 || prm.shared_parts != nullptr) {
+  if (prm.max_parts > 1) {
     const long pairs = (long)prm.num_seqs * prm.q_per_seq * prm.num_kv_heads * G;
     timer.begin(KernelKind::kDecodeReduce, stream);
     hipLaunchKernelGGL((decode_reduce_kernel<TQ, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256),
@@ -1287,7 +1405,7 @@ int balanced_waves_per_cu() {
   static int cached = 0;
   if (cached == 0) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ, false>, 256, 0) !=
             hipSuccess ||
         blocks <= 0) {
       (void)hipGetLastError();

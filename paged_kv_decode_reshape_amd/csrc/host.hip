@@ -374,37 +374,55 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
   return PKV_OK;
 }
 
-// Shared-prefix decode: fixed partitions (partition_size, or 256 when 0), the
-// summary rows of every (sequence, query head, partition) and one int32 per
-// sequence for the count of its shared partitions.
-constexpr int kSharedDefaultPartition = 256;
+// Shared-prefix decode. A group's shared region (its prefix rounded down to
+// 64-token windows) is cut into pieces of partition_size tokens (512 when 0),
+// the last one shorter; their summaries use the fixed-partition layout (one
+// row per sequence, query head and piece). Each sequence's own tokens are then
+// split like plain decode, balanced over the resident waves (at most 4096
+// sequences), with that split's slots and descriptors after the shared
+// summaries. One int32 per sequence holds where its own tokens start.
+constexpr int kSharedDefaultPartition = 512;
 
-pkv_status shared_split(const pkv_pool* pool, int num_seqs, int num_q_heads, int max_blocks_per_seq,
-                        int partition_size, DecodeSplit* sp) {
-  if (partition_size < 0)
-    return fail(PKV_ERR_INVALID_ARG, "partition_size must be >= 0 for shared-prefix decode (got %d)",
-                partition_size);
-  return decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq,
-                      partition_size == 0 ? kSharedDefaultPartition : partition_size, sp);
-}
+struct SharedLayout {
+  DecodeSplit fixed;       // partitions of the shared prefixes (and of the fallback)
+  DecodeSplit own;         // split of the own tokens
+  size_t pre_rows = 0;
+  size_t own_rows = 0;     // balanced slots' summary rows
+  size_t off_pre_o = 0, off_parts = 0, off_ml = 0, off_o = 0, off_desc = 0, bytes = 0;
+};
 
-pkv_status shared_workspace(const pkv_pool* pool, int num_seqs, int num_q_heads, int max_blocks_per_seq,
-                            int partition_size, size_t* bytes, size_t* rows_out) {
+pkv_status shared_layout(const pkv_pool* pool, int num_seqs, int num_q_heads, int max_blocks_per_seq,
+                         int partition_size, SharedLayout* lay) {
   if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
-  if (!bytes) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
   if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
     return fail(PKV_ERR_INVALID_ARG, "num_seqs >= 0, num_q_heads > 0 and max_blocks_per_seq > 0 required");
   if (num_q_heads % pool->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
                 num_q_heads, pool->num_kv_heads);
-  DecodeSplit sp;
-  pkv_status st = shared_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
+  if (partition_size < 0)
+    return fail(PKV_ERR_INVALID_ARG, "partition_size must be >= 0 for shared-prefix decode (got %d)",
+                partition_size);
+  *lay = SharedLayout{};
+  pkv_status st = decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq,
+                               partition_size == 0 ? kSharedDefaultPartition : partition_size, &lay->fixed);
   if (st != PKV_OK) return st;
-  const size_t rows = (size_t)num_seqs * num_q_heads * sp.max_parts;
-  *bytes = rows == 0 ? 0
-                     : round16(rows * 2 * sizeof(float)) + round16(rows * pool->head_dim * sizeof(float)) +
-                           round16((size_t)num_seqs * sizeof(int32_t));
-  if (rows_out) *rows_out = rows;
+  st = decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, 0, &lay->own);
+  if (st != PKV_OK) return st;
+  if (!lay->own.balanced)
+    return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode takes at most %d sequences (got %d)",
+                pkv::decode_balanced_max_seqs(), num_seqs);
+  const int group = num_q_heads / pool->num_kv_heads;
+  const size_t d = pool->head_dim;
+  lay->pre_rows = (size_t)num_seqs * num_q_heads * lay->fixed.max_parts;
+  lay->own_rows = lay->own.balanced ? decode_summary_rows(lay->own, num_seqs, num_q_heads, group) : 0;
+  if (num_seqs == 0) return PKV_OK;
+  lay->off_pre_o = round16(lay->pre_rows * 2 * sizeof(float));
+  lay->off_parts = lay->off_pre_o + round16(lay->pre_rows * d * sizeof(float));
+  lay->off_ml = lay->off_parts + round16((size_t)num_seqs * sizeof(int32_t));
+  lay->off_o = lay->off_ml + round16(lay->own_rows * 2 * sizeof(float));
+  lay->off_desc = lay->off_o + round16(lay->own_rows * d * sizeof(float));
+  lay->bytes = lay->off_desc +
+               (lay->own.balanced ? (size_t)lay->own.wave_cap * 2 * pkv::decode_balanced_desc_bytes() : 0);
   return PKV_OK;
 }
 
@@ -415,7 +433,12 @@ extern "C" {
 pkv_status paged_attention_decode_shared_workspace_bytes(const pkv_pool* pool, int num_seqs,
                                                          int num_q_heads, int max_blocks_per_seq,
                                                          int partition_size, size_t* bytes) {
-  return shared_workspace(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, bytes, nullptr);
+  if (!bytes) return fail(PKV_ERR_INVALID_ARG, "bytes is NULL");
+  SharedLayout lay;
+  pkv_status st = shared_layout(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &lay);
+  if (st != PKV_OK) return st;
+  *bytes = lay.bytes;
+  return PKV_OK;
 }
 
 pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* out, const void* query,
@@ -448,16 +471,15 @@ pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* 
   if (!aligned(out, 16) || !aligned(query, 16)) return fail(PKV_ERR_INVALID_ARG, "out/query must be 16-byte aligned");
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(group_starts, 4) || !aligned(prefix_lens, 4))
     return fail(PKV_ERR_INVALID_ARG, "block_tables/context_lens/group_starts/prefix_lens must be 4-byte aligned");
-  DecodeSplit sp;
-  st = shared_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
+  SharedLayout lay;
+  st = shared_layout(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &lay);
   if (st != PKV_OK) return st;
-  size_t need = 0, rows = 0;
-  st = shared_workspace(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &need, &rows);
-  if (st != PKV_OK) return st;
+  const size_t need = lay.bytes;
   if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes required, got NULL", need);
   if (!aligned(workspace, 16)) return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
+  const DecodeSplit& sp = lay.fixed;
   // Members per wavefront: the 16 matrix-core columns hold 16 / G members' heads.
   const int mpw = kMfmaColumns / group;
   const long member_tiles = (max_group_size + mpw - 1) / mpw;
@@ -465,19 +487,30 @@ pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* 
   const long punits = (long)pool->num_kv_heads * member_tiles * num_groups * sp.max_parts;
   if ((units + 3) / 4 >= (1L << 24) || (punits + 3) / 4 >= (1L << 24))
     return fail(PKV_ERR_UNSUPPORTED, "too many work units in one call");
+  const pkv::PoolType type = pool_type(pool->dtype);
   char* ws = static_cast<char*>(workspace);
-  float* ws_ml = reinterpret_cast<float*>(ws);
-  float* ws_o = reinterpret_cast<float*>(ws + round16(rows * 2 * sizeof(float)));
-  int32_t* shared_parts = reinterpret_cast<int32_t*>(ws + round16(rows * 2 * sizeof(float)) +
-                                                     round16(rows * pool->head_dim * sizeof(float)));
-  pkv::DecodeParams prm{out, ws_ml, ws_o, nullptr, query, pool->k_layers[layer], pool->v_layers[layer],
+  float* pre_ml = reinterpret_cast<float*>(ws);
+  float* pre_o = reinterpret_cast<float*>(ws + lay.off_pre_o);
+  int32_t* shared_start = reinterpret_cast<int32_t*>(ws + lay.off_parts);
+  float* ws_ml = pre_ml;
+  float* ws_o = pre_o;
+  void* ws_desc = nullptr;
+  int num_waves = 0;
+  if (lay.own.balanced) {
+    ws_ml = reinterpret_cast<float*>(ws + lay.off_ml);
+    ws_o = reinterpret_cast<float*>(ws + lay.off_o);
+    ws_desc = ws + lay.off_desc;
+    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, group, false);
+    num_waves = (int)std::max(1L, std::min(lay.own.wave_cap, slots));
+  }
+  pkv::DecodeParams prm{out, ws_ml, ws_o, ws_desc, query, pool->k_layers[layer], pool->v_layers[layer],
                         block_tables, context_lens, num_seqs, pool->num_kv_heads, group,
                         pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
-                        0, scale * 1.4426950408889634f * pool->k_scale[layer],
+                        num_waves, scale * 1.4426950408889634f * pool->k_scale[layer],
                         pool->v_scale[layer], 1, group_starts, prefix_lens, num_groups, (int)member_tiles,
-                        shared_parts};
+                        shared_start, pre_ml, pre_o};
   (void)hipGetLastError();
-  hipError_t err = pkv::launch_decode(prm, pool_type(pool->dtype), (hipStream_t)stream, pkv::KernelTimer{});
+  hipError_t err = pkv::launch_decode(prm, type, (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "paged_attention_decode_shared launch");
   return PKV_OK;
 }

@@ -54,14 +54,19 @@ struct DecodeParams {
   float scale_log2;        // scale * log2(e), times the K scale of an e4m3 pool
   float v_scale;           // e4m3 pools: the V scale; else 1
   int q_per_seq;           // query rows per sequence, at positions ctx - q_per_seq .. ctx - 1
-  // Shared prefixes (fixed partitions only; all NULL / 0 otherwise). Group k
-  // is sequences [group_starts[k], group_starts[k+1]); its first
-  // prefix_lens[k] tokens sit in the same physical blocks for every member.
+  // Shared prefixes (balanced split; all NULL / 0 otherwise). Group k is
+  // sequences [group_starts[k], group_starts[k+1]); its first prefix_lens[k]
+  // tokens sit in the same physical blocks for every member. The group's
+  // shared region (its prefix rounded down to 64 tokens) is cut into pieces
+  // of part_tokens tokens, the last one shorter, computed once for all members.
   const int32_t* group_starts;
   const int32_t* prefix_lens;
   int num_groups;
   int member_tiles;        // member tiles per group in the prefix launch (largest group / members per wave)
-  int32_t* shared_parts;   // workspace [num_seqs]: leading partitions of each sequence done by the prefix kernel
+  int32_t* shared_start;   // workspace [num_seqs]: first token a sequence reads on its own (a multiple of
+                           // 64); its ceil(shared_start / part_tokens) pieces before it are shared
+  float* pre_ml;           // shared pieces' summaries: float2 [num_seqs][Hq][max_parts]
+  float* pre_o;            // float [num_seqs][Hq][max_parts][D], unnormalized, times the V scale
 };
 
 struct PrefillParams {

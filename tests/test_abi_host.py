@@ -155,12 +155,17 @@ def test_shared_prefix_decode_checks():
     h = pkv.kv_pool_create(1, 4096, 16, 8, 128, pkv.BF16, [256], [512])
     hf = pkv.kv_pool_create(1, 64, 16, 8, 128, pkv.F32, [256], [512])
     try:
-        # workspace: summary rows of every (sequence, head, 256-token partition)
-        # plus one int32 per sequence
-        rows = 3 * 32 * 8                                         # 128 blocks = 2048 tokens = 8 partitions
-        want = ((rows * 8 + 15) // 16) * 16 + rows * 128 * 4 + 16
+        # workspace: summaries of every (sequence, head, 512-token piece),
+        # one int32 per sequence, then the balanced split's slots (two per
+        # wave, G heads each) and descriptors; at most one wave per window
+        rows = 3 * 32 * 4                                         # 128 blocks = 2048 tokens = 4 pieces
+        waves = 3 * 8 * 2048 // 64
+        r16 = lambda x: (x + 15) // 16 * 16
+        want = (r16(rows * 8) + rows * 128 * 4 + 16 + r16(waves * 2 * 4 * 8) + waves * 2 * 4 * 128 * 4 +
+                waves * 2 * 32)
         assert pkv.paged_attention_decode_shared_workspace_bytes(h, 3, 32, 128, 0) == want
-        assert pkv.paged_attention_decode_shared_workspace_bytes(h, 3, 32, 128, 256) == want
+        assert pkv.paged_attention_decode_shared_workspace_bytes(h, 3, 32, 128, 512) == want
+        assert pkv.paged_attention_decode_shared_workspace_bytes(h, 3, 32, 128, 256) > want
         assert _status(pkv.paged_attention_decode_shared_workspace_bytes, h, 3, 32, 128, -1)[0] == -1
         assert _status(pkv.paged_attention_decode_shared_workspace_bytes, h, 3, 32, 128, 100)[0] == -1
         args = (0, 16, 16, 16, 16, 16, 16)   # layer, out, query, tables, lens, group_starts, prefix_lens
