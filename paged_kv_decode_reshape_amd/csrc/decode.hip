@@ -513,7 +513,9 @@ __device__ __forceinline__ mf_bf16x8 mf_fp8_half(const Vec16& v) {
 // MQ: several query rows per sequence (a.nq); otherwise one.
 // qrow0: the query row of column row 0 (b * nq for a sequence's own rows; the
 // first member's row when the columns are sequences sharing a prefix).
-template <typename T, int D, int G, bool MQ>
+// kStream: K/V loads carry the nontemporal hint (the cache is read once per
+// step); off when other wavefronts of the workgroup read the same tiles.
+template <typename T, int D, int G, bool MQ, bool kStream = true>
 __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, MfmaWaveLds<D>& lds, int b, int h,
                                                             int tok_begin, int tok_end, int ctx, int& done,
                                                             int share, int qrow0) {
@@ -594,7 +596,10 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
     for (int r = 0; r < 4; ++r) {
       const char* kt = kbase + (size_t)bid[r] * blk_bytes;
 #pragma unroll
-      for (int j = 0; j < KL; ++j) kr[r][j] = ld16_stream(kt + j * (4 * kBlockSize * 16) + k_lane);
+      for (int j = 0; j < KL; ++j) {
+        const char* pk = kt + j * (4 * kBlockSize * 16) + k_lane;
+        kr[r][j] = kStream ? ld16_stream(pk) : ld16(pk);
+      }
     }
     Vec16 vr[2][VLD];
 #pragma unroll
@@ -603,7 +608,8 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
       for (int u = 0; u < VLD; ++u) {
         const int row0 = u * RPI;                       // first row of the instruction in the half
         const char* vt = vbase + (size_t)bid[2 * kk + row0 / kBlockSize] * blk_bytes;
-        vr[kk][u] = ld16_stream(vt + (row0 % kBlockSize) * D * (int)sizeof(T) + v_lane);
+        const char* pv = vt + (row0 % kBlockSize) * D * (int)sizeof(T) + v_lane;
+        vr[kk][u] = kStream ? ld16_stream(pv) : ld16(pv);
       }
     }
 
@@ -913,7 +919,8 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   // Blocks come from the first member's table (all members hold the same ids
   // there); with ctx = tok_end + nm no column is masked inside the piece.
   const MfmaSummary<D> st =
-      run_segment_mfma<T, D, G, true>(a, lds[wave], seq0, h, tok_begin, tok_end, tok_end + nm, done, 0, seq0 + m0);
+      run_segment_mfma<T, D, G, true, false>(a, lds[wave], seq0, h, tok_begin, tok_end, tok_end + nm, done, 0,
+                                             seq0 + m0);
   const int hq = args.hkv * G;
   const size_t qh0 = (size_t)(seq0 + m0) * hq + (size_t)h * G;
   write_partial<T, D, G>(reinterpret_cast<float2*>(prm.pre_ml) + qh0 * prm.max_parts + part, prm.max_parts,
