@@ -9,7 +9,8 @@ pool (one library "layer" each, >= 2 GiB in total) so the 256 MB Infinity
 Cache cannot serve repeated reads.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4|5] [--kv-dtype bf16|fp8]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3|4|5|6] [--kv-dtype bf16|fp8]
+                  [--block-size 16|32] [--queries-per-seq T] [--shared] [--graph]
 
 --kv-dtype fp8 keeps the same bf16 step (queries, new K/V rows, outputs) but
 stores the cache as e4m3 codes with per-layer scales: the append quantizes,
@@ -61,10 +62,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def make_step(config: int):
+def make_step(config: int, block_size: int = 16):
     from paged_kv_decode_reshape_amd import workloads as W
+    if block_size != 16 and config != 3:
+        raise SystemExit("--block-size other than 16 is benchmarked on config 3")
     if config == 3:
-        return W.llama8b_continuous()
+        return W.llama8b_continuous(block_size=block_size)
     if config == 4:
         return W.long_context()
     if config == 5:
@@ -193,6 +196,8 @@ def main():
                     help="cache storage: bf16 (the workload's dtype) or e4m3 codes")
     ap.add_argument("--queries-per-seq", type=int, default=1,
                     help="query rows per decoding sequence (> 1: speculative-verification step)")
+    ap.add_argument("--block-size", type=int, default=16, choices=(16, 32),
+                    help="tokens per pool block (32: config 3 only)")
     ap.add_argument("--shared", action="store_true",
                     help="decode through paged_attention_decode_shared with the step's sharing groups "
                          "(--config 6)")
@@ -220,7 +225,7 @@ def main():
         f"{props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB")
 
     t0 = time.time()
-    step = make_step(args.config)
+    step = make_step(args.config, args.block_size)
     s = step
     log(f"workload {s.name}: generated in {time.time() - t0:.1f}s; "
         f"{len(s.decode_seqs)} decode seqs, tokens {int(s.context_lens.sum())}, info {s.info}")
@@ -432,7 +437,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": read_traffic(kvd) if tq == 1 and not shared and args.config == 3 else None,
+            "traffic": (read_traffic(kvd) if tq == 1 and not shared and args.config == 3 and s.block_size == 16
+                        else None),
             "algorithmic_bytes_per_launch": part_bytes,
         },
     }

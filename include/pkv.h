@@ -43,8 +43,12 @@
  *     [0, num_blocks), 0 <= context_lens[b] <= max_blocks_per_seq*block_size,
  *     slots < num_blocks*block_size, no two tokens of one call with the same
  *     slot (they would race).
- *   - Supported geometry: block_size 16; head_dim 64 or 128; query heads per
- *     KV head (num_q_heads / num_kv_heads) from 1 to 8.
+ *   - Supported geometry: block_size 16, or 32 for bf16 and e4m3 pools (the
+ *     pages call sixteen tokens a common block size and thirty-two often
+ *     better when very long generations dominate: "The Serving Playbook",
+ *     "The block table lives in the hottest kernel in the system"); head_dim
+ *     64 or 128; query heads per KV head (num_q_heads / num_kv_heads) from 1
+ *     to 8.
  *
  * Pool layout in HBM, per layer (this is the "reshape" of reshape_and_cache:
  * the head dimension is cut into 16-byte vectors so that loads stay wide

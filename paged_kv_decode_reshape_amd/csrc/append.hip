@@ -12,8 +12,9 @@
 // One thread moves one 16-byte vector of K and the same vector of V. Threads
 // are numbered (token, kv head, vector) with the vector fastest, so reads of
 // the token-major input and writes of V rows are contiguous 16-byte runs; K
-// vectors land 256 bytes apart (bf16, D=128) in the pool's K layout
-// [block][head][D/x][16][x].
+// vectors land 16 * block_size bytes apart in the pool's K layout
+// [block][head][D/x][block_size][x] (block_size 16, or 32 for bf16 and e4m3
+// pools).
 //
 // An e4m3 pool takes bf16 rows: a thread reads 32 bytes (16 values) and
 // writes their 16 codes, quantized with the layer's 1/scale (saturating,
@@ -26,7 +27,7 @@ namespace pkv {
 
 namespace {
 
-template <typename T, int D>
+template <typename T, int D, int BS>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams prm) {
   constexpr int EPV = ElemTraits<T>::kPerVec;
   constexpr int VPR = D / EPV;
@@ -39,13 +40,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams prm) {
   const int c = rem % VPR;
   const int64_t slot = prm.slots[t];
   if (slot < 0) return;
-  const int64_t blk = slot / kBlockSize;
-  const int off = (int)(slot % kBlockSize);
+  const int64_t blk = slot / BS;
+  const int off = (int)(slot % BS);
   const size_t src = ((size_t)t * prm.num_kv_heads + h) * D + (size_t)c * EPV;
-  const size_t tile = ((size_t)blk * prm.num_kv_heads + h) * (size_t)kBlockSize * D;
+  const size_t tile = ((size_t)blk * prm.num_kv_heads + h) * (size_t)BS * D;
   const Vec16 k = ld16(reinterpret_cast<const T*>(prm.key) + src);
   const Vec16 v = ld16(reinterpret_cast<const T*>(prm.value) + src);
-  st16(reinterpret_cast<T*>(prm.kpool) + tile + ((size_t)c * kBlockSize + off) * EPV, k);
+  st16(reinterpret_cast<T*>(prm.kpool) + tile + ((size_t)c * BS + off) * EPV, k);
   st16(reinterpret_cast<T*>(prm.vpool) + tile + (size_t)off * D + (size_t)c * EPV, v);
 }
 
@@ -64,7 +65,7 @@ __device__ __forceinline__ Vec16 quantize16(const uint16_t* p, float inv_scale) 
   return q;
 }
 
-template <int D>
+template <int D, int BS>
 __global__ __launch_bounds__(256) void append_fp8_kernel(AppendParams prm) {
   constexpr int VPR = D / 16;   // 16-byte code vectors per token row
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -76,13 +77,13 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendParams prm) {
   const int c = rem % VPR;
   const int64_t slot = prm.slots[t];
   if (slot < 0) return;
-  const int64_t blk = slot / kBlockSize;
-  const int off = (int)(slot % kBlockSize);
+  const int64_t blk = slot / BS;
+  const int off = (int)(slot % BS);
   const size_t src = ((size_t)t * prm.num_kv_heads + h) * D + (size_t)c * 16;
-  const size_t tile = ((size_t)blk * prm.num_kv_heads + h) * (size_t)kBlockSize * D;
+  const size_t tile = ((size_t)blk * prm.num_kv_heads + h) * (size_t)BS * D;
   const Vec16 k = quantize16(reinterpret_cast<const uint16_t*>(prm.key) + src, prm.k_inv_scale);
   const Vec16 v = quantize16(reinterpret_cast<const uint16_t*>(prm.value) + src, prm.v_inv_scale);
-  st16(reinterpret_cast<uint8_t*>(prm.kpool) + tile + ((size_t)c * kBlockSize + off) * 16, k);
+  st16(reinterpret_cast<uint8_t*>(prm.kpool) + tile + ((size_t)c * BS + off) * 16, k);
   st16(reinterpret_cast<uint8_t*>(prm.vpool) + tile + (size_t)off * D + (size_t)c * 16, v);
 }
 
@@ -91,7 +92,11 @@ hipError_t launch_append_fp8(const AppendParams& prm, hipStream_t stream, const 
   const long threads = (long)prm.num_tokens * prm.num_kv_heads * (D / 16);
   const unsigned grid = (unsigned)((threads + 255) / 256);
   timer.begin(KernelKind::kAppend, stream);
-  hipLaunchKernelGGL((append_fp8_kernel<D>), dim3(grid), dim3(256), 0, stream, prm);
+  if (prm.block_size == 32) {
+    hipLaunchKernelGGL((append_fp8_kernel<D, 32>), dim3(grid), dim3(256), 0, stream, prm);
+  } else {
+    hipLaunchKernelGGL((append_fp8_kernel<D, kBlockSize>), dim3(grid), dim3(256), 0, stream, prm);
+  }
   timer.end(KernelKind::kAppend, stream);
   return hipGetLastError();
 }
@@ -102,7 +107,11 @@ hipError_t launch_append_t(const AppendParams& prm, hipStream_t stream, const Ke
   const long threads = (long)prm.num_tokens * prm.num_kv_heads * VPR;
   const unsigned grid = (unsigned)((threads + 255) / 256);
   timer.begin(KernelKind::kAppend, stream);
-  hipLaunchKernelGGL((append_kernel<T, D>), dim3(grid), dim3(256), 0, stream, prm);
+  if (prm.block_size == 32) {
+    hipLaunchKernelGGL((append_kernel<T, D, 32>), dim3(grid), dim3(256), 0, stream, prm);
+  } else {
+    hipLaunchKernelGGL((append_kernel<T, D, kBlockSize>), dim3(grid), dim3(256), 0, stream, prm);
+  }
   timer.end(KernelKind::kAppend, stream);
   return hipGetLastError();
 }

@@ -515,7 +515,9 @@ __device__ __forceinline__ mf_bf16x8 mf_fp8_half(const Vec16& v) {
 // first member's row when the columns are sequences sharing a prefix).
 // kStream: K/V loads carry the nontemporal hint (the cache is read once per
 // step); off when other wavefronts of the workgroup read the same tiles.
-template <typename T, int D, int G, bool MQ, bool kStream = true>
+// BS: tokens per pool block (16 or 32); a 64-token window is 64 / BS blocks
+// and each 16-token MFMA tile lies inside one block.
+template <typename T, int D, int G, bool MQ, int BS, bool kStream = true>
 __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, MfmaWaveLds<D>& lds, int b, int h,
                                                             int tok_begin, int tok_end, int ctx, int& done,
                                                             int share, int qrow0) {
@@ -530,13 +532,15 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
   constexpr int RPI = kWave / VPRB;                   // V rows per load instruction
   constexpr int VLD = 32 / RPI;                       // V load instructions per half window
   constexpr int TPW = 64;
-  static_assert(kBlockSize % RPI == 0, "a V load instruction stays inside one block");
+  static_assert(BS == 16 || BS == 32, "block size 16 or 32");
+  static_assert(16 % RPI == 0, "a V load instruction stays inside one 16-token tile");
+  constexpr int BPW = TPW / BS;                       // blocks per window
 
   const int lane = threadIdx.x & 63;
   const int quad = lane >> 4, col = lane & 15;
   const int nwin = (tok_end - tok_begin + TPW - 1) / TPW;
-  const int lb_begin = tok_begin / kBlockSize;
-  const int nblk = (tok_end - tok_begin + kBlockSize - 1) / kBlockSize;
+  const int lb_begin = tok_begin / BS;
+  const int nblk = (tok_end - tok_begin + BS - 1) / BS;
   // Block ids of the segment, 64 per register, clamped to its last block so
   // that every address formed below is in bounds.
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin;
@@ -564,11 +568,11 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
     }
   }
 
-  const size_t tile_bytes = (size_t)kBlockSize * D * sizeof(T);
+  const size_t tile_bytes = (size_t)BS * D * sizeof(T);
   const size_t blk_bytes = (size_t)a.hkv * tile_bytes;
   const char* kbase = static_cast<const char*>(a.kpool) + (size_t)h * tile_bytes;
   const char* vbase = static_cast<const char*>(a.vpool) + (size_t)h * tile_bytes;
-  const uint32_t k_lane = (uint32_t)((quad * kBlockSize + col) * 16);   // vector (4j + quad) of token col
+  const uint32_t k_lane = (uint32_t)((quad * BS + col) * 16);   // vector (4j + quad) of token col
   const int v_row = lane / VPRB, v_vec = lane % VPRB;
   const uint32_t v_lane = (uint32_t)(v_row * D * (int)sizeof(T) + v_vec * 16);
   const int vkey = 4 * quad + (col >> 2), vcol = 4 * (col & 3);   // transposed V read of this lane
@@ -584,20 +588,20 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
     if (share > 0) set_wave_priority(3 - (4 * done) / share);
     ++done;
     const int t0 = tok_begin + w * TPW;
-    const int lb = 4 * w;
+    const int lb = BPW * w;
     if (lb > 0 && (lb & 63) == 0) ids = bt[min(lb + lane, nblk - 1)];
-    int bid[4];
+    int bid[4];                                         // block of the window's 16-token tile r
 #pragma unroll
-    for (int r = 0; r < 4; ++r) bid[r] = __builtin_amdgcn_readlane(ids, min(lb + r, nblk - 1) & 63);
+    for (int r = 0; r < 4; ++r) bid[r] = __builtin_amdgcn_readlane(ids, min(lb + 16 * r / BS, nblk - 1) & 63);
 
     // ---- loads: the window's K fragments and V rows ----
     Vec16 kr[4][KL];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const char* kt = kbase + (size_t)bid[r] * blk_bytes;
+      const char* kt = kbase + (size_t)bid[r] * blk_bytes + (16 * r % BS) * 16;
 #pragma unroll
       for (int j = 0; j < KL; ++j) {
-        const char* pk = kt + j * (4 * kBlockSize * 16) + k_lane;
+        const char* pk = kt + j * (4 * BS * 16) + k_lane;
         kr[r][j] = kStream ? ld16_stream(pk) : ld16(pk);
       }
     }
@@ -606,9 +610,9 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int u = 0; u < VLD; ++u) {
-        const int row0 = u * RPI;                       // first row of the instruction in the half
-        const char* vt = vbase + (size_t)bid[2 * kk + row0 / kBlockSize] * blk_bytes;
-        const char* pv = vt + (row0 % kBlockSize) * D * (int)sizeof(T) + v_lane;
+        const int tw = 32 * kk + u * RPI;               // first window row of the instruction
+        const char* vt = vbase + (size_t)bid[tw / 16] * blk_bytes;
+        const char* pv = vt + (tw % BS) * D * (int)sizeof(T) + v_lane;
         vr[kk][u] = kStream ? ld16_stream(pv) : ld16(pv);
       }
     }
@@ -767,13 +771,14 @@ struct UsesMfma {
 template <typename T, int D, int G>
 using SegLds = typename std::conditional<UsesMfma<T>::value, MfmaWaveLds<D>, WaveLds<T, D, G>>::type;
 
-template <typename T, int D, int G, bool MQ>
+template <typename T, int D, int G, bool MQ, int BS>
 __device__ __forceinline__ auto run_seg(const DecodeArgs& a, SegLds<T, D, G>& lds, int b, int h, int tok_begin,
                                         int tok_end, int ctx, int& done, int share) {
   if constexpr (UsesMfma<T>::value) {
-    return run_segment_mfma<T, D, G, MQ>(a, lds, b, h, tok_begin, tok_end, ctx, done, share,
-                                         b * (MQ ? a.nq : 1));
+    return run_segment_mfma<T, D, G, MQ, BS>(a, lds, b, h, tok_begin, tok_end, ctx, done, share,
+                                             b * (MQ ? a.nq : 1));
   } else {
+    static_assert(BS == kBlockSize, "lane-per-token segments take 16-token blocks");
     return run_segment<T, D, G>(a, lds, b, h, tok_begin, tok_end, ctx, done, share);
   }
 }
@@ -789,7 +794,7 @@ constexpr int decode_waves_per_simd() {
 // ---------------------------------------------------------------------------
 // Fixed partitions: one wavefront per (b, h, partition).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G, bool MQ>
+template <typename T, int D, int G, bool MQ, int BS>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_partition_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
@@ -828,7 +833,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   if (tok_begin >= ctx) return;
   const int tok_end = min(ctx, tok_begin + prm.part_tokens);
   int done = 0;
-  const auto st = run_seg<T, D, G, MQ>(args, lds[wave], b, h, tok_begin, tok_end, ctx, done, 0);
+  const auto st = run_seg<T, D, G, MQ, BS>(args, lds[wave], b, h, tok_begin, tok_end, ctx, done, 0);
   if (ctx <= prm.part_tokens) {
     write_rows<T, D, G>(out_row, st, args.v_scale, nq, hq);
   } else {
@@ -872,7 +877,7 @@ __device__ __forceinline__ int group_shared_tokens(const int32_t* __restrict__ c
   return plen / 64 * 64;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, int BS>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_prefix_kernel(
     const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
   __shared__ MfmaWaveLds<D> lds[4];
@@ -919,7 +924,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   // Blocks come from the first member's table (all members hold the same ids
   // there); with ctx = tok_end + nm no column is masked inside the piece.
   const MfmaSummary<D> st =
-      run_segment_mfma<T, D, G, true, false>(a, lds[wave], seq0, h, tok_begin, tok_end, tok_end + nm, done, 0,
+      run_segment_mfma<T, D, G, true, BS, false>(a, lds[wave], seq0, h, tok_begin, tok_end, tok_end + nm, done, 0,
                                              seq0 + m0);
   const int hq = args.hkv * G;
   const size_t qh0 = (size_t)(seq0 + m0) * hq + (size_t)h * G;
@@ -1124,7 +1129,7 @@ __device__ __forceinline__ void write_rows_shared(typename IoType<T>::type* out_
 
 // SH: the rows start after their shared partitions (decode_prefix_kernel has
 // run), and every row is merged with those partitions' summaries.
-template <typename T, int D, int G, bool MQ, bool SH>
+template <typename T, int D, int G, bool MQ, bool SH, int BS>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_balanced_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     SlotDesc* __restrict__ ws_desc, const int32_t* __restrict__ context_lens, DecodeArgs args,
@@ -1193,7 +1198,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
     const int w0 = r % nwb;
     const int w1 = min(nwb, w0 + (x1 - x));
     const auto st =
-        run_seg<T, D, G, MQ>(args, lds[wave], b, h, t0 + w0 * 64, min(ctx, t0 + w1 * 64), ctx, done, x1 - x0);
+        run_seg<T, D, G, MQ, BS>(args, lds[wave], b, h, t0 + w0 * 64, min(ctx, t0 + w1 * 64), ctx, done, x1 - x0);
     const int hq = args.hkv * G;
     const size_t qh0 = (size_t)b * nq * hq + (size_t)h * G;
     if (w0 == 0 && w1 == nwb) {
@@ -1333,7 +1338,7 @@ __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
   }
 }
 
-template <typename T, int D, int G, bool MQ>
+template <typename T, int D, int G, bool MQ, int BS>
 hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
   using TQ = typename IoType<T>::type;
   const DecodeArgs args{prm.query, prm.kpool, prm.vpool, prm.block_tables, prm.num_kv_heads,
@@ -1348,7 +1353,7 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
       const long punits = (long)prm.num_kv_heads * prm.member_tiles * prm.num_groups * prm.max_parts;
       const long pblocks = std::max((punits + 3) / 4, ((long)prm.num_seqs + 255) / 256);
       timer.begin(KernelKind::kDecodePrefix, stream);
-      hipLaunchKernelGGL((decode_prefix_kernel<T, D, G>), dim3((unsigned)pblocks), dim3(256), 0, stream,
+      hipLaunchKernelGGL((decode_prefix_kernel<T, D, G, BS>), dim3((unsigned)pblocks), dim3(256), 0, stream,
                          prm.context_lens, args, prm);
       timer.end(KernelKind::kDecodePrefix, stream);
       if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1360,14 +1365,14 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
     const dim3 grid((unsigned)((prm.num_waves + 3) / 4));
     if constexpr (kShareable) {
       if (prm.shared_start != nullptr) {
-        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, true>), grid, dim3(256), 0, stream, out,
+        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, true, BS>), grid, dim3(256), 0, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       } else {
-        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false>), grid, dim3(256), 0, stream, out,
+        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS>), grid, dim3(256), 0, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       }
     } else {
-      hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false>), grid, dim3(256), 0, stream, out,
+      hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS>), grid, dim3(256), 0, stream, out,
                          prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
     }
     timer.end(KernelKind::kDecodePartition, stream);
@@ -1381,7 +1386,7 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
   }
   const long units = (long)prm.num_kv_heads * prm.num_seqs * prm.max_parts;
   timer.begin(KernelKind::kDecodePartition, stream);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ>), dim3((unsigned)((units + 3) / 4)), dim3(256),
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ, BS>), dim3((unsigned)((units + 3) / 4)), dim3(256),
                      0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
   timer.end(KernelKind::kDecodePartition, stream);
   if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1396,15 +1401,21 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
   return err;
 }
 
-// Several query rows per sequence run on the matrix cores only.
+// Several query rows per sequence, and 32-token blocks, run on the matrix
+// cores only.
 template <typename T, int D, int G>
 hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
   if constexpr (UsesMfma<T>::value) {
-    if (prm.q_per_seq > 1) return launch_decode_tgm<T, D, G, true>(prm, stream, timer);
+    if (prm.block_size == 32) {
+      if (prm.q_per_seq > 1) return launch_decode_tgm<T, D, G, true, 32>(prm, stream, timer);
+      return launch_decode_tgm<T, D, G, false, 32>(prm, stream, timer);
+    }
+    if (prm.block_size != kBlockSize) return hipErrorNotSupported;
+    if (prm.q_per_seq > 1) return launch_decode_tgm<T, D, G, true, kBlockSize>(prm, stream, timer);
   } else {
-    if (prm.q_per_seq > 1) return hipErrorNotSupported;
+    if (prm.q_per_seq > 1 || prm.block_size != kBlockSize) return hipErrorNotSupported;
   }
-  return launch_decode_tgm<T, D, G, false>(prm, stream, timer);
+  return launch_decode_tgm<T, D, G, false, kBlockSize>(prm, stream, timer);
 }
 
 template <typename T, int D, int G, bool MQ>
@@ -1412,7 +1423,7 @@ int balanced_waves_per_cu() {
   static int cached = 0;
   if (cached == 0) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ, false>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ, false, kBlockSize>, 256, 0) !=
             hipSuccess ||
         blocks <= 0) {
       (void)hipGetLastError();

@@ -59,7 +59,10 @@ pkv_status check_geometry(int num_blocks, int block_size, int num_kv_heads, int 
   if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be positive (got %d)", num_kv_heads);
   if (block_size <= 0 || head_dim <= 0) return fail(PKV_ERR_INVALID_ARG, "block_size and head_dim must be positive");
   if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_FP8_E4M3) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  if (block_size != pkv::kPoolBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
+  if (block_size != pkv::kPoolBlockSize && block_size != pkv::kPoolBlockSizeLarge)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16, or 32 for bf16 and e4m3 pools)", block_size);
+  if (block_size == pkv::kPoolBlockSizeLarge && dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size 32 takes bf16 and e4m3 pools (fp32 pools use 16)");
   if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d unsupported (64 or 128)", head_dim);
   return PKV_OK;
 }
@@ -277,7 +280,7 @@ pkv_status reshape_and_cache(const pkv_pool* pool, int layer, const void* key,
   if (threads >= (1L << 32) - 256) return fail(PKV_ERR_UNSUPPORTED, "too many tokens in one call");
   pkv::AppendParams prm{pool->k_layers[layer], pool->v_layers[layer], key, value, slot_mapping,
                         num_tokens, pool->num_kv_heads, pool->head_dim,
-                        1.0f / pool->k_scale[layer], 1.0f / pool->v_scale[layer]};
+                        1.0f / pool->k_scale[layer], 1.0f / pool->v_scale[layer], pool->block_size};
   (void)hipGetLastError();
   hipError_t err = pkv::launch_append(prm, pool_type(pool->dtype), (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "reshape_and_cache launch");
@@ -367,7 +370,8 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
                         block_tables, context_lens, num_seqs, pool->num_kv_heads, group,
                         pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
                         num_waves, scale * 1.4426950408889634f * pool->k_scale[layer],
-                        pool->v_scale[layer], q_per_seq};
+                        pool->v_scale[layer], q_per_seq, nullptr, nullptr, 0, 0, nullptr, nullptr, nullptr,
+                        pool->block_size};
   (void)hipGetLastError();
   hipError_t err = pkv::launch_decode(prm, type, (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "paged_attention_decode launch");
@@ -508,7 +512,7 @@ pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* 
                         pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
                         num_waves, scale * 1.4426950408889634f * pool->k_scale[layer],
                         pool->v_scale[layer], 1, group_starts, prefix_lens, num_groups, (int)member_tiles,
-                        shared_start, pre_ml, pre_o};
+                        shared_start, pre_ml, pre_o, pool->block_size};
   (void)hipGetLastError();
   hipError_t err = pkv::launch_decode(prm, type, (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "paged_attention_decode_shared launch");
@@ -605,7 +609,8 @@ pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* 
   pkv::PrefillParams prm{out, query, pool->k_layers[layer], pool->v_layers[layer], cu_q_lens,
                          block_tables, context_lens, num_seqs, total_q_tokens, max_q_len,
                          pool->num_kv_heads, group, pool->head_dim, max_blocks_per_seq,
-                         scale * 1.4426950408889634f * pool->k_scale[layer], pool->v_scale[layer]};
+                         scale * 1.4426950408889634f * pool->k_scale[layer], pool->v_scale[layer],
+                         pool->block_size};
   (void)hipGetLastError();
   hipError_t err = pkv::launch_prefill(prm, pool_type(pool->dtype), (hipStream_t)stream, pkv::KernelTimer{});
   if (err == hipErrorNotSupported) return fail(PKV_ERR_UNSUPPORTED, "prefill geometry not supported");

@@ -6,7 +6,10 @@
 
 namespace pkv {
 
-constexpr int kPoolBlockSize = 16;  // tokens per KV block supported by the kernels
+// Tokens per KV block the kernels take: 16 for every pool type, and 32 for
+// bf16 and e4m3 pools.
+constexpr int kPoolBlockSize = 16;
+constexpr int kPoolBlockSizeLarge = 32;
 
 enum class KernelKind : int { kAppend = 0, kDecodePartition = 1, kDecodeReduce = 2, kPrefill = 3, kDecodePrefix = 4 };
 
@@ -31,6 +34,7 @@ struct AppendParams {
   int head_dim;
   float k_inv_scale;       // e4m3 pools: 1 / the layer's K scale (fp32)
   float v_inv_scale;       // e4m3 pools: 1 / the layer's V scale (fp32)
+  int block_size;          // tokens per pool block (16 or 32)
 };
 
 struct DecodeParams {
@@ -67,6 +71,7 @@ struct DecodeParams {
                            // 64); its ceil(shared_start / part_tokens) pieces before it are shared
   float* pre_ml;           // shared pieces' summaries: float2 [num_seqs][Hq][max_parts]
   float* pre_o;            // float [num_seqs][Hq][max_parts][D], unnormalized, times the V scale
+  int block_size;          // tokens per pool block: 16, or 32 for bf16 and e4m3 pools
 };
 
 struct PrefillParams {
@@ -86,6 +91,7 @@ struct PrefillParams {
   int max_blocks;
   float scale_log2;        // scale * log2(e), times the K scale of an e4m3 pool
   float v_scale;           // e4m3 pools: the V scale; else 1
+  int block_size;          // tokens per pool block (16 or 32)
 };
 
 hipError_t launch_append(const AppendParams& prm, PoolType type, hipStream_t stream,

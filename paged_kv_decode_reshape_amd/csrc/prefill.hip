@@ -68,13 +68,13 @@ __host__ __device__ constexpr int prefill_row_subtiles(int g) { return (g <= 4 &
 // group has at most 4 waves (12 waves, 3 per SIMD), else two.
 __host__ __device__ constexpr int prefill_groups(int g) { return g * prefill_row_subtiles(g) <= 4 ? 3 : 2; }
 
-template <int D, int NWG, int NG>
+template <int D, int NWG, int NG, int BS>
 union PrefillLds {
   // V rows padded by 32 bytes: the transposed reads of 8 consecutive keys then
   // fall on distinct LDS banks.
   static constexpr int kVStride = D + 16;
   struct {
-    alignas(16) uint16_t k[NG][kKeyTile / kBlockSize][kBlockSize * D];   // K tiles, pool layout
+    alignas(16) uint16_t k[NG][kKeyTile / BS][BS * D];                   // K tiles, pool layout
     alignas(16) uint16_t v[NG][kKeyTile][kVStride];                     // V tiles, [key][head dim]
   } tile;
   struct {                                                               // groups 1.., at the end
@@ -86,7 +86,8 @@ union PrefillLds {
 
 // TP: the pool's element type, bf16 bits (uint16_t) or e4m3 codes (uint8_t);
 // queries, outputs and the LDS tiles are bf16 either way.
-template <int D, int G, typename TP>
+// BS: tokens per pool block (16 or 32); a 64-key tile is 64 / BS blocks.
+template <int D, int G, typename TP, int BS>
 __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G)) void prefill_chunk_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ query, const TP* __restrict__ kpool,
     const TP* __restrict__ vpool, const int32_t* __restrict__ cu_q_lens,
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   constexpr int VPR = D / 8;              // 16-byte vectors per token row
   constexpr int kVecs = kKeyTile * VPR;   // 16-byte vectors per key tile of K (and of V)
   constexpr int PER = (NG * kVecs + NT - 1) / NT;   // vectors each thread stages per step
-  __shared__ PrefillLds<D, NWG, NG> lds;
+  __shared__ PrefillLds<D, NWG, NG, BS> lds;
 
   const int s = blockIdx.z;
   const int h = blockIdx.y;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   for (int n = 0; n < NTILES; ++n) o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t* bt = block_tables + (size_t)s * prm.max_blocks;
-  const size_t tile_elems = (size_t)kBlockSize * D;
+  const size_t tile_elems = (size_t)BS * D;
   const size_t head_off = (size_t)h * tile_elems;
   const size_t blk_stride = (size_t)hkv * tile_elems;
 
@@ -179,21 +180,25 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   //   no clearing (their scores are masked); V rows are cleared (they may
   //   hold anything, NaN included, and their zero weights would not cancel
   //   a NaN).
-  constexpr int kBlockVecs = kBlockSize * VPR;
-  constexpr int kStepBlocks = NG * kKeyTile / kBlockSize;
+  constexpr int kBlockVecs = BS * VPR;
+  constexpr int kStepBlocks = NG * kKeyTile / BS;
   constexpr bool kAllSlots = NT * PER == NG * kVecs;   // every thread's slots hold a vector
   static_assert(kBlockVecs % kWave == 0, "a wavefront's vectors must share a block");
   const int wave_vec0 = w * kWave;
   // An e4m3 pool is staged 8 codes (8 bytes) per LDS vector and widened to
-  // bf16 (exactly) when stored to LDS. Its K tile is [D/16][16][16]: LDS
-  // vector (c8, token tin) reads 8 bytes at ((c8/2)*16 + tin)*16 + (c8%2)*8.
+  // bf16 (exactly) when stored to LDS. Its K tile is [D/16][BS][16]: LDS
+  // vector (c8, token tin) reads 8 bytes at ((c8/2)*BS + tin)*16 + (c8%2)*8.
+  // A wavefront's 64 LDS vectors start at a multiple of 64, so lane l holds
+  // c8 = c0 + l/BS (c0 even) and tin = l % BS.
   constexpr bool kF8 = sizeof(TP) == 1;
   constexpr int SW = kF8 ? 2 : 4;                                                  // staged words per vector
   const uint32_t lane_k = (uint32_t)lane * 16u;                                   // K in LDS (and a bf16 pool)
-  const uint32_t lane_kg = kF8 ? (uint32_t)((((lane >> 5) * 16 + (lane & 15)) * 16) + ((lane >> 4) & 1) * 8)
-                               : lane_k;                                          // K in the pool tile
+  const uint32_t lane_kg =
+      !kF8 ? lane_k
+           : BS == 16 ? (uint32_t)((((lane >> 5) * 16 + (lane & 15)) * 16) + ((lane >> 4) & 1) * 8)
+                      : (uint32_t)((lane & 31) * 16 + (lane >> 5) * 8);           // K in the pool tile
   const uint32_t lane_vg = (uint32_t)((lane / VPR) * D + (lane % VPR) * 8) * (uint32_t)sizeof(TP);  // V in the pool tile
-  const uint32_t lane_vl = (uint32_t)((lane / VPR) * PrefillLds<D, NWG, NG>::kVStride + (lane % VPR) * 8) * 2u;  // V in LDS
+  const uint32_t lane_vl = (uint32_t)((lane / VPR) * PrefillLds<D, NWG, NG, BS>::kVStride + (lane % VPR) * 8) * 2u;  // V in LDS
   const int lane_tok = lane / VPR;                                                // V: token offset of the lane
   char* const lds_k = reinterpret_cast<char*>(&lds.tile.k[0][0][0]);
   char* const lds_v = reinterpret_cast<char*>(&lds.tile.v[0][0][0]);
@@ -231,7 +236,7 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
     for (int u = 0; u < PER; ++u) {
       const int pb = (wave_vec0 + u * NT) / kBlockVecs;   // block of the step, uniform
       const int lb = j * kStepBlocks + pb;
-      ids[u] = (pb < kStepBlocks && lb * kBlockSize < kv_end) ? bt[lb] : 0;
+      ids[u] = (pb < kStepBlocks && lb * BS < kv_end) ? bt[lb] : 0;
     }
   };
   auto load_step = [&](int j, const int (&ids)[PER]) {
@@ -240,13 +245,13 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
       const int q0 = wave_vec0 + u * NT;                   // uniform
       if (!kAllSlots && q0 >= NG * kVecs) continue;
       const int qq0 = q0 % kVecs;
-      const int key0 = j * NG * kKeyTile + (q0 / kBlockVecs) * kBlockSize;   // first key of the block
+      const int key0 = j * NG * kKeyTile + (q0 / kBlockVecs) * BS;   // first key of the block
       if (key0 < kv_end) {                                 // uniform: blocks past the range are not read
         const size_t base = ((size_t)ids[u] * blk_stride + head_off) * sizeof(TP);
         const char* kb = reinterpret_cast<const char*>(kpool) + base;
         const char* vb = reinterpret_cast<const char*>(vpool) + base;
         kreg[u] = ld_stage(kb + (uint32_t)(qq0 % kBlockVecs) * (uint32_t)(8 * sizeof(TP)) + lane_kg);
-        const int tok0 = (qq0 / VPR) % kBlockSize;         // uniform
+        const int tok0 = (qq0 / VPR) % BS;                 // uniform
         vreg[u] = ld_stage(vb + (uint32_t)(tok0 * D * (int)sizeof(TP)) + lane_vg);
       }
     }
@@ -259,14 +264,14 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
       const int q0 = wave_vec0 + u * NT;
       if (!kAllSlots && q0 >= NG * kVecs) continue;
       const int t = q0 / kVecs, qq0 = q0 % kVecs;
-      const int key0 = j * NG * kKeyTile + (q0 / kBlockVecs) * kBlockSize;   // first key of the block
-      const int tok0 = (qq0 / VPR) % kBlockSize;
+      const int key0 = j * NG * kKeyTile + (q0 / kBlockVecs) * BS;   // first key of the block
+      const int tok0 = (qq0 / VPR) % BS;
       if (key0 + tok0 + lane_tok >= kv_end) {
 #pragma unroll
         for (int i = 0; i < SW; ++i) vreg[u].w[i] = 0u;
       }
       *reinterpret_cast<uint4*>(lds_k + (uint32_t)(t * (kKeyTile * D) + qq0 * 8) * 2u + lane_k) = to_bf16(kreg[u]);
-      *reinterpret_cast<uint4*>(lds_v + (uint32_t)((t * kKeyTile + qq0 / VPR) * PrefillLds<D, NWG, NG>::kVStride) * 2u +
+      *reinterpret_cast<uint4*>(lds_v + (uint32_t)((t * kKeyTile + qq0 / VPR) * PrefillLds<D, NWG, NG, BS>::kVStride) * 2u +
                                 lane_vl) = to_bf16(vreg[u]);
     }
   };
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
       st[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KSTEPS; ++k) {
-        const Vec16 kf = lds_ld16(&lds.tile.k[grp][r][((4 * k + quad) * kBlockSize + col) * 8]);
+        const Vec16 kf = lds_ld16(&lds.tile.k[grp][16 * r / BS][((4 * k + quad) * BS + 16 * r % BS + col) * 8]);
         st[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf), qf[k], st[r], 0, 0, 0);
       }
     }
@@ -440,10 +445,18 @@ hipError_t launch_prefill_dg(const PrefillParams& prm, hipStream_t stream) {
   constexpr int RT = prefill_row_subtiles(G);
   const dim3 grid((unsigned)((prm.max_q_len + kQRows * RT - 1) / (kQRows * RT)), (unsigned)prm.num_kv_heads,
                   (unsigned)prm.num_seqs);
-  hipLaunchKernelGGL((prefill_chunk_kernel<D, G, TP>), grid, dim3(64 * G * RT * prefill_groups(G)), 0, stream,
-                     static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
-                     static_cast<const TP*>(prm.kpool), static_cast<const TP*>(prm.vpool),
-                     prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
+  const dim3 block(64 * G * RT * prefill_groups(G));
+  if (prm.block_size == 32) {
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, TP, 32>), grid, block, 0, stream,
+                       static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
+                       static_cast<const TP*>(prm.kpool), static_cast<const TP*>(prm.vpool),
+                       prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
+  } else {
+    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, TP, kBlockSize>), grid, block, 0, stream,
+                       static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
+                       static_cast<const TP*>(prm.kpool), static_cast<const TP*>(prm.vpool),
+                       prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
+  }
   return hipGetLastError();
 }
 
@@ -473,6 +486,7 @@ hipError_t launch_prefill(const PrefillParams& prm, PoolType type, hipStream_t s
   if (prm.group < 1 || prm.group > kMaxGroup) return hipErrorNotSupported;
   if (prm.head_dim != 64 && prm.head_dim != 128) return hipErrorNotSupported;
   if (type != PoolType::kBF16 && type != PoolType::kFP8) return hipErrorNotSupported;
+  if (prm.block_size != kBlockSize && prm.block_size != 32) return hipErrorNotSupported;
   timer.begin(KernelKind::kPrefill, stream);
   const hipError_t err = type == PoolType::kFP8 ? launch_prefill_t<uint8_t>(prm, stream)
                                                 : launch_prefill_t<uint16_t>(prm, stream);

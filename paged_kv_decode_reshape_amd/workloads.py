@@ -373,15 +373,16 @@ def _churn_tables(rng, ctx, bs, rounds=4, median=600.0, sigma=1.0, lo=16, hi=819
     return tables, num_blocks, poison
 
 
-def llama8b_continuous(rep: int = 0, batch: int = 256) -> Step:
+def llama8b_continuous(rep: int = 0, batch: int = 256, block_size: int = BLOCK_SIZE) -> Step:
     """Llama-8B-shaped layer, B=256 continuous batching, lognormal lengths, churned pool."""
     rng = _rng(3, rep)
-    bs = BLOCK_SIZE
+    bs = block_size
     ctx = lognormal_lengths(rng, batch)
     tables, num_blocks, poison = _churn_tables(rng, ctx, bs)
     info = {"adjacent_block_fraction": adjacency_fraction(tables, ctx, bs),
             "total_tokens": int(ctx.sum())}
-    return _assemble("llama8b_b256_lognormal", rng, "bf16", 32, 8, 128, bs, num_blocks,
+    name = "llama8b_b256_lognormal" + ("" if bs == BLOCK_SIZE else f"_bs{bs}")
+    return _assemble(name, rng, "bf16", 32, 8, 128, bs, num_blocks,
                      poison, ctx, tables, np.ones(batch, np.int64), np.arange(batch), [],
                      info=info)
 
@@ -418,11 +419,11 @@ def mixed_chunked_prefill(rep: int = 0, chunk: int = 512, cached: int = 2048,
 
 
 def custom(name, *, seed, dtype, hq, hkv, d, ctx, q_lens=None, pool_factor=1.25,
-           boost_k_fraction=0.0, partition_size=0) -> Step:
+           boost_k_fraction=0.0, partition_size=0, block_size=BLOCK_SIZE) -> Step:
     """General seeded step for tests: per-sequence lengths ``ctx`` and, optionally,
     prefill chunk lengths ``q_lens`` (0 = the sequence decodes one token)."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    bs = BLOCK_SIZE
+    bs = block_size
     ctx = np.asarray(ctx, dtype=np.int32)
     q_lens = np.zeros(len(ctx), np.int64) if q_lens is None else np.asarray(q_lens, np.int64)
     num_blocks = max(_pool_size(ctx, bs, pool_factor), 2)
@@ -438,7 +439,7 @@ def custom(name, *, seed, dtype, hq, hkv, d, ctx, q_lens=None, pool_factor=1.25,
                      partition_size=partition_size)
 
 
-def shared_prefix(name, *, seed, dtype, hq, hkv, d, groups, pool_factor=1.25) -> Step:
+def shared_prefix(name, *, seed, dtype, hq, hkv, d, groups, pool_factor=1.25, block_size=BLOCK_SIZE) -> Step:
     """Decode step whose sequences share prefixes in groups.
 
     ``groups`` is a list of (prefix_len, [context lengths of the members]).
@@ -451,7 +452,7 @@ def shared_prefix(name, *, seed, dtype, hq, hkv, d, groups, pool_factor=1.25) ->
     drawn once.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
-    bs = BLOCK_SIZE
+    bs = block_size
     ctx = np.asarray([c for _, members in groups for c in members], dtype=np.int32)
     starts = np.concatenate([[0], np.cumsum([len(m) for _, m in groups])]).astype(np.int32)
     plens = np.asarray([p for p, _ in groups], dtype=np.int32)

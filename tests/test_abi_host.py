@@ -44,7 +44,12 @@ def _status(fn, *args):
 def test_pool_bytes_and_geometry_checks():
     assert pkv.kv_pool_bytes(10, 16, 8, 128, pkv.BF16) == (10 * 8 * 16 * 128 * 2,) * 2
     assert pkv.kv_pool_bytes(3, 16, 1, 64, pkv.F32) == (3 * 16 * 64 * 4,) * 2
-    assert _status(pkv.kv_pool_bytes, 10, 32, 8, 128, pkv.BF16)[0] == -2   # block_size 32
+    # block_size 32: bf16 and e4m3 pools only
+    assert pkv.kv_pool_bytes(10, 32, 8, 128, pkv.BF16) == (10 * 8 * 32 * 128 * 2,) * 2
+    assert pkv.kv_pool_bytes(10, 32, 8, 64, pkv.FP8_E4M3) == (10 * 8 * 32 * 64,) * 2
+    assert _status(pkv.kv_pool_bytes, 10, 32, 8, 128, pkv.F32)[0] == -2
+    assert _status(pkv.kv_pool_bytes, 10, 64, 8, 128, pkv.BF16)[0] == -2
+    assert _status(pkv.kv_pool_bytes, 10, 8, 8, 128, pkv.BF16)[0] == -2
     assert _status(pkv.kv_pool_bytes, 10, 16, 8, 96, pkv.BF16)[0] == -2    # head_dim 96
     assert _status(pkv.kv_pool_bytes, 0, 16, 8, 128, pkv.BF16)[0] == -1
     assert _status(pkv.kv_pool_bytes, 10, 16, 8, 128, 7)[0] == -1

@@ -1,0 +1,152 @@
+"""GPU parity with 32-token blocks against the CPU oracle.
+
+The pages call sixteen tokens a common block size and note that thirty-two
+is often better on workloads dominated by very long generations ("The
+Serving Playbook", "The block table lives in the hottest kernel in the
+system"). bf16 and e4m3 pools take block_size 32. The pool layout is that of
+16-token blocks with 32 tokens per vector run: K [blocks][Hkv][D/x][32][x],
+V [blocks][Hkv][32][D].
+
+Bars: append bit-exact (bf16 bits; e4m3 codes against the oracle's encoder);
+attention |gpu - oracle| <= 2e-3 + 1e-2 |oracle| (bf16 queries and outputs,
+fp32 accumulation). Pools start NaN-filled and table entries past a
+sequence's last block point at a NaN block, so any read outside a sequence's
+tokens would show.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import fp8 as f8
+from paged_kv_decode_reshape_amd import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpu_harness import DevicePool, POISON_BITS, assert_close, to_f32
+
+BS = 32
+CTX = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 257, 700, 1500]
+
+
+def oracle_pools(step, k_scale=None, v_scale=None):
+    pk = oracle.new_pool(step.num_blocks, step.block_size, step.num_kv_heads, step.head_dim)
+    pv = oracle.new_pool(step.num_blocks, step.block_size, step.num_kv_heads, step.head_dim)
+    for key, value, slots in ((step.cached_key, step.cached_value, step.cached_slots),
+                              (step.new_key, step.new_value, step.new_slots)):
+        k, v = key.f32, value.f32
+        if k_scale is not None:
+            k, v = f8.quantize_dequantize(k, k_scale), f8.quantize_dequantize(v, v_scale)
+        oracle.append(pk, pv, k, v, slots)
+    return pk, pv
+
+
+def make_pool(step, kv, ks=1.0 / 96, vs=1.0 / 32):
+    if kv == "fp8":
+        pool = DevicePool(step, kv="fp8", k_scales=[ks], v_scales=[vs])
+    else:
+        pool = DevicePool(step)
+    pool.fill()
+    return pool
+
+
+@pytest.mark.parametrize("kv,d", [("bf16", 128), ("bf16", 64), ("fp8", 128), ("fp8", 64)])
+def test_block32_append_bit_exact(kv, d):
+    step = W.custom(f"b32app_{kv}_{d}", seed=1100 + d, dtype="bf16", hq=4, hkv=2, d=d,
+                    ctx=[1, 16, 31, 32, 33, 100], block_size=BS)
+    step.cached_slots = step.cached_slots.copy()
+    step.cached_slots[::5] = -1                        # negative slots are skipped
+    ks, vs = 1.0 / 96, 1.0 / 32
+    pool = make_pool(step, kv, ks, vs)
+    kbits, vbits = pool.decode_pool()
+    ref_k = np.full(kbits.shape, POISON_BITS[kv], dtype=kbits.dtype)
+    ref_v = np.full(vbits.shape, POISON_BITS[kv], dtype=vbits.dtype)
+    for vk, vv, slots in ((step.cached_key, step.cached_value, step.cached_slots),
+                          (step.new_key, step.new_value, step.new_slots)):
+        keep = slots >= 0
+        blk, off = slots[keep] // BS, slots[keep] % BS
+        if kv == "fp8":
+            ref_k[blk, off] = f8.fp8_e4m3_encode(vk.f32[keep], np.float32(1) / np.float32(ks))
+            ref_v[blk, off] = f8.fp8_e4m3_encode(vv.f32[keep], np.float32(1) / np.float32(vs))
+        else:
+            ref_k[blk, off] = vk.bits[keep]
+            ref_v[blk, off] = vv.bits[keep]
+    assert np.array_equal(kbits, ref_k), "K slots differ"
+    assert np.array_equal(vbits, ref_v), "V slots differ"
+
+
+@pytest.mark.parametrize("kv,hq,hkv,d,part", [
+    ("bf16", 32, 8, 128, 0), ("bf16", 32, 8, 128, 64), ("bf16", 8, 1, 128, 512), ("bf16", 4, 4, 64, -1),
+    ("bf16", 12, 2, 128, 128), ("fp8", 32, 8, 128, 0), ("fp8", 6, 2, 64, 64), ("fp8", 64, 8, 128, 512)])
+def test_block32_decode(kv, hq, hkv, d, part):
+    step = W.custom(f"b32dec_{kv}_{hq}_{hkv}_{d}", seed=1200 + hq + d, dtype="bf16", hq=hq, hkv=hkv, d=d,
+                    ctx=CTX + [0], block_size=BS)
+    scales = (1.0 / 96, 1.0 / 32) if kv == "fp8" else (None, None)
+    pool = make_pool(step, kv)
+    out = to_f32(pool.decode(part))
+    torch.cuda.synchronize()
+    pk, pv = oracle_pools(step, *scales)
+    bt, cl = step.decode_inputs()
+    ref = oracle.paged_decode(step.decode_query.f32, pk, pv, bt, cl, step.scale)
+    assert_close(out, ref, "bf16", step.name)
+
+
+@pytest.mark.parametrize("kv,hq,hkv,d,tq,part", [
+    ("bf16", 32, 8, 128, 4, 0), ("bf16", 8, 8, 64, 16, 64), ("fp8", 32, 8, 128, 3, 0)])
+def test_block32_multi_query(kv, hq, hkv, d, tq, part):
+    ctx = [c for c in CTX if c >= tq]
+    step = W.custom(f"b32mq_{kv}_{tq}", seed=1300 + tq + d, dtype="bf16", hq=hq, hkv=hkv, d=d, ctx=ctx,
+                    q_lens=[tq] * len(ctx), block_size=BS)
+    scales = (1.0 / 96, 1.0 / 32) if kv == "fp8" else (None, None)
+    pool = make_pool(step, kv)
+    out = to_f32(pool.decode_multi(tq, part))
+    torch.cuda.synchronize()
+    pk, pv = oracle_pools(step, *scales)
+    bt, cl = step.prefill_inputs()
+    ref = oracle.paged_prefill_chunk(step.prefill_query.f32, step.cu_q_lens, pk, pv, bt, cl, step.scale)
+    assert_close(out, ref, "bf16", step.name)
+
+
+@pytest.mark.parametrize("kv,hq,hkv,d", [("bf16", 32, 8, 128), ("fp8", 8, 2, 64), ("bf16", 4, 1, 128)])
+def test_block32_prefill(kv, hq, hkv, d):
+    ctx = [1, 15, 33, 64, 100, 257, 300]
+    q_lens = [1, 15, 16, 17, 33, 100, 64]
+    step = W.custom(f"b32pf_{kv}_{hq}_{d}", seed=1400 + hq + d, dtype="bf16", hq=hq, hkv=hkv, d=d, ctx=ctx,
+                    q_lens=q_lens, block_size=BS)
+    scales = (1.0 / 96, 1.0 / 32) if kv == "fp8" else (None, None)
+    pool = make_pool(step, kv)
+    out = to_f32(pool.prefill())
+    torch.cuda.synchronize()
+    pk, pv = oracle_pools(step, *scales)
+    bt, cl = step.prefill_inputs()
+    ref = oracle.paged_prefill_chunk(step.prefill_query.f32, step.cu_q_lens, pk, pv, bt, cl, step.scale)
+    assert_close(out, ref, "bf16", step.name)
+
+
+@pytest.mark.parametrize("part", [0, 64])
+def test_block32_shared_prefix(part):
+    groups = [(40, [41, 60, 100]), (0, [5]), (130, [131 + 7 * i for i in range(9)]), (640, [641, 700, 1000])]
+    step = W.shared_prefix(f"b32sh_{part}", seed=1500 + part, dtype="bf16", hq=32, hkv=8, d=128, groups=groups,
+                           block_size=BS)
+    pool = make_pool(step, "bf16")
+    out = to_f32(pool.decode_shared(part))
+    torch.cuda.synchronize()
+    pk, pv = oracle_pools(step)
+    bt, cl = step.decode_inputs()
+    ref = oracle.paged_decode(step.decode_query.f32, pk, pv, bt, cl, step.scale)
+    assert_close(out, ref, "bf16", step.name)
+
+
+def test_block32_llama8b_step_sampled():
+    """The B = 256 lognormal step with 32-token blocks, in the launch
+    configuration bench.py --block-size 32 times, on sampled sequences."""
+    step = W.llama8b_continuous(block_size=BS)
+    pool = make_pool(step, "bf16")
+    out = to_f32(pool.decode(0))
+    torch.cuda.synchronize()
+    pk, pv = oracle_pools(step)
+    bt, cl = step.decode_inputs()
+    seqs = sorted({0, 1, 17, 100, 128, 200, 255, int(np.argmax(cl)), int(np.argmin(cl))})
+    ref = oracle.paged_decode(step.decode_query.f32, pk, pv, bt, cl, step.scale, seqs=seqs)
+    assert_close(out[seqs], ref[seqs], "bf16", step.name)
