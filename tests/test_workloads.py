@@ -66,3 +66,73 @@ def test_custom_with_prefill_and_empty():
     _check_step(step)
     assert step.cu_q_lens.tolist() == [0, 12, 45]
     assert step.decode_seqs.tolist() == [0, 1]
+
+
+def _check_shared_step(step):
+    """Sharing groups: members' tables agree on the whole prefix blocks, no
+    block outside them is listed twice, every slot is written once, and a
+    member's copy of a partly filled prefix block holds the prefix values."""
+    bs = step.block_size
+    gs, pl = step.info["group_starts"], step.info["prefix_lens"]
+    assert gs[0] == 0 and gs[-1] == len(step.context_lens) and (np.diff(gs) >= 0).all()
+    owners = {}
+    for k in range(len(pl)):
+        n_sh = int(pl[k]) // bs
+        rows = step.block_tables[gs[k]:gs[k + 1]]
+        assert (rows[:, :n_sh] == rows[0, :n_sh]).all(), "members disagree on a shared block"
+        for i, s in enumerate(range(gs[k], gs[k + 1])):
+            c = int(step.context_lens[s])
+            assert c >= pl[k]
+            nb = W.blocks_needed(c, bs)
+            assert (step.block_tables[s, nb:] == step.poison_block).all()
+            for j, blk in enumerate(step.block_tables[s, :nb].tolist()):
+                key = (k, j) if j < n_sh else (k, s, j)
+                assert owners.setdefault(blk, key) == key, "a physical block is owned twice"
+    slots = np.concatenate([step.cached_slots, step.new_slots])
+    assert len(np.unique(slots)) == len(slots), "duplicate slot"
+    # whole shared blocks are written once, every member writes the rest of
+    # its context (a partly filled prefix block is copied per member);
+    # unique_tokens counts each logical prefix token once
+    stored = sum(int(pl[k]) // bs * bs + sum(int(c) - int(pl[k]) // bs * bs
+                                              for c in step.context_lens[gs[k]:gs[k + 1]])
+                 for k in range(len(pl)))
+    assert len(slots) == stored
+    assert step.info["unique_tokens"] == sum(int(pl[k]) + sum(int(c) - int(pl[k])
+                                                              for c in step.context_lens[gs[k]:gs[k + 1]])
+                                             for k in range(len(pl)))
+    # the values stored at each member's logical prefix positions agree
+    pos_val = {}
+    for vals, sl in ((step.cached_key.bits, step.cached_slots), (step.new_key.bits, step.new_slots)):
+        for x, slot in zip(vals, sl.tolist()):
+            pos_val[slot] = x
+    for k in range(len(pl)):
+        members = range(gs[k], gs[k + 1])
+        for p in range(int(pl[k])):
+            ref = None
+            for s in members:
+                slot = int(step.block_tables[s, p // bs]) * bs + p % bs
+                if ref is None:
+                    ref = pos_val[slot]
+                assert np.array_equal(pos_val[slot], ref), f"prefix position {p} differs in group {k}"
+
+
+def test_shared_prefix_generator():
+    groups = [(40, [41, 60, 100]), (0, [5]), (256, [256]), (33, [34, 35, 90]), (0, [0])]
+    for bs in (16, 32):
+        step = W.shared_prefix(f"sh{bs}", seed=5, dtype="bf16", hq=8, hkv=2, d=64, groups=groups,
+                               block_size=bs)
+        assert step.block_size == bs
+        _check_shared_step(step)
+
+
+def test_parallel_sampling_shape():
+    step = W.parallel_sampling(prompts=4, samples=8, prompt_len=2000, max_new=64)
+    assert len(step.context_lens) == 32 and (step.info["prefix_lens"] == 2000).all()
+    assert ((step.context_lens > 2000) & (step.context_lens <= 2064)).all()
+    _check_shared_step(step)
+
+
+def test_block32_churn_step():
+    step = W.llama8b_continuous(block_size=32)
+    assert step.block_size == 32 and step.name.endswith("_bs32")
+    _check_step(step)
