@@ -331,4 +331,30 @@ def pin_copy_on_write_fork(orc):
     assert np.array_equal(orc.gather(pk, np.array([3, 7]), 32), prompt_k[:32])
 
 
+def pin_block_size_32_matches_sdpa(orc):
+    """With 32-token blocks the oracle's decode and chunk attention equal
+    torch float64 SDPA on the unpaged K/V, exactly as with 16-token blocks."""
+    for bs in (32, 16):
+        step = W.custom(f"pin32_{bs}", seed=23, dtype="f32", hq=6, hkv=2, d=16,
+                        ctx=[1, 2, 31, 32, 33, 64, 65, 150], block_size=bs)
+        pk, pv = oracle_pools(orc, step)
+        assert pk.shape[1] == bs
+        bt, cl = step.decode_inputs()
+        out = orc.paged_decode(step.decode_query.f32, pk, pv, bt, cl, step.scale)
+        for b in range(len(cl)):
+            k, v = contiguous_kv(step, b)
+            ref = torch_sdpa(step.decode_query.f32[b:b + 1], k, v, step.scale)[0]
+            np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12)
+    step = W.custom("pin32_chunk", seed=24, dtype="f32", hq=4, hkv=1, d=16, ctx=[33, 70, 64],
+                    q_lens=[33, 5, 32], block_size=32)
+    pk, pv = oracle_pools(orc, step)
+    bt, cl = step.prefill_inputs()
+    out = orc.paged_prefill_chunk(step.prefill_query.f32, step.cu_q_lens, pk, pv, bt, cl, step.scale)
+    for i, s in enumerate(step.prefill_seqs):
+        k, v = contiguous_kv(step, int(s))
+        lo, hi = int(step.cu_q_lens[i]), int(step.cu_q_lens[i + 1])
+        ref = torch_sdpa(step.prefill_query.f32[lo:hi], k, v, step.scale, causal_offset=len(k) - (hi - lo))
+        np.testing.assert_allclose(out[lo:hi], ref, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
