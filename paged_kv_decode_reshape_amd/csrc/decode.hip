@@ -1102,7 +1102,7 @@ __device__ __forceinline__ void write_rows_shared(typename IoType<T>::type* out_
   const size_t row = (qh0 + col) * max_parts;
   const float2* ml = reinterpret_cast<const float2*>(pre_ml) + row;
   const float* ob = pre_o + row * D + 4 * quad;
-#pragma unroll 2
+#pragma unroll 1
   for (int p = 0; p < nsh; ++p) {
     const float2 sm = ml[p];
     const float mn = fmaxf(m, sm.x);
@@ -1160,7 +1160,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
           const float4* o4 = reinterpret_cast<const float4*>(prm.pre_o + qh * prm.max_parts * D) + i % (D / 4);
           float m = -INFINITY, l = 0.f;
           float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+#pragma unroll 1
           for (int p = 0; p < nsh; ++p) merge_state(m, l, acc, ml[p].x, ml[p].y, o4[(size_t)p * (D / 4)]);
           store_row4<TQ>(out_ptr + qh * D + (size_t)(i % (D / 4)) * 4, acc, 1.0f / l);
         }
