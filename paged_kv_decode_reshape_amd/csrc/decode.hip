@@ -869,11 +869,21 @@ __device__ __forceinline__ int find_group(const int32_t* __restrict__ gs, int nu
   return lo;
 }
 
+// Group k's first sequence and one past its last, kept inside the batch even
+// if group_starts breaks its contract.
+__device__ __forceinline__ int group_begin(const DecodeParams& prm, int k) {
+  return min(max(prm.group_starts[k], 0), prm.num_seqs);
+}
+__device__ __forceinline__ int group_end(const DecodeParams& prm, int k) {
+  return min(max(prm.group_starts[k + 1], group_begin(prm, k)), prm.num_seqs);
+}
+
 // Shared region of group k: its prefix, limited to the first member's context
 // (whose table supplies the block ids), rounded down to whole 64-token windows.
 __device__ __forceinline__ int group_shared_tokens(const int32_t* __restrict__ context_lens,
                                                    const DecodeParams& prm, int k) {
-  const int plen = min(max(prm.prefix_lens[k], 0), max(context_lens[prm.group_starts[k]], 0));
+  const int first = min(group_begin(prm, k), prm.num_seqs - 1);   // an empty group has no members to use it
+  const int plen = min(max(prm.prefix_lens[k], 0), max(context_lens[first], 0));
   return plen / 64 * 64;
 }
 
@@ -908,8 +918,8 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   if (prev >= prm.max_parts) return;
   const int part = prm.max_parts - 1 - (int)prev;
 
-  const int seq0 = prm.group_starts[k];
-  const int members = prm.group_starts[k + 1] - seq0;
+  const int seq0 = group_begin(prm, k);
+  const int members = group_end(prm, k) - seq0;
   const int m0 = mt * MPW;
   if (m0 >= members) return;
   const int nm = min(MPW, members - m0);

@@ -134,3 +134,23 @@ def test_parallel_sampling_step_sampled():
     seqs = sorted({0, 1, 7, 8, 100, 131, 200, 255})
     ref = oracle_decode(step, seqs=seqs)
     assert_close(out[seqs], ref[seqs], "bf16", step.name)
+
+
+def test_shared_empty_groups():
+    """Empty groups (equal consecutive group starts), first and last among
+    them, with large prefix lengths, change nothing: they have no members."""
+    step = shared_step("sh_empty", 964, 32, 8, 128)
+    gs, pl = step.info["group_starts"], step.info["prefix_lens"]
+    new_gs, new_pl = [0], []
+    for k in range(len(pl)):
+        new_gs.append(int(gs[k]))                       # an empty group before each real one
+        new_pl.append(4096)
+        new_gs.append(int(gs[k + 1]))
+        new_pl.append(int(pl[k]))
+    new_gs.append(int(gs[-1]))                          # and an empty group at the end
+    new_pl.append(4096)
+    pool = DevicePool(step)
+    pool.fill()
+    out = to_f32(pool.decode_shared(64, groups=new_gs, prefix_lens=new_pl))
+    torch.cuda.synchronize()
+    assert_close(out, oracle_decode(step), "bf16", step.name)
