@@ -1348,6 +1348,159 @@ __global__ __launch_bounds__(256) void decode_balanced_reduce_kernel(
   }
 }
 
+// The same combine for launches with few, long rows (long contexts split over
+// dozens of waves each): one workgroup per four partition waves i (and one
+// query row of the sequence; grid y); for each split (b, h) row whose first piece (w0 == 0) one
+// of those waves holds, combine the pieces held by waves i..last with the
+// online-softmax rule, per query head:
+//   M = max m,  L = sum 2^(m - M) l,  out = sum 2^(m - M) o / L.
+// Pieces after the first sit in slot 0 of each later wave with a non-empty
+// share, so the piece list follows from the share arithmetic and the loads of
+// different pieces are independent: a lane owns 16-byte slices of the G x D
+// output and walks the pieces kPieces at a time, all their loads in flight
+// together, rescaling its running sums as the maximum grows. A row of few
+// pieces is combined by the wave holding its first piece; a long one by all
+// four waves of the workgroup, each taking every fourth group of pieces, their
+// states merged in LDS.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void decode_balanced_reduce_coop_kernel(
+    T* __restrict__ out_ptr, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+    const SlotDesc* __restrict__ ws_desc, DecodeParams prm) {
+  constexpr int kSlices = G * D / 4;                       // float4 slices of one piece
+  constexpr int NF = (kSlices + kWave - 1) / kWave;        // slices per lane
+  constexpr int kPieces = NF >= 4 ? 2 : 8 / NF;            // pieces loaded together
+  constexpr int kCoopMin = 16;                             // pieces after the first from which the
+                                                           // workgroup's four waves share a row
+  __shared__ float4 sh_acc[4][NF * kWave];
+  __shared__ float2 sh_ml[4][NF * kWave];
+  const int lane = threadIdx.x & 63;
+  const int w4 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long nw = prm.num_waves;
+  const long wbase = (long)blockIdx.x * 4;
+  if (wbase >= nw) return;                                 // the whole workgroup
+  const float2* ml = reinterpret_cast<const float2*>(ws_ml);
+  const float4* wo = reinterpret_cast<const float4*>(ws_o);
+  const int nq = prm.q_per_seq;
+  const int qr = blockIdx.y;                               // query row of the sequence (grid y: one per row)
+  // The rows whose first piece the workgroup's waves hold, in one order for
+  // all four waves: a row with few pieces is combined by its own wave, a row
+  // with many by all four (every fourth group of pieces each), merged in LDS.
+  // The workgroup's eight slot descriptors, one per lane 0..7, loaded together.
+  int d_row = -1, d_w0 = 1, d_start = 0, d_windows = 0, d_total = 0;
+  if (lane < 8 && wbase + lane / 2 < nw) {
+    const SlotDesc dd = ws_desc[wbase * 2 + lane];
+    d_row = dd.row;
+    d_w0 = dd.w0;
+    d_start = dd.row_start;
+    d_windows = dd.row_windows;
+    d_total = dd.total;
+  }
+  for (int r = 0; r < 8; ++r) {
+    const long owner = wbase + r / 2;
+    if (owner >= nw) break;
+    const int row = __builtin_amdgcn_readlane(d_row, r);
+    if (row < 0 || __builtin_amdgcn_readlane(d_w0, r) != 0) continue;
+    const int total = __builtin_amdgcn_readlane(d_total, r);
+    const int row_windows = __builtin_amdgcn_readlane(d_windows, r);
+    // A row spans about row_windows * nw / total waves: only a long one can be
+    // shared, and the other waves skip the rest without a division.
+    const bool long_row = (long)row_windows * nw >= (long)(kCoopMin + 2) * total;
+    if (!long_row && w4 != r / 2) continue;
+    const long last = share_of((long)__builtin_amdgcn_readlane(d_start, r) + row_windows - 1, nw, total);
+    const bool coop = long_row && last - owner >= kCoopMin;   // uniform over the workgroup
+    if (!coop && w4 != r / 2) continue;
+    // Lane slice f = lane + 64 j covers head f / (D/4), dims 4 (f % (D/4)) .. +4.
+    float m[NF], l[NF];
+    float4 acc[NF];
+    if (!coop || w4 == 0) {
+      // The first piece: it holds key 0, which every query row sees.
+      const size_t row0 = ((size_t)(owner * 2 + (r & 1)) * nq + qr) * G;
+#pragma unroll
+      for (int j = 0; j < NF; ++j) {
+        const int f = min(lane + kWave * j, kSlices - 1);
+        const float2 sm = ml[row0 + f / (D / 4)];
+        m[j] = sm.x;
+        l[j] = sm.y;
+        acc[j] = wo[row0 * (D / 4) + f];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NF; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+        acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    const long stride = coop ? 4 * kPieces : kPieces;
+    for (long i0 = owner + 1 + (coop ? (long)w4 * kPieces : 0); i0 <= last; i0 += stride) {
+      float2 sm[kPieces][NF];
+      float4 ov[kPieces][NF];
+      bool live[kPieces];
+#pragma unroll
+      for (int u = 0; u < kPieces; ++u) {
+        const long i = min(i0 + u, last);
+        live[u] = (i0 + u <= last) && share_begin(i, nw, total) != share_begin(i + 1, nw, total);
+        const size_t rowi = ((size_t)i * 2 * nq + qr) * G;   // slot 0 of wave i, row qr
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const int f = min(lane + kWave * j, kSlices - 1);
+          sm[u][j] = ml[rowi + f / (D / 4)];
+          ov[u][j] = wo[rowi * (D / 4) + f];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kPieces; ++u) {
+        if (!live[u]) continue;                            // wave-uniform: empty share or past the end
+#pragma unroll
+        for (int j = 0; j < NF; ++j) merge_state(m[j], l[j], acc[j], sm[u][j].x, sm[u][j].y, ov[u][j]);
+      }
+    }
+    if (coop) {
+#pragma unroll
+      for (int j = 0; j < NF; ++j) {
+        sh_ml[w4][lane + kWave * j] = make_float2(m[j], l[j]);
+        sh_acc[w4][lane + kWave * j] = acc[j];
+      }
+      __syncthreads();
+      if (w4 == 0) {
+        for (int w = 1; w < 4; ++w) {
+#pragma unroll
+          for (int j = 0; j < NF; ++j) {
+            const float2 o = sh_ml[w][lane + kWave * j];
+            merge_state(m[j], l[j], acc[j], o.x, o.y, sh_acc[w][lane + kWave * j]);
+          }
+        }
+      }
+      __syncthreads();                                     // the LDS is free for the next row
+      if (w4 != 0) continue;
+    }
+    const int b = row / prm.num_kv_heads, h = row % prm.num_kv_heads;
+    if (prm.shared_start != nullptr) {
+      // Shared prefixes (one query row): the row's shared partitions, summaries
+      // in the fixed-partition layout with o already times the V scale.
+      const int nsh = (prm.shared_start[b] + prm.part_tokens - 1) / prm.part_tokens;
+      const size_t qh0 = (size_t)b * prm.num_kv_heads * G + (size_t)h * G;
+#pragma unroll 2
+      for (int p = 0; p < nsh; ++p) {
+#pragma unroll
+        for (int j = 0; j < NF; ++j) {
+          const int f = min(lane + kWave * j, kSlices - 1);
+          const size_t qh = qh0 + f / (D / 4);
+          const float2 sm = reinterpret_cast<const float2*>(prm.pre_ml)[qh * prm.max_parts + p];
+          const float4 ov = reinterpret_cast<const float4*>(prm.pre_o + (qh * prm.max_parts + p) * D)[f % (D / 4)];
+          merge_state(m[j], l[j], acc[j], sm.x, sm.y, ov);
+        }
+      }
+    }
+    T* out = out_ptr + (((size_t)b * nq + qr) * prm.num_kv_heads * G + (size_t)h * G) * D;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int f = lane + kWave * j;
+      if (f < kSlices) store_row4<T>(out + (size_t)f * 4, acc[j], 1.0f / l[j]);
+    }
+  }
+}
+
 template <typename T, int D, int G, bool MQ, int BS>
 hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
   using TQ = typename IoType<T>::type;
@@ -1388,9 +1541,15 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
     timer.end(KernelKind::kDecodePartition, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     timer.begin(KernelKind::kDecodeReduce, stream);
-    hipLaunchKernelGGL((decode_balanced_reduce_kernel<TQ, D, G>),
-                       dim3((unsigned)((prm.num_waves + 3) / 4), (unsigned)prm.q_per_seq), dim3(256), 0, stream,
-                       out, prm.ws_ml, prm.ws_o, desc, prm);
+    const dim3 rgrid((unsigned)((prm.num_waves + 3) / 4), (unsigned)prm.q_per_seq);
+    if ((long)prm.num_seqs * prm.num_kv_heads * 8 <= prm.num_waves) {
+      // Few rows for many waves: each row spans about eight or more waves.
+      hipLaunchKernelGGL((decode_balanced_reduce_coop_kernel<TQ, D, G>), rgrid, dim3(256), 0, stream, out,
+                         prm.ws_ml, prm.ws_o, desc, prm);
+    } else {
+      hipLaunchKernelGGL((decode_balanced_reduce_kernel<TQ, D, G>), rgrid, dim3(256), 0, stream, out, prm.ws_ml,
+                         prm.ws_o, desc, prm);
+    }
     timer.end(KernelKind::kDecodeReduce, stream);
     return hipGetLastError();
   }

@@ -95,6 +95,14 @@ def test_decode_long_context_split():
     run_and_check(step)
 
 
+def test_decode_long_context_balanced():
+    """The 8 x 32768-token step with the default balanced split: 64 rows over
+    the GPU's resident waves, each row combined from dozens of pieces by the
+    workgroup-shared reduction."""
+    step = W.long_context()
+    run_and_check(step, partition_size=0)
+
+
 def test_decode_mixed_step_decode_part():
     step = W.mixed_chunked_prefill()
     run_and_check(step, seqs=list(range(0, 128, 5)))
