@@ -62,10 +62,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def make_step(config: int, block_size: int = 16):
+def make_step(config: int, block_size: int = 16, qwen=(16, 512)):
     from paged_kv_decode_reshape_amd import workloads as W
     if block_size != 16 and config != 3:
         raise SystemExit("--block-size other than 16 is benchmarked on config 3")
+    if config == 2:
+        if tuple(qwen) not in W.QWEN_GRID:
+            raise SystemExit(f"--qwen-batch/--qwen-context {qwen} is not a point of the grid {W.QWEN_GRID}")
+        return W.qwen_layer(*qwen)
     if config == 3:
         return W.llama8b_continuous(block_size=block_size)
     if config == 4:
@@ -74,7 +78,7 @@ def make_step(config: int, block_size: int = 16):
         return W.mixed_chunked_prefill()
     if config == 6:
         return W.parallel_sampling()
-    raise SystemExit(f"--config {config}: the bench runs configs 3, 4, 5 or 6 (1 and 2 are parity cases)")
+    raise SystemExit(f"--config {config}: the bench runs configs 2 to 6 (1 is a parity case)")
 
 
 def multi_query_inputs(step, t: int, seed: int = 11):
@@ -196,6 +200,8 @@ def main():
                     help="cache storage: bf16 (the workload's dtype) or e4m3 codes")
     ap.add_argument("--queries-per-seq", type=int, default=1,
                     help="query rows per decoding sequence (> 1: speculative-verification step)")
+    ap.add_argument("--qwen-batch", type=int, default=16, help="--config 2: sequences (1, 4, 16, 64, 128)")
+    ap.add_argument("--qwen-context", type=int, default=512, help="--config 2: context (128, 512, 2048)")
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32),
                     help="tokens per pool block (32: config 3 only)")
     ap.add_argument("--shared", action="store_true",
@@ -225,7 +231,7 @@ def main():
         f"{props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB")
 
     t0 = time.time()
-    step = make_step(args.config, args.block_size)
+    step = make_step(args.config, args.block_size, (args.qwen_batch, args.qwen_context))
     s = step
     log(f"workload {s.name}: generated in {time.time() - t0:.1f}s; "
         f"{len(s.decode_seqs)} decode seqs, tokens {int(s.context_lens.sum())}, info {s.info}")
@@ -254,7 +260,12 @@ def main():
 
     # ---- pools: R replicas = R library layers ----
     kb, _ = pkv.kv_pool_bytes(s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim, dt_code)
-    reps = args.replicas or max(2, math.ceil(2 * 2**30 / (2 * kb)))
+    # Enough copies that the rotation spans >= 2 GiB, capped at 64: smaller
+    # pools then fit the 256 MB Infinity Cache together and the timing is warm
+    # (config.cache says which).
+    reps = args.replicas or min(64, max(2, math.ceil(2 * 2**30 / (2 * kb))))
+    cache_state = "cold (rotation >= 2 GiB)" if reps * 2 * kb >= 2 * 2**30 else "warm (rotation fits the Infinity Cache)" \
+        if reps * 2 * kb <= 256 * 2**20 else "partly warm"
     k_layers = [torch.empty(kb // pool_e, dtype=pool_dt, device=dev) for _ in range(reps)]
     v_layers = [torch.empty(kb // pool_e, dtype=pool_dt, device=dev) for _ in range(reps)]
     pool = pkv.kv_pool_create(reps, s.num_blocks, s.block_size, s.num_kv_heads, s.head_dim,
@@ -404,9 +415,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": s.dtype,
-        "data": ("synthetic (seeded N(0,1) values, 32 prompts x 8 samples sharing prompt blocks, "
-                 "uniform 1..512 generated tokens)" if "group_starts" in s.info else
-                 "synthetic (seeded N(0,1) values, lognormal lengths, churned block tables)"),
+        "data": {2: "synthetic (seeded N(0,1) values, uniform context, blocks scattered by a seeded permutation)",
+                 3: "synthetic (seeded N(0,1) values, lognormal lengths, churned block tables)",
+                 4: "synthetic (seeded N(0,1) values, 1% of K rows x8, blocks scattered by a seeded permutation)",
+                 5: "synthetic (seeded N(0,1) values, uniform 128..4096 decode contexts, one shared scattered pool)",
+                 6: "synthetic (seeded N(0,1) values, 32 prompts x 8 samples sharing prompt blocks, "
+                    "uniform 1..512 generated tokens)"}[args.config],
         "config": {
             "workload": s.name if tq == 1 else f"{s.name}_q{tq}",
             "batch": nseq,
@@ -417,6 +431,7 @@ def main():
             "kv_cache_dtype": "fp8_e4m3" if kvd == "fp8" else s.dtype,
             "queries_per_seq": tq,
             "shared_prefix_decode": shared,
+            "cache": cache_state,
             "pool_replicas": reps,
             "parallelism": "single GPU",
         },
