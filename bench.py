@@ -204,6 +204,8 @@ def main():
     ap.add_argument("--qwen-context", type=int, default=512, help="--config 2: context (128, 512, 2048)")
     ap.add_argument("--block-size", type=int, default=16, choices=(16, 32),
                     help="tokens per pool block (32: config 3 only)")
+    ap.add_argument("--fused-append", action="store_true",
+                    help="append and decode in one call (paged_attention_decode_append)")
     ap.add_argument("--shared", action="store_true",
                     help="decode through paged_attention_decode_shared with the step's sharing groups "
                          "(--config 6)")
@@ -242,6 +244,9 @@ def main():
     if tq < 1:
         raise SystemExit("--queries-per-seq must be >= 1")
     shared = bool(args.shared)
+    fused = bool(args.fused_append)
+    if fused and (shared or tq != 1 or s.cu_q_lens is not None):
+        raise SystemExit("--fused-append takes a decode-only step with one query row per sequence")
     if shared and ("group_starts" not in s.info or tq != 1):
         raise SystemExit("--shared needs a workload with sharing groups (--config 6) and one query per sequence")
     ab = algorithmic_bytes(s, kvd, tq, shared)
@@ -293,6 +298,9 @@ def main():
         n_new = len(s.new_slots)
         q_d = dev_vals(s.decode_query)
     out = torch.empty((nseq * tq, s.num_q_heads, s.head_dim), dtype=tdt, device=dev)
+    if fused:
+        # the new rows are in sequence order: every decoding sequence appends one token
+        assert len(s.new_slots) == nseq and (cl > 0).all()
     part = s.partition_size if args.partition_size is None else args.partition_size
     if shared:
         gs_d, pl_d = dev_int(s.info["group_starts"]), dev_int(s.info["prefix_lens"])
@@ -316,6 +324,10 @@ def main():
     def one_step(i):
         layer = i % reps
         stream = torch.cuda.current_stream(dev)     # the capture stream while a graph is recorded
+        if fused:
+            pkv.paged_attention_decode_append(pool, layer, out, q_d, new_k, new_v, bt_d, cl_d, nseq, s.num_q_heads,
+                                              bt.shape[1], s.scale, part, ws, wsb, stream)
+            return
         pkv.reshape_and_cache(pool, layer, new_k, new_v, new_slots, n_new, stream)
         if shared:
             pkv.paged_attention_decode_shared(pool, layer, out, q_d, bt_d, cl_d, gs_d, pl_d, nseq, n_groups,
@@ -431,6 +443,7 @@ def main():
             "kv_cache_dtype": "fp8_e4m3" if kvd == "fp8" else s.dtype,
             "queries_per_seq": tq,
             "shared_prefix_decode": shared,
+            "fused_append": fused,
             "cache": cache_state,
             "pool_replicas": reps,
             "parallelism": "single GPU",
@@ -446,14 +459,15 @@ def main():
         "decode_attention_gbs": round(part_bytes / (decode_us * 1e-6) / 1e9, 1) if decode_us else None,
         "algorithmic_bytes": ab,
         "roofline": {
-            "kernel": "decode_prefix_kernel + decode_partition_kernel" if shared else "decode_partition_kernel",
+            "kernel": ("decode_prefix_kernel + decode_partition_kernel" if shared else
+                       "decode_partition_kernel (append fused)" if fused else "decode_partition_kernel"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (read_traffic(kvd) if tq == 1 and not shared and args.config == 3 and s.block_size == 16
-                        else None),
+            "traffic": (read_traffic(kvd) if tq == 1 and not shared and not fused and args.config == 3 and
+                        s.block_size == 16 else None),
             "algorithmic_bytes_per_launch": part_bytes,
         },
     }

@@ -190,6 +190,31 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
                                   int partition_size, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* Append and decode in one call, for latency-bound steps: the same result as
+ * reshape_and_cache of each sequence's new token at position
+ * context_lens[b] - 1 (slot block_tables[b][(ctx-1) / block_size] *
+ * block_size + (ctx-1) % block_size) followed by paged_attention_decode,
+ * with one kernel launch fewer. The wavefront whose segment ends a
+ * sequence's row writes that row's new K/V into the slot, in the form the
+ * pool stores (bf16 bits, or e4m3 codes quantized exactly as
+ * reshape_and_cache does), and waits for the stores before it reads the
+ * slot; outputs and pool contents are bit-identical to the two calls. The
+ * pages append the new token's K/V and then attend ("LLM 7", 3., "What the
+ * Cache Stores"), and note that at small batch the launches, not the work,
+ * set the step time ("The Serving Playbook", "CUDA graphs and the CPU you
+ * forgot about"). With partition_size < 0 a short-context step is one kernel.
+ * At large batch the two calls are faster: the extra work sits on the
+ * row-ending wave's critical path.
+ *   key, value: [num_seqs][num_kv_heads][head_dim], bf16, 16-byte aligned;
+ *     row b is written only when context_lens[b] >= 1.
+ *   Everything else: as for paged_attention_decode (same workspace size).
+ * bf16 and e4m3 pools; an fp32 pool gives PKV_ERR_UNSUPPORTED. */
+pkv_status paged_attention_decode_append(const pkv_pool* pool, int layer, void* out, const void* query,
+                                         const void* key, const void* value, const int32_t* block_tables,
+                                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                         int max_blocks_per_seq, float scale, int partition_size,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Decode with several query rows per sequence (speculative verification of
  * queries_per_seq - 1 draft tokens plus one, or a short chunk): sequence b's
  * queries_per_seq = T new tokens are already appended, so its cache holds

@@ -21,7 +21,7 @@ __all__ = [
     "KERNEL_DECODE_REDUCE", "KERNEL_PREFILL", "KERNEL_DECODE_PREFIX", "library_path", "load",
     "kv_pool_bytes", "kv_pool_create", "kv_pool_set_fp8_scales", "kv_pool_destroy",
     "reshape_and_cache", "copy_blocks",
-    "paged_attention_decode_workspace_bytes", "paged_attention_decode",
+    "paged_attention_decode_workspace_bytes", "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_multi_workspace_bytes", "paged_attention_decode_multi",
     "paged_attention_decode_shared_workspace_bytes", "paged_attention_decode_shared",
     "paged_attention_prefill_chunk", "pkv_timing_enable", "pkv_timing_disable",
@@ -56,6 +56,9 @@ _SIGNATURES = {
     "paged_attention_decode": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_int, c_int, c_int, c_float, c_int, c_void_p, c_size_t,
                                        c_void_p]),
+    "paged_attention_decode_append": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, c_void_p, c_int, c_int, c_int, c_float, c_int,
+                                              c_void_p, c_size_t, c_void_p]),
     "paged_attention_decode_multi_workspace_bytes": (c_int, [c_void_p, c_int, c_int, c_int, c_int, c_int,
                                                              _P(c_size_t)]),
     "paged_attention_decode_multi": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_void_p,
@@ -184,6 +187,16 @@ def paged_attention_decode(pool, layer, out, query, block_tables, context_lens, 
                                          _ptr(context_lens), num_seqs, num_q_heads,
                                          max_blocks_per_seq, float(scale), partition_size,
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def paged_attention_decode_append(pool, layer, out, query, key, value, block_tables, context_lens, num_seqs,
+                                  num_q_heads, max_blocks_per_seq, scale, partition_size=0,
+                                  workspace=None, workspace_bytes=0, stream=None):
+    _check(load().paged_attention_decode_append(pool, layer, _ptr(out), _ptr(query), _ptr(key), _ptr(value),
+                                                _ptr(block_tables), _ptr(context_lens), num_seqs,
+                                                num_q_heads, max_blocks_per_seq, float(scale),
+                                                partition_size, _ptr(workspace), workspace_bytes,
+                                                _stream(stream)))
 
 
 def paged_attention_decode_multi_workspace_bytes(pool, num_seqs, queries_per_seq, num_q_heads,

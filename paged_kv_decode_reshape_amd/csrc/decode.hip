@@ -176,6 +176,10 @@ struct DecodeArgs {
   float scale_log2;        // softmax scale * log2(e) (* the K scale of an e4m3 pool)
   float v_scale;           // e4m3 pools: the layer's V scale; else 1
   int nq;                  // query rows per sequence (1 for plain decode)
+  const void* new_key;     // fused append: [B][hkv][D] bf16 rows of position ctx - 1, or NULL
+  const void* new_value;
+  float k_inv_scale;       // e4m3 pools: 1 / the K and V scales, for the fused append
+  float v_inv_scale;
 };
 
 // Accumulate tokens [tok_begin, tok_end) of (b, h) into a fresh summary.
@@ -517,7 +521,8 @@ __device__ __forceinline__ mf_bf16x8 mf_fp8_half(const Vec16& v) {
 // step); off when other wavefronts of the workgroup read the same tiles.
 // BS: tokens per pool block (16 or 32); a 64-token window is 64 / BS blocks
 // and each 16-token MFMA tile lies inside one block.
-template <typename T, int D, int G, bool MQ, int BS, bool kStream = true>
+// AP: fused append (one query row per sequence).
+template <typename T, int D, int G, bool MQ, int BS, bool kStream = true, bool AP = false>
 __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, MfmaWaveLds<D>& lds, int b, int h,
                                                             int tok_begin, int tok_end, int ctx, int& done,
                                                             int share, int qrow0) {
@@ -577,6 +582,33 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
   const uint32_t v_lane = (uint32_t)(v_row * D * (int)sizeof(T) + v_vec * 16);
   const int vkey = 4 * quad + (col >> 2), vcol = 4 * (col & 3);   // transposed V read of this lane
 
+  // Fused append: the segment that ends the row writes the new token's K and
+  // V (position ctx - 1) into their slot, in the form the pool stores; before
+  // loading the window that holds the slot it waits for those stores. No
+  // other wavefront reads this (block, head) tile in the launch.
+  static_assert(!(AP && MQ), "the fused append takes one query row per sequence");
+  bool append_pending = false;
+  if constexpr (AP) {
+    if (tok_end == ctx && ctx > 0) {                    // wave-uniform
+      constexpr int NVEC = D * (int)sizeof(T) / 16;     // 16-byte pool vectors per token row
+      constexpr int EPV = 16 / (int)sizeof(T);          // elements per vector
+      const int pn = ctx - 1;
+      const int blk = bt[nblk - 1];                     // the segment's last block holds position pn
+      const int off = pn % BS;
+      if (lane < 2 * NVEC) {
+        const bool is_v = lane >= NVEC;
+        const int vec = lane % NVEC;
+        const size_t row = ((size_t)b * a.hkv + h) * D + (size_t)vec * EPV;
+        const uint16_t* src = static_cast<const uint16_t*>(is_v ? a.new_value : a.new_key) + row;
+        const Vec16 v = kF8 ? quantize16(src, is_v ? a.v_inv_scale : a.k_inv_scale) : ld16(src);
+        char* dst = const_cast<char*>(is_v ? vbase : kbase) + (size_t)blk * blk_bytes +
+                    (is_v ? (size_t)off * D * sizeof(T) + (size_t)vec * 16 : ((size_t)vec * BS + off) * 16);
+        st16(dst, v);
+      }
+      append_pending = true;
+    }
+  }
+
   MfmaSummary<D> st;
   st.m = -INFINITY;
   st.l = 0.f;
@@ -593,6 +625,11 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
     int bid[4];                                         // block of the window's 16-token tile r
 #pragma unroll
     for (int r = 0; r < 4; ++r) bid[r] = __builtin_amdgcn_readlane(ids, min(lb + 16 * r / BS, nblk - 1) & 63);
+    if constexpr (AP) {
+      // vmcnt(0) before the window holding the appended slot: the stores have
+      // completed; the memory clobber keeps the loads below the wait.
+      if (append_pending && t0 + TPW >= tok_end) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
 
     // ---- loads: the window's K fragments and V rows ----
     Vec16 kr[4][KL];
@@ -771,14 +808,14 @@ struct UsesMfma {
 template <typename T, int D, int G>
 using SegLds = typename std::conditional<UsesMfma<T>::value, MfmaWaveLds<D>, WaveLds<T, D, G>>::type;
 
-template <typename T, int D, int G, bool MQ, int BS>
+template <typename T, int D, int G, bool MQ, int BS, bool AP = false>
 __device__ __forceinline__ auto run_seg(const DecodeArgs& a, SegLds<T, D, G>& lds, int b, int h, int tok_begin,
                                         int tok_end, int ctx, int& done, int share) {
   if constexpr (UsesMfma<T>::value) {
-    return run_segment_mfma<T, D, G, MQ, BS>(a, lds, b, h, tok_begin, tok_end, ctx, done, share,
-                                             b * (MQ ? a.nq : 1));
+    return run_segment_mfma<T, D, G, MQ, BS, true, AP>(a, lds, b, h, tok_begin, tok_end, ctx, done, share,
+                                                       b * (MQ ? a.nq : 1));
   } else {
-    static_assert(BS == kBlockSize, "lane-per-token segments take 16-token blocks");
+    static_assert(BS == kBlockSize && !AP, "lane-per-token segments: 16-token blocks, no fused append");
     return run_segment<T, D, G>(a, lds, b, h, tok_begin, tok_end, ctx, done, share);
   }
 }
@@ -794,7 +831,7 @@ constexpr int decode_waves_per_simd() {
 // ---------------------------------------------------------------------------
 // Fixed partitions: one wavefront per (b, h, partition).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G, bool MQ, int BS>
+template <typename T, int D, int G, bool MQ, int BS, bool AP>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_partition_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
@@ -833,7 +870,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   if (tok_begin >= ctx) return;
   const int tok_end = min(ctx, tok_begin + prm.part_tokens);
   int done = 0;
-  const auto st = run_seg<T, D, G, MQ, BS>(args, lds[wave], b, h, tok_begin, tok_end, ctx, done, 0);
+  const auto st = run_seg<T, D, G, MQ, BS, AP>(args, lds[wave], b, h, tok_begin, tok_end, ctx, done, 0);
   if (ctx <= prm.part_tokens) {
     write_rows<T, D, G>(out_row, st, args.v_scale, nq, hq);
   } else {
@@ -1139,7 +1176,7 @@ __device__ __forceinline__ void write_rows_shared(typename IoType<T>::type* out_
 
 // SH: the rows start after their shared partitions (decode_prefix_kernel has
 // run), and every row is merged with those partitions' summaries.
-template <typename T, int D, int G, bool MQ, bool SH, int BS>
+template <typename T, int D, int G, bool MQ, bool SH, int BS, bool AP>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_balanced_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     SlotDesc* __restrict__ ws_desc, const int32_t* __restrict__ context_lens, DecodeArgs args,
@@ -1208,7 +1245,8 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
     const int w0 = r % nwb;
     const int w1 = min(nwb, w0 + (x1 - x));
     const auto st =
-        run_seg<T, D, G, MQ, BS>(args, lds[wave], b, h, t0 + w0 * 64, min(ctx, t0 + w1 * 64), ctx, done, x1 - x0);
+        run_seg<T, D, G, MQ, BS, AP>(args, lds[wave], b, h, t0 + w0 * 64, min(ctx, t0 + w1 * 64), ctx, done,
+                                     x1 - x0);
     const int hq = args.hkv * G;
     const size_t qh0 = (size_t)b * nq * hq + (size_t)h * G;
     if (w0 == 0 && w1 == nwb) {
@@ -1505,7 +1543,8 @@ template <typename T, int D, int G, bool MQ, int BS>
 hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
   using TQ = typename IoType<T>::type;
   const DecodeArgs args{prm.query, prm.kpool, prm.vpool, prm.block_tables, prm.num_kv_heads,
-                        prm.max_blocks, prm.scale_log2, prm.v_scale, prm.q_per_seq};
+                        prm.max_blocks, prm.scale_log2, prm.v_scale, prm.q_per_seq,
+                        prm.new_key, prm.new_value, prm.k_inv_scale, prm.v_inv_scale};
   TQ* out = static_cast<TQ*>(prm.out);
   hipError_t err;
   // Shared prefixes: the groups' shared partitions first (they also record
@@ -1528,14 +1567,17 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
     const dim3 grid((unsigned)((prm.num_waves + 3) / 4));
     if constexpr (kShareable) {
       if (prm.shared_start != nullptr) {
-        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, true, BS>), grid, dim3(256), 0, stream, out,
+        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, true, BS, false>), grid, dim3(256), 0, stream, out,
+                           prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
+      } else if (prm.new_key != nullptr) {
+        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS, true>), grid, dim3(256), 0, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       } else {
-        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS>), grid, dim3(256), 0, stream, out,
+        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), 0, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       }
     } else {
-      hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS>), grid, dim3(256), 0, stream, out,
+      hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), 0, stream, out,
                          prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
     }
     timer.end(KernelKind::kDecodePartition, stream);
@@ -1555,8 +1597,18 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
   }
   const long units = (long)prm.num_kv_heads * prm.num_seqs * prm.max_parts;
   timer.begin(KernelKind::kDecodePartition, stream);
-  hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ, BS>), dim3((unsigned)((units + 3) / 4)), dim3(256),
-                     0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
+  bool fused = false;
+  if constexpr (kShareable) {
+    if (prm.new_key != nullptr) {
+      hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ, BS, true>), dim3((unsigned)((units + 3) / 4)),
+                         dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
+      fused = true;
+    }
+  }
+  if (!fused) {
+    hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ, BS, false>), dim3((unsigned)((units + 3) / 4)),
+                       dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
+  }
   timer.end(KernelKind::kDecodePartition, stream);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (prm.max_parts > 1) {
@@ -1592,7 +1644,7 @@ int balanced_waves_per_cu() {
   static int cached = 0;
   if (cached == 0) {
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ, false, kBlockSize>, 256, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ, false, kBlockSize, false>, 256, 0) !=
             hipSuccess ||
         blocks <= 0) {
       (void)hipGetLastError();

@@ -224,4 +224,19 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16 bf16 values at p, times inv_scale, as 16 e4m3 codes.
+__device__ __forceinline__ Vec16 quantize16(const uint16_t* p, float inv_scale) {
+  const Vec16 a = ld16(p), b = ld16(p + 8);
+  float f[16];
+  widen<uint16_t>(a, f);
+  widen<uint16_t>(b, f + 8);
+  Vec16 q;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = f32x2_to_fp8x2<false>(f[4 * i], f[4 * i + 1], inv_scale, 0u);
+    q.w[i] = f32x2_to_fp8x2<true>(f[4 * i + 2], f[4 * i + 3], inv_scale, w);
+  }
+  return q;
+}
+
 }  // namespace pkv

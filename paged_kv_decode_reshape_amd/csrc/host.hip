@@ -313,10 +313,13 @@ pkv_status decode_workspace(const pkv_pool* pool, int num_seqs, int q_per_seq, i
   return PKV_OK;
 }
 
+// new_key / new_value (both or neither): the fused append of
+// paged_attention_decode_append.
 pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* query, int q_per_seq,
                       const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
                       int num_q_heads, int max_blocks_per_seq, float scale, int partition_size,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      const void* new_key = nullptr, const void* new_value = nullptr) {
   pkv_status st = check_pool_layer(pool, layer);
   if (st != PKV_OK) return st;
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
@@ -339,6 +342,13 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
   if (!aligned(out, 16) || !aligned(query, 16)) return fail(PKV_ERR_INVALID_ARG, "out/query must be 16-byte aligned");
   if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
     return fail(PKV_ERR_INVALID_ARG, "block_tables/context_lens must be 4-byte aligned");
+  if (new_key || new_value) {
+    if (!new_key || !new_value) return fail(PKV_ERR_INVALID_ARG, "key and value must not be NULL");
+    if (!aligned(new_key, 16) || !aligned(new_value, 16))
+      return fail(PKV_ERR_INVALID_ARG, "key/value must be 16-byte aligned");
+    if (pool->dtype == PKV_F32)
+      return fail(PKV_ERR_UNSUPPORTED, "the fused append runs in the matrix-core decode: bf16 and e4m3 pools only");
+  }
   DecodeSplit sp;
   st = decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
   if (st != PKV_OK) return st;
@@ -371,7 +381,8 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
                         pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
                         num_waves, scale * 1.4426950408889634f * pool->k_scale[layer],
                         pool->v_scale[layer], q_per_seq, nullptr, nullptr, 0, 0, nullptr, nullptr, nullptr,
-                        pool->block_size};
+                        pool->block_size, new_key, new_value, 1.0f / pool->k_scale[layer],
+                        1.0f / pool->v_scale[layer]};
   (void)hipGetLastError();
   hipError_t err = pkv::launch_decode(prm, type, (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "paged_attention_decode launch");
@@ -560,6 +571,17 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
                                   size_t workspace_bytes, void* stream) {
   return decode_run(pool, layer, out, query, 1, block_tables, context_lens, num_seqs, num_q_heads,
                     max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+pkv_status paged_attention_decode_append(const pkv_pool* pool, int layer, void* out, const void* query,
+                                         const void* key, const void* value, const int32_t* block_tables,
+                                         const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                         int max_blocks_per_seq, float scale, int partition_size,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!pool) return fail(PKV_ERR_INVALID_ARG, "pool is NULL");
+  if (num_seqs > 0 && (!key || !value)) return fail(PKV_ERR_INVALID_ARG, "key and value must not be NULL");
+  return decode_run(pool, layer, out, query, 1, block_tables, context_lens, num_seqs, num_q_heads,
+                    max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, stream, key, value);
 }
 
 pkv_status paged_attention_decode_multi_workspace_bytes(const pkv_pool* pool, int num_seqs,

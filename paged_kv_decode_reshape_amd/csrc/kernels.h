@@ -72,6 +72,14 @@ struct DecodeParams {
   float* pre_ml;           // shared pieces' summaries: float2 [num_seqs][Hq][max_parts]
   float* pre_o;            // float [num_seqs][Hq][max_parts][D], unnormalized, times the V scale
   int block_size;          // tokens per pool block: 16, or 32 for bf16 and e4m3 pools
+  // Fused append (one query row per sequence, matrix-core segments; NULL
+  // otherwise): sequence b's new K/V rows [num_seqs][Hkv][D] (bf16) belong at
+  // position context_lens[b] - 1 and are written into the pool by the wave
+  // whose segment ends the row (e4m3 pools: quantized with the inverse scales).
+  const void* new_key;
+  const void* new_value;
+  float k_inv_scale;
+  float v_inv_scale;
 };
 
 struct PrefillParams {
