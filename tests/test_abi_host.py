@@ -191,3 +191,22 @@ def test_shared_prefix_decode_checks():
     finally:
         pkv.kv_pool_destroy(h)
         pkv.kv_pool_destroy(hf)
+
+
+def test_fused_append_decode_checks():
+    h = pkv.kv_pool_create(1, 64, 16, 8, 128, pkv.BF16, [256], [512])
+    hf = pkv.kv_pool_create(1, 64, 16, 8, 128, pkv.F32, [256], [512])
+    try:
+        args = (0, 16, 16)                       # layer, out, query
+        # key and value are required, 16-byte aligned
+        assert _status(pkv.paged_attention_decode_append, h, *args, None, 16, 16, 16, 4, 32, 4, 1.0)[0] == -1
+        assert _status(pkv.paged_attention_decode_append, h, *args, 16, 24, 16, 16, 4, 32, 4, 1.0)[0] == -1
+        # fp32 pools run the lane-per-token decode, which has no fused append
+        st, msg = _status(pkv.paged_attention_decode_append, hf, *args, 16, 16, 16, 16, 4, 32, 4, 1.0, -1)
+        assert st == -2 and "bf16" in msg
+        # the usual decode checks apply (heads not a multiple of KV heads)
+        assert _status(pkv.paged_attention_decode_append, h, *args, 16, 16, 16, 16, 4, 30, 4, 1.0)[0] == -1
+        pkv.paged_attention_decode_append(h, *args, 16, 16, 16, 16, 0, 32, 4, 1.0)   # no sequences: no-op
+    finally:
+        pkv.kv_pool_destroy(h)
+        pkv.kv_pool_destroy(hf)
