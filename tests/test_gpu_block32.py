@@ -24,6 +24,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
+    import full_refs
     from gpu_harness import DevicePool, POISON_BITS, assert_close, to_f32
 
 BS = 32
@@ -138,15 +139,11 @@ def test_block32_shared_prefix(part):
     assert_close(out, ref, "bf16", step.name)
 
 
-def test_block32_llama8b_step_sampled():
+def test_block32_llama8b_step():
     """The B = 256 lognormal step with 32-token blocks, in the launch
-    configuration bench.py --block-size 32 times, on sampled sequences."""
-    step = W.llama8b_continuous(block_size=BS)
+    configuration bench.py --block-size 32 times, every output row."""
+    step = full_refs.step("llama8b_bs32")
     pool = make_pool(step, "bf16")
     out = to_f32(pool.decode(0))
     torch.cuda.synchronize()
-    pk, pv = oracle_pools(step)
-    bt, cl = step.decode_inputs()
-    seqs = sorted({0, 1, 17, 100, 128, 200, 255, int(np.argmax(cl)), int(np.argmin(cl))})
-    ref = oracle.paged_decode(step.decode_query.f32, pk, pv, bt, cl, step.scale, seqs=seqs)
-    assert_close(out[seqs], ref[seqs], "bf16", step.name)
+    assert_close(out, full_refs.decode_ref("llama8b_bs32"), "bf16", step.name)

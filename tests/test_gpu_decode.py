@@ -13,6 +13,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
+    import full_refs
     from gpu_harness import DevicePool, POISON_BITS, assert_close, int_tensor, to_device, to_f32
 
 
@@ -80,13 +81,21 @@ def test_decode_qwen_grid(batch, context):
     run_and_check(W.qwen_layer(batch, context))
 
 
-def test_decode_llama8b_b256_sampled():
-    step = W.llama8b_continuous()
-    rng = np.random.default_rng(0)
-    ctx = step.context_lens
-    longest = int(np.argmax(ctx))
-    seqs = sorted(set(rng.choice(len(ctx), 24, replace=False).tolist()) | {longest, int(np.argmin(ctx))})
-    run_and_check(step, seqs=seqs)
+def check_full(kind, partition_size=None):
+    """A full-size workload in the launch configuration bench.py times, every
+    output row against the oracle."""
+    step = full_refs.step(kind)
+    pool = DevicePool(step)
+    pool.fill()
+    out = to_f32(pool.decode(partition_size))
+    torch.cuda.synchronize()
+    return assert_close(out, full_refs.decode_ref(kind), step.dtype, step.name)
+
+
+def test_decode_llama8b_b256():
+    """B = 256 Llama-8B-shaped layer, lognormal contexts, churned block
+    tables, balanced split: all 256 x 32 output rows."""
+    check_full("llama8b")
 
 
 def test_decode_long_context_split():
@@ -104,8 +113,8 @@ def test_decode_long_context_balanced():
 
 
 def test_decode_mixed_step_decode_part():
-    step = W.mixed_chunked_prefill()
-    run_and_check(step, seqs=list(range(0, 128, 5)))
+    """The 128 decodes of the mixed chunked-prefill step, every row."""
+    check_full("mixed")
 
 
 # ---------------------------------------------------------------------------

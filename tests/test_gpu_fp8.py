@@ -19,6 +19,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
+    import full_refs
     from gpu_harness import DevicePool, POISON_BITS, assert_close, to_f32
 
 
@@ -123,14 +124,14 @@ def test_fp8_decode_unit_scales():
     check_decode(step, 1.0, 1.0)
 
 
-def test_fp8_decode_llama8b_b256_sampled():
-    """The B=256 lognormal-length Llama-8B layer with an e4m3 pool, sampled rows."""
-    step = W.llama8b_continuous()
-    ctx = step.context_lens
-    rng = np.random.default_rng(1)
-    seqs = sorted(set(rng.choice(len(ctx), 24, replace=False).tolist())
-                  | {int(np.argmax(ctx)), int(np.argmin(ctx))})
-    check_decode(step, 1.0 / 80, 1.0 / 80, seqs=seqs)
+def test_fp8_decode_llama8b_b256():
+    """The B=256 lognormal-length Llama-8B layer with an e4m3 pool (the
+    scales bench.py --kv-dtype fp8 uses), every output row."""
+    step = full_refs.step("llama8b")
+    pool = fp8_pool(step, 1.0 / 80, 1.0 / 80)
+    out = to_f32(pool.decode())
+    torch.cuda.synchronize()
+    assert_close(out, full_refs.decode_ref("llama8b", 1.0 / 80, 1.0 / 80), "bf16", step.name)
 
 
 # ---------------------------------------------------------------------------
@@ -158,8 +159,14 @@ def test_fp8_prefill_ragged_chunks(hq, hkv, d):
     check_prefill(step, 1.0 / 96, 1.0 / 32)
 
 
-def test_fp8_prefill_mixed_step_chunk_sampled():
-    """The 512-token chunk on 2048 cached tokens (Hq=32, Hkv=8, D=128), e4m3 pool."""
-    step = W.mixed_chunked_prefill()
-    rows = sorted(set(range(0, 512, 11)) | {0, 1, 15, 16, 17, 63, 64, 255, 256, 510, 511})
-    check_prefill(step, 1.0 / 80, 1.0 / 80, rows)
+def test_fp8_mixed_step():
+    """The mixed chunked-prefill step with an e4m3 pool: the 512-token chunk
+    and the 128 decodes, every output row."""
+    step = full_refs.step("mixed")
+    pool = fp8_pool(step, 1.0 / 80, 1.0 / 80)
+    dec = to_f32(pool.decode())
+    pre = to_f32(pool.prefill())
+    torch.cuda.synchronize()
+    ref_dec, ref_pre = full_refs.refs("mixed", 1.0 / 80, 1.0 / 80)
+    assert_close(dec, ref_dec, "bf16", step.name + " decode")
+    assert_close(pre, ref_pre, "bf16", step.name + " chunk")

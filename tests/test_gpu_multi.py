@@ -76,8 +76,9 @@ def test_multi_one_row_is_decode():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-def test_multi_llama8b_b256_lognormal_sampled():
-    """B=256 Llama-8B-shaped layer, lognormal contexts, 4 query rows each."""
+def test_multi_llama8b_b256_lognormal():
+    """B=256 Llama-8B-shaped layer, lognormal contexts, 4 query rows each:
+    every output row."""
     rng = np.random.default_rng(7)
     ctx = W.lognormal_lengths(rng, 256).astype(int).tolist()
     step = multi_step("mq_llama", 850, 32, 8, 128, 4, ctx)
@@ -85,7 +86,4 @@ def test_multi_llama8b_b256_lognormal_sampled():
     pool.fill()
     out = to_f32(pool.decode_multi(4, 0))
     torch.cuda.synchronize()
-    seqs = sorted(set(rng.choice(len(ctx), 12, replace=False).tolist()) | {int(np.argmax(ctx))})
-    rows = [4 * s + j for s in seqs for j in range(4)]
-    ref = oracle_multi(step, rows=rows)
-    assert_close(out[rows], ref[rows], "bf16", step.name)
+    assert_close(out, oracle_multi(step), "bf16", step.name)

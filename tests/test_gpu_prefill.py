@@ -12,6 +12,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
+    import full_refs
     from gpu_harness import DevicePool, assert_close, to_device, to_f32
 
 
@@ -35,11 +36,15 @@ def check(step, rows=None):
     return assert_close(out[idx], ref[idx], step.dtype, step.name)
 
 
-def test_prefill_mixed_step_chunk_sampled():
-    """The 512-token chunk on 2048 cached tokens (Hq=32, Hkv=8, D=128)."""
-    step = W.mixed_chunked_prefill()
-    rows = sorted(set(range(0, 512, 7)) | {0, 1, 15, 16, 17, 63, 64, 255, 256, 510, 511})
-    check(step, rows)
+def test_prefill_mixed_step_chunk():
+    """The 512-token chunk on 2048 cached tokens (Hq=32, Hkv=8, D=128): all
+    512 x 32 output rows."""
+    step = full_refs.step("mixed")
+    pool = DevicePool(step)
+    pool.fill()
+    out = to_f32(pool.prefill())
+    torch.cuda.synchronize()
+    assert_close(out, full_refs.prefill_ref("mixed"), step.dtype, step.name)
 
 
 @pytest.mark.parametrize("hq,hkv,d", [(4, 1, 128), (8, 2, 128), (8, 1, 64), (16, 2, 64), (2, 2, 128)])
