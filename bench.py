@@ -143,6 +143,49 @@ def read_traffic(kv_dtype: str):
         return None
 
 
+def host_description() -> dict:
+    """The host the CPU baseline runs on: CPU model, logical CPUs, the CPUs this
+    process may run on, and numpy's BLAS (vendor, version, thread pool)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = {}
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = {"vendor": i.get("internal_api"), "version": i.get("version"),
+                        "threads": i.get("num_threads")}
+                break
+    except Exception:
+        pass
+    if not blas:
+        try:
+            cfg = np.show_config(mode="dicts")
+            b = cfg["Build Dependencies"]["blas"]
+            blas = {"vendor": b.get("name"), "version": b.get("version"), "threads": None}
+        except Exception:
+            blas = {"vendor": "unknown"}
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas": blas}
+
+
+def percentiles(xs) -> dict:
+    a = np.asarray(xs, dtype=np.float64)
+    if a.size == 0:
+        return {}
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "mean": round(float(a.mean()), 2), "n": int(a.size)}
+
+
 def cpu_baseline(step, kv_dtype: str = "bf16", multi=None, min_seconds: float = 10.0, max_reps: int = 30):
     """The oracle, as it stands, on the same workload: append (with e4m3
     quantization for an fp8 cache) + decode (+ prefill), repeated until about
@@ -309,7 +352,7 @@ def main():
         wsb = pkv.paged_attention_decode_shared_workspace_bytes(pool, nseq, s.num_q_heads, bt.shape[1], part)
     else:
         wsb = pkv.paged_attention_decode_multi_workspace_bytes(pool, nseq, tq, s.num_q_heads, bt.shape[1], part)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=dev)
     has_prefill = s.cu_q_lens is not None
     if has_prefill:
         pbt, pcl = s.prefill_inputs()
@@ -360,8 +403,9 @@ def main():
     kinds_all = (("append", pkv.KERNEL_APPEND), ("partition", pkv.KERNEL_DECODE_PARTITION),
                  ("reduce", pkv.KERNEL_DECODE_REDUCE), ("prefill", pkv.KERNEL_PREFILL),
                  ("prefix", pkv.KERNEL_DECODE_PREFIX))
-    timed_kinds = [pkv.KERNEL_DECODE_PARTITION] + ([pkv.KERNEL_PREFILL] if has_prefill else []) + \
-        ([pkv.KERNEL_DECODE_PREFIX] if shared else [])
+    timed_kinds = [pkv.KERNEL_DECODE_PARTITION, pkv.KERNEL_DECODE_REDUCE] + \
+        ([pkv.KERNEL_PREFILL] if has_prefill else []) + ([pkv.KERNEL_DECODE_PREFIX] if shared else [])
+    launches = {}
     if args.graph:
         # One captured step per pool replica; step i replays graph i % reps.
         # Kernel durations then come from the separate eager pass below.
@@ -390,6 +434,8 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         kt = {name: pkv.pkv_timing_read(kind) for name, kind in kinds_all if kind in timed_kinds}
+        launches = {name: pkv.pkv_timing_read_launches(kind, 2 * args.steps + 8)
+                    for name, kind in kinds_all if kind in timed_kinds}
         pkv.pkv_timing_disable()
     # The other kernels' durations, from a separate untimed pass with events on
     # every kernel.
@@ -402,6 +448,20 @@ def main():
         if kind not in timed_kinds:
             kt[name] = pkv.pkv_timing_read(kind)
     pkv.pkv_timing_disable()
+    # Per-step durations: a separate pass of the same number of steps, with one
+    # event pair around every step on the launch stream (no library events),
+    # for the median and p10/p90.
+    stream_now = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream_now)
+        if args.graph:
+            graphs[i % reps].replay()
+        else:
+            one_step(args.warmup + i)
+        evs[i][1].record(stream_now)
+    torch.cuda.synchronize()
+    step_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
     ms_per_step = wall * 1e3 / args.steps
     avg_us = {k: (ms / n * 1e3 if n else 0.0) for k, (n, ms) in kt.items()}
     avg_us = {k: avg_us[k] for k, _ in kinds_all}
@@ -413,8 +473,21 @@ def main():
     # With shared prefixes the KV is read by two kernels (the groups' shared
     # partitions, then each sequence's own): the roofline covers both.
     read_us = avg_us["partition"] + avg_us["prefix"]
-    achieved = part_bytes / (read_us * 1e-6) / 1e9 if read_us else 0.0
     decode_us = read_us + avg_us["reduce"]
+    # The roofline covers the whole decode: the partition kernel(s) and, where
+    # split rows are combined by a second kernel, that reduction too.
+    achieved = part_bytes / (decode_us * 1e-6) / 1e9 if decode_us else 0.0
+    achieved_read = part_bytes / (read_us * 1e-6) / 1e9 if read_us else 0.0
+    balanced = (part == 0) and nseq <= 4096
+    if shared:
+        kernel_label = "decode_prefix_kernel + decode_balanced_kernel + decode_balanced_reduce_kernel"
+    elif balanced and not avg_us["reduce"]:
+        kernel_label = "decode_balanced_kernel (split rows combined in the launch" + \
+                       (", append fused)" if fused else ")")
+    elif balanced:
+        kernel_label = "decode_balanced_kernel + decode_balanced_reduce(_coop)_kernel"
+    else:
+        kernel_label = "decode_partition_kernel" + (" + decode_reduce_kernel" if avg_us["reduce"] else "")
     result = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) and us per layer-step",
         "value": round(value, 1),
@@ -452,15 +525,17 @@ def main():
         "us_per_layer_step": round(ms_per_step * 1e3, 2),
         "kernel_us": {k: round(v, 2) for k, v in avg_us.items()},
         "kernel_us_source": ("all kernels: a separate eager pass of " if args.graph else
-                             "partition" + (" and prefill" if has_prefill else "") +
+                             "decode partition and reduction" + (" and prefill" if has_prefill else "") +
                              ": HIP events in the timed region; the others: a separate ") +
                             f"{n_break}-step pass with events on every kernel",
+        "kernel_us_percentiles": {k: percentiles([x * 1e3 for x in v]) for k, v in launches.items() if v},
+        "step_us": dict(percentiles(step_us), source=f"a separate pass of {args.steps} steps, one HIP event "
+                                                     "pair around each step on the launch stream"),
         "graph": bool(args.graph),
         "decode_attention_gbs": round(part_bytes / (decode_us * 1e-6) / 1e9, 1) if decode_us else None,
         "algorithmic_bytes": ab,
         "roofline": {
-            "kernel": ("decode_prefix_kernel + decode_partition_kernel" if shared else
-                       "decode_partition_kernel (append fused)" if fused else "decode_partition_kernel"),
+            "kernel": kernel_label,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -469,6 +544,9 @@ def main():
             "traffic": (read_traffic(kvd) if tq == 1 and not shared and not fused and args.config == 3 and
                         s.block_size == 16 else None),
             "algorithmic_bytes_per_launch": part_bytes,
+            "decode_us": round(decode_us, 2),
+            "partition_only": {"achieved": round(achieved_read, 1),
+                               "frac": round(achieved_read / HBM_PEAK_GBS, 4), "us": round(read_us, 2)},
         },
     }
     if has_prefill and avg_us["prefill"]:
@@ -481,7 +559,7 @@ def main():
         t_cpu, runs, threads = cpu_baseline(s, kvd, multi)
         result["cpu_baseline"] = {
             "value": round(step_bytes / t_cpu / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_description(),
             "sample": f"the whole step ({s.name}{', e4m3 cache' if kvd == 'fp8' else ''}"
                       f"{f', {tq} query rows per sequence' if tq > 1 else ''}: append + decode of all {nseq} sequences"
                       f"{' + prefill chunk' if has_prefill else ''}), numpy float64, median of {runs} runs"

@@ -44,9 +44,9 @@
  *     slots < num_blocks*block_size, no two tokens of one call with the same
  *     slot (they would race).
  *   - Supported geometry: block_size 16, or 32 for bf16 and e4m3 pools (the
- *     pages call sixteen tokens a common block size and thirty-two often
- *     better when very long generations dominate: "The Serving Playbook",
- *     "The block table lives in the hottest kernel in the system"); head_dim
+ *     pages give 16 as the usual choice and favour 32 for traffic made mostly
+ *     of long generations: "The Serving Playbook", "The block table lives in
+ *     the hottest kernel in the system"); head_dim
  *     64 or 128; query heads per KV head (num_q_heads / num_kv_heads) from 1
  *     to 8.
  *
@@ -172,17 +172,25 @@ pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_
  *   partition_size: how the KV axis is split over wavefronts.
  *     0 (recommended): balanced split. The 64-token windows of all
  *       (sequence, KV head) rows are shared equally by one wavefront per
- *       resident wave slot of the GPU; rows cut between wavefronts leave
- *       partial (max, sum, output) summaries that a second kernel combines.
- *       The split is derived on the device from context_lens. Used for up
- *       to 4096 sequences; larger batches fall back to 512-token partitions.
+ *       resident wave slot of the GPU; a row cut between wavefronts leaves
+ *       partial (max, sum, output) summaries, and the wavefront that
+ *       finishes the row's last piece combines them in the same launch (a
+ *       completion counter per row, in the workspace). The split is derived
+ *       on the device from context_lens. Used for up to 4096 sequences;
+ *       larger batches fall back to 512-token partitions.
  *     > 0: fixed partitions of that many tokens (a multiple of 64); a
  *       sequence longer than one partition is combined by a second kernel.
  *     < 0: never split (one wavefront per (sequence, KV head)).
  *   workspace: device memory of at least
  *     paged_attention_decode_workspace_bytes(...) bytes (may be NULL when
- *     that is 0), 16-byte aligned. Contents on entry are ignored; calls that
- *     share a workspace must be ordered (same stream). */
+ *     that is 0), 16-byte aligned. Its first 16 KiB hold completion
+ *     counters (one int32 per balanced-split wavefront): they must be zero
+ *     before the workspace's first use (allocate it zero-filled), and every
+ *     call that completes leaves them zero again, so one workspace serves any
+ *     sequence of decode calls of any variant (plain, _append, _multi,
+ *     _shared) and sizes up to its length. The rest of the workspace is
+ *     scratch whose contents on entry are ignored. Calls that share a
+ *     workspace must be ordered (same stream). */
 pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
                                   const void* query, const int32_t* block_tables,
                                   const int32_t* context_lens, int num_seqs,
@@ -247,9 +255,9 @@ pkv_status paged_attention_decode_multi(const pkv_pool* pool, int layer, void* o
  * point their block tables at the same physical blocks ("The Serving
  * Playbook", "Paged KV cache" and "Sharing is a reference count": parallel
  * sampling, beam search and a common system prompt are all several block
- * tables over one set of blocks). When such sequences decode in one batch the
- * shared portion need be read from HBM only once for the batch, not once per
- * sequence ("The Serving Playbook", "RadixAttention", "The tree changes what
+ * tables over one set of blocks). When such sequences decode in one batch,
+ * their common blocks can be streamed from HBM a single time for the whole
+ * group ("The Serving Playbook", "RadixAttention", "The tree changes what
  * the scheduler should do"). The result is that of paged_attention_decode on
  * the same arguments (within rounding); only the work is organised
  * differently. A group's shared region is its prefix rounded down to whole
@@ -274,7 +282,8 @@ pkv_status paged_attention_decode_multi(const pkv_pool* pool, int layer, void* o
  *     inside the region uses only the pieces wholly before its context end.
  *   partition_size: piece size, > 0 and a multiple of 64, or 0 for 512.
  *   workspace: at least paged_attention_decode_shared_workspace_bytes(...)
- *     bytes, 16-byte aligned; contents on entry are ignored.
+ *     bytes, 16-byte aligned, with the zero counters at its start that
+ *     paged_attention_decode describes (this call leaves them untouched).
  * bf16 and e4m3 pools (the shared products run on bf16 MFMA) and at most 4096
  * sequences; otherwise PKV_ERR_UNSUPPORTED. */
 pkv_status paged_attention_decode_shared_workspace_bytes(const pkv_pool* pool, int num_seqs,
@@ -329,6 +338,41 @@ typedef enum {
 pkv_status pkv_timing_enable(int max_launches, unsigned int kind_mask);
 pkv_status pkv_timing_disable(void);
 pkv_status pkv_timing_read(pkv_kernel_kind kind, int* launches, double* total_ms);
+
+/* The recorded launches of one kernel kind one by one: writes the duration in
+ * milliseconds of the first min(capacity, recorded) launches, in launch
+ * order, to ms[] (a host array of `capacity` floats) and their count to
+ * *launches. Waits for the events like pkv_timing_read. */
+pkv_status pkv_timing_read_launches(pkv_kernel_kind kind, float* ms, int capacity, int* launches);
+
+/* Device-value checks. Values inside device buffers (block ids, context
+ * lengths, slots, chunk bounds) are the caller's contract and are not checked
+ * by the release library, libpkv.so: checking them on the host would need a
+ * synchronization, and a wrong block id becomes a wild read in the hottest
+ * kernel ("The Serving Playbook", "The block table lives in the hottest
+ * kernel in the system"). The debug library, libpkv_debug.so (the same
+ * sources built with PKV_DEBUG=1, same entry points), tests each such value
+ * in the kernels before forming any address from it:
+ *   PKV_DEBUG_SLOT    a slot >= num_blocks * block_size: that write is skipped;
+ *   PKV_DEBUG_BLOCK   a block id outside [0, num_blocks) in a block table or
+ *                     a copy pair: block 0 is read instead / the copy skipped;
+ *   PKV_DEBUG_CONTEXT a context length outside [0, max_blocks_per_seq *
+ *                     block_size]: clamped into that range;
+ *   PKV_DEBUG_CHUNK   prefill chunk bounds from cu_q_lens that leave the
+ *                     query tensor, exceed max_q_len or the context: the
+ *                     sequence is skipped.
+ * The affected outputs are then defined (finite, no out-of-range access) but
+ * not meaningful. pkv_debug_read_errors waits for the device
+ * (hipDeviceSynchronize), returns the bits set since the last clear in
+ * *flags, and clears them if `clear` is non-zero. The release library returns
+ * PKV_ERR_UNSUPPORTED with *flags = 0. Not for use under graph capture. */
+enum {
+    PKV_DEBUG_SLOT = 1,
+    PKV_DEBUG_BLOCK = 2,
+    PKV_DEBUG_CONTEXT = 4,
+    PKV_DEBUG_CHUNK = 8
+};
+pkv_status pkv_debug_read_errors(unsigned int* flags, int clear);
 
 #ifdef __cplusplus
 }

@@ -54,8 +54,16 @@ import numpy as np
 
 def kv_cache_bytes(layers: int, kv_heads: int, head_dim: int, dtype_bytes: int,
                    seq_len: int = 1, batch: int = 1) -> int:
-    """Bytes of K plus V for ``batch`` sequences of ``seq_len`` tokens."""
-    return 2 * layers * kv_heads * head_dim * dtype_bytes * seq_len * batch
+    """Bytes of K plus V for ``batch`` sequences of ``seq_len`` tokens.
+
+    Derivation: a cached token keeps, in every layer and for every KV head,
+    one key vector and one value vector of head_dim elements. Its bytes are
+    the number of stored vectors times the bytes of one vector; a batch holds
+    seq_len * batch such tokens.
+    """
+    vectors_per_token = 2 * layers * kv_heads            # a key and a value per (layer, KV head)
+    bytes_per_vector = head_dim * dtype_bytes
+    return vectors_per_token * bytes_per_vector * seq_len * batch
 
 
 def blocks_for(ctx: int, block_size: int) -> int:

@@ -25,18 +25,25 @@ __all__ = [
     "paged_attention_decode_multi_workspace_bytes", "paged_attention_decode_multi",
     "paged_attention_decode_shared_workspace_bytes", "paged_attention_decode_shared",
     "paged_attention_prefill_chunk", "pkv_timing_enable", "pkv_timing_disable",
-    "pkv_timing_read", "pkv_last_error", "EXPORTED_SYMBOLS",
+    "pkv_timing_read", "pkv_timing_read_launches", "pkv_last_error", "pkv_debug_read_errors",
+    "DEBUG_SLOT", "DEBUG_BLOCK", "DEBUG_CONTEXT", "DEBUG_CHUNK", "library_variant", "EXPORTED_SYMBOLS",
 ]
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
 KERNEL_APPEND, KERNEL_DECODE_PARTITION, KERNEL_DECODE_REDUCE, KERNEL_PREFILL = 0, 1, 2, 3
 KERNEL_DECODE_PREFIX = 4
+DEBUG_SLOT, DEBUG_BLOCK, DEBUG_CONTEXT, DEBUG_CHUNK = 1, 2, 4, 8
 
 _STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID_ARG", -2: "PKV_ERR_UNSUPPORTED",
            -3: "PKV_ERR_HIP", -4: "PKV_ERR_WORKSPACE"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_lib = None
+# Two builds of the same sources: "release" (libpkv.so) and "debug"
+# (libpkv_debug.so, device-value checks compiled in). Calls go to the
+# variant selected by library_variant(), the release library by default.
+_LIB_FILES = {"release": "libpkv.so", "debug": "libpkv_debug.so"}
+_libs = {}
+_variant = "release"
 
 c_int, c_float, c_size_t, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 _P = ctypes.POINTER
@@ -75,6 +82,8 @@ _SIGNATURES = {
     "pkv_timing_enable": (c_int, [c_int, ctypes.c_uint]),
     "pkv_timing_disable": (c_int, []),
     "pkv_timing_read": (c_int, [c_int, _P(c_int), _P(ctypes.c_double)]),
+    "pkv_timing_read_launches": (c_int, [c_int, _P(c_float), c_int, _P(c_int)]),
+    "pkv_debug_read_errors": (c_int, [_P(ctypes.c_uint), c_int]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -85,15 +94,20 @@ class PkvError(RuntimeError):
         self.status = status
 
 
-def library_path() -> str:
-    return os.path.join(_HERE, "libpkv.so")
+def library_path(variant: str | None = None) -> str:
+    v = variant or _variant
+    # A test build of the same entry points (the host-sanitized library) can
+    # stand in for the release library.
+    if v == "release" and os.environ.get("PKV_LIBRARY_PATH"):
+        return os.environ["PKV_LIBRARY_PATH"]
+    return os.path.join(_HERE, _LIB_FILES[v])
 
 
-def load():
-    """Load libpkv.so (once). Raises if it has not been built."""
-    global _lib
-    if _lib is None:
-        path = library_path()
+def load(variant: str | None = None):
+    """Load the selected library variant (once). Raises if it has not been built."""
+    v = variant or _variant
+    if v not in _libs:
+        path = library_path(v)
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
                                "(there is no fallback implementation)")
@@ -101,8 +115,29 @@ def load():
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(lib, name)
             fn.restype, fn.argtypes = res, args
-        _lib = lib
-    return _lib
+        _libs[v] = lib
+    return _libs[v]
+
+
+class library_variant:
+    """Context manager: calls inside go to the given variant ("release" or
+    "debug"). Pool handles belong to the variant that created them."""
+
+    def __init__(self, variant: str):
+        if variant not in _LIB_FILES:
+            raise ValueError(f"unknown library variant {variant!r}")
+        self.variant = variant
+
+    def __enter__(self):
+        global _variant
+        self.prev, _variant = _variant, self.variant
+        load()
+        return self
+
+    def __exit__(self, *exc):
+        global _variant
+        _variant = self.prev
+        return False
 
 
 def _ptr(x):
@@ -265,3 +300,19 @@ def pkv_timing_read(kind):
     n, ms = c_int(), ctypes.c_double()
     _check(load().pkv_timing_read(kind, ctypes.byref(n), ctypes.byref(ms)))
     return n.value, ms.value
+
+
+def pkv_timing_read_launches(kind, capacity):
+    """Durations in ms of up to ``capacity`` recorded launches of one kernel kind, in launch order."""
+    buf = (c_float * max(capacity, 1))()
+    n = c_int()
+    _check(load().pkv_timing_read_launches(kind, buf, capacity, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]
+
+
+def pkv_debug_read_errors(clear=True):
+    """Bits (DEBUG_*) the device-value checks of the debug library set since
+    the last clear; waits for the device."""
+    f = ctypes.c_uint()
+    _check(load().pkv_debug_read_errors(ctypes.byref(f), 1 if clear else 0))
+    return f.value

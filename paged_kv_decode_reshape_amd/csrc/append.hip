@@ -40,6 +40,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams prm) {
   const int c = rem % VPR;
   const int64_t slot = prm.slots[t];
   if (slot < 0) return;
+#if PKV_DEBUG
+  if (slot >= (int64_t)prm.num_blocks * BS) {
+    debug_flag(prm.err, kErrSlot);
+    return;
+  }
+#endif
   const int64_t blk = slot / BS;
   const int off = (int)(slot % BS);
   const size_t src = ((size_t)t * prm.num_kv_heads + h) * D + (size_t)c * EPV;
@@ -62,6 +68,12 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(AppendParams prm) {
   const int c = rem % VPR;
   const int64_t slot = prm.slots[t];
   if (slot < 0) return;
+#if PKV_DEBUG
+  if (slot >= (int64_t)prm.num_blocks * BS) {
+    debug_flag(prm.err, kErrSlot);
+    return;
+  }
+#endif
   const int64_t blk = slot / BS;
   const int off = (int)(slot % BS);
   const size_t src = ((size_t)t * prm.num_kv_heads + h) * D + (size_t)c * 16;
@@ -111,6 +123,12 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyParams prm) {
   const int layer = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
   const int32_t src = prm.pairs[2 * pair], dst = prm.pairs[2 * pair + 1];
+#if PKV_DEBUG
+  if ((unsigned)src >= (unsigned)prm.num_blocks || (unsigned)dst >= (unsigned)prm.num_blocks) {
+    if (threadIdx.x == 0) debug_flag(prm.err, kErrBlock);
+    return;
+  }
+#endif
   const char* from = static_cast<const char*>(is_v ? prm.v[layer] : prm.k[layer]) + (size_t)src * prm.block_bytes;
   char* to = static_cast<char*>(is_v ? prm.v[layer] : prm.k[layer]) + (size_t)dst * prm.block_bytes;
   for (int off = threadIdx.x * 16; off < prm.block_bytes; off += 256 * 16) st16(to + off, ld16(from + off));

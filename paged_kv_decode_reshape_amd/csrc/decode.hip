@@ -180,6 +180,8 @@ struct DecodeArgs {
   const void* new_value;
   float k_inv_scale;       // e4m3 pools: 1 / the K and V scales, for the fused append
   float v_inv_scale;
+  int num_blocks;          // blocks in the pool (device-value checks)
+  uint32_t* err;           // error word of the device-value checks (PKV_DEBUG builds)
 };
 
 // Accumulate tokens [tok_begin, tok_end) of (b, h) into a fresh summary.
@@ -220,7 +222,7 @@ __device__ __forceinline__ Summary<G, DecodeShape<T, D, G>::kVEpv> run_segment(
   // that every id is a real block of this sequence and every address formed
   // below is in bounds. Issued first: the K loads wait on it.
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin;
-  int ids = bt[min(lane, nblk - 1)];
+  int ids = checked_block(bt[min(lane, nblk - 1)], a.num_blocks, a.err);
 
   wave_lds_sync();   // the wave's previous segment may still be reading q / p
   {
@@ -254,7 +256,7 @@ __device__ __forceinline__ Summary<G, DecodeShape<T, D, G>::kVEpv> run_segment(
   // values themselves, not by indexing bid, which would put bid in memory.
   auto window_bids = [&](int w, int (&bid)[BPW], int& kb) __attribute__((always_inline)) {
     const int lb = 4 * w;                               // first local block of the window
-    if (lb > 0 && (lb & 63) == 0) ids = bt[min(lb + lane, nblk - 1)];
+    if (lb > 0 && (lb & 63) == 0) ids = checked_block(bt[min(lb + lane, nblk - 1)], a.num_blocks, a.err);
     int sel = 0;
 #pragma unroll
     for (int r = 0; r < BPW; ++r) {
@@ -426,7 +428,9 @@ __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row,
 
 // Partial summary: (m, l) of head g at ml[g * ml_stride], unnormalized o at o_base + g * o_stride.
 // The partial output is stored times v_scale, so the reduction needs no scale.
-template <typename T, int D, int G>
+// kCoherent: device-scope stores, for a summary another wavefront of the
+// launch combines.
+template <typename T, int D, int G, bool kCoherent = false>
 __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base,
                                               size_t o_stride,
                                               const Summary<G, DecodeShape<T, D, G>::kVEpv>& st, float v_scale,
@@ -439,14 +443,23 @@ __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, floa
     for (int g = 0; g < G; ++g) {
       float* wo = o_base + g * o_stride + (size_t)lane * EPV;
 #pragma unroll
-      for (int e = 0; e < EPV; e += 4)
-        *reinterpret_cast<float4*>(wo + e) = make_float4(st.o[g][e] * v_scale, st.o[g][e + 1] * v_scale,
-                                                         st.o[g][e + 2] * v_scale, st.o[g][e + 3] * v_scale);
+      for (int e = 0; e < EPV; e += 4) {
+        if constexpr (kCoherent) {
+          coherent_store2(wo + e, st.o[g][e] * v_scale, st.o[g][e + 1] * v_scale);
+          coherent_store2(wo + e + 2, st.o[g][e + 2] * v_scale, st.o[g][e + 3] * v_scale);
+        } else {
+          *reinterpret_cast<float4*>(wo + e) = make_float4(st.o[g][e] * v_scale, st.o[g][e + 1] * v_scale,
+                                                           st.o[g][e + 2] * v_scale, st.o[g][e + 3] * v_scale);
+        }
+      }
     }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) ml[g * ml_stride] = make_float2(st.m[g], st.l[g]);
+    for (int g = 0; g < G; ++g) {
+      if constexpr (kCoherent) coherent_store2(reinterpret_cast<float*>(ml + g * ml_stride), st.m[g], st.l[g]);
+      else ml[g * ml_stride] = make_float2(st.m[g], st.l[g]);
+    }
   }
 }
 
@@ -549,7 +562,7 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
   // Block ids of the segment, 64 per register, clamped to its last block so
   // that every address formed below is in bounds.
   const int32_t* bt = a.block_tables + (size_t)b * a.max_blocks + lb_begin;
-  int ids = bt[min(lane, nblk - 1)];
+  int ids = checked_block(bt[min(lane, nblk - 1)], a.num_blocks, a.err);
 
   // Column col is query row j = col / G of the sequence, head g = col % G of
   // the group (columns past nq * G are zero queries, never written). Row j
@@ -593,7 +606,7 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
       constexpr int NVEC = D * (int)sizeof(T) / 16;     // 16-byte pool vectors per token row
       constexpr int EPV = 16 / (int)sizeof(T);          // elements per vector
       const int pn = ctx - 1;
-      const int blk = bt[nblk - 1];                     // the segment's last block holds position pn
+      const int blk = checked_block(bt[nblk - 1], a.num_blocks, a.err);   // the block holding position pn
       const int off = pn % BS;
       if (lane < 2 * NVEC) {
         const bool is_v = lane >= NVEC;
@@ -621,7 +634,7 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
     ++done;
     const int t0 = tok_begin + w * TPW;
     const int lb = BPW * w;
-    if (lb > 0 && (lb & 63) == 0) ids = bt[min(lb + lane, nblk - 1)];
+    if (lb > 0 && (lb & 63) == 0) ids = checked_block(bt[min(lb + lane, nblk - 1)], a.num_blocks, a.err);
     int bid[4];                                         // block of the window's 16-token tile r
 #pragma unroll
     for (int r = 0; r < 4; ++r) bid[r] = __builtin_amdgcn_readlane(ids, min(lb + 16 * r / BS, nblk - 1) & 63);
@@ -781,7 +794,9 @@ __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row, co
 }
 
 // Partial summary of column col = (row j, head g) at index j * pj + g.
-template <typename T, int D, int G>
+// kCoherent: device-scope stores, for a summary another wavefront of the
+// launch combines.
+template <typename T, int D, int G, bool kCoherent = false>
 __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base, size_t o_stride,
                                               const MfmaSummary<D>& st, float v_scale, int nq, int pj) {
   const int lane = threadIdx.x & 63;
@@ -792,10 +807,18 @@ __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, floa
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
       const mf_f32x4 o = st.o[n];
-      *reinterpret_cast<float4*>(wo + 16 * n + 4 * quad) =
-          make_float4(o[0] * v_scale, o[1] * v_scale, o[2] * v_scale, o[3] * v_scale);
+      float* p = wo + 16 * n + 4 * quad;
+      if constexpr (kCoherent) {
+        coherent_store2(p, o[0] * v_scale, o[1] * v_scale);
+        coherent_store2(p + 2, o[2] * v_scale, o[3] * v_scale);
+      } else {
+        *reinterpret_cast<float4*>(p) = make_float4(o[0] * v_scale, o[1] * v_scale, o[2] * v_scale, o[3] * v_scale);
+      }
     }
-    if (quad == 0) ml[idx * ml_stride] = make_float2(st.m, st.l);
+    if (quad == 0) {
+      if constexpr (kCoherent) coherent_store2(reinterpret_cast<float*>(ml + idx * ml_stride), st.m, st.l);
+      else ml[idx * ml_stride] = make_float2(st.m, st.l);
+    }
   }
 }
 
@@ -851,7 +874,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   if (prev >= prm.max_parts) return;
   const int part = prm.max_parts - 1 - (int)prev;
 
-  const int ctx = context_lens[b];
+  const int ctx = checked_ctx(context_lens[b], (long)args.max_blocks * BS, args.err);
   const int hq = args.hkv * G;
   // Output (and partial) rows of query row j, head g: qh0 + j * hq + g.
   const size_t qh0 = (size_t)b * nq * hq + (size_t)h * G;
@@ -883,9 +906,9 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
 // ---------------------------------------------------------------------------
 // Shared prefixes: sequences whose leading tokens live in the same physical
 // blocks ("The Serving Playbook", "Paged KV cache" and "Sharing is a reference
-// count") read those blocks once for the whole group ("RadixAttention": the
-// shared portion is fetched from HBM once for the batch, not once per
-// sequence). One wavefront per (group, KV head, member tile, partition inside
+// count") can read those blocks once for the whole group instead of once per
+// member ("RadixAttention": requests batched with a common prefix read the
+// same KV blocks). One wavefront per (group, KV head, member tile, partition inside
 // the prefix): its 16 MFMA columns are the G query heads of 16/G members, so
 // each K/V tile is loaded once and multiplied against every member's query.
 // It writes each member's partial summary for that partition in the layout of
@@ -920,7 +943,8 @@ __device__ __forceinline__ int group_end(const DecodeParams& prm, int k) {
 __device__ __forceinline__ int group_shared_tokens(const int32_t* __restrict__ context_lens,
                                                    const DecodeParams& prm, int k) {
   const int first = min(group_begin(prm, k), prm.num_seqs - 1);   // an empty group has no members to use it
-  const int plen = min(max(prm.prefix_lens[k], 0), max(context_lens[first], 0));
+  const int plen = min(max(prm.prefix_lens[k], 0),
+                       max(checked_ctx(context_lens[first], (long)prm.max_blocks * prm.block_size, prm.err), 0));
   return plen / 64 * 64;
 }
 
@@ -936,7 +960,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   for (long b = (long)blockIdx.x * blockDim.x + threadIdx.x; b < prm.num_seqs; b += (long)gridDim.x * blockDim.x) {
     const int k = find_group(prm.group_starts, prm.num_groups, (int)b);
     const int sk = group_shared_tokens(context_lens, prm, k);
-    const int ctx = max(context_lens[b], 0);
+    const int ctx = max(checked_ctx(context_lens[b], (long)prm.max_blocks * BS, args.err), 0);
     prm.shared_start[b] = ctx >= sk ? sk : ctx / P * P;
   }
 
@@ -1026,7 +1050,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
   const int rows = prm.q_per_seq * prm.num_kv_heads * prm.group;   // output rows per sequence
   if (pair >= (long)prm.num_seqs * rows) return;
   const int b = (int)(pair / rows);
-  const int ctx = context_lens[b];
+  const int ctx = checked_ctx(context_lens[b], (long)prm.max_blocks * prm.block_size, prm.err);
   const int nparts = (ctx + prm.part_tokens - 1) / prm.part_tokens;
   if (nparts <= 1) return;
   const float2* ml = reinterpret_cast<const float2*>(ws_ml) + (size_t)pair * prm.max_parts;
@@ -1070,20 +1094,21 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(
 // With shared prefixes (start non-NULL) a sequence's windows begin at its
 // token start[b].
 __device__ __forceinline__ int own_tokens(const int32_t* __restrict__ context_lens,
-                                          const int32_t* __restrict__ start, int b) {
-  const int ctx = max(context_lens[b], 0);
+                                          const int32_t* __restrict__ start, int b, long max_ctx, uint32_t* err) {
+  const int ctx = max(checked_ctx(context_lens[b], max_ctx, err), 0);
   return start ? ctx - start[b] : ctx;
 }
 
 __device__ __forceinline__ int window_prefix_sum(const int32_t* __restrict__ context_lens,
                                                  const int32_t* __restrict__ start,
-                                                 int num_seqs, int hkv, int* cum, int* scratch) {
+                                                 int num_seqs, int hkv, int* cum, int* scratch,
+                                                 long max_ctx, uint32_t* err) {
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int per = (num_seqs + 255) / 256;
   const int lo = min(num_seqs, t * per), hi = min(num_seqs, lo + per);
   int sum = 0;
-  for (int b = lo; b < hi; ++b) sum += (own_tokens(context_lens, start, b) + 63) / 64 * hkv;
+  for (int b = lo; b < hi; ++b) sum += (own_tokens(context_lens, start, b, max_ctx, err) + 63) / 64 * hkv;
   // Inclusive scan inside the wavefront, then across the 4 wavefronts.
   int inc = sum;
 #pragma unroll
@@ -1097,7 +1122,7 @@ __device__ __forceinline__ int window_prefix_sum(const int32_t* __restrict__ con
   for (int w = 0; w < wave; ++w) run += scratch[w];
   for (int b = lo; b < hi; ++b) {
     cum[b] = run;
-    run += (own_tokens(context_lens, start, b) + 63) / 64 * hkv;
+    run += (own_tokens(context_lens, start, b, max_ctx, err) + 63) / 64 * hkv;
   }
   if (t == 255) cum[num_seqs] = run;
   __syncthreads();
@@ -1174,20 +1199,93 @@ __device__ __forceinline__ void write_rows_shared(typename IoType<T>::type* out_
   }
 }
 
+// Combine of one split row inside the partition launch (one query row per
+// sequence, no shared prefixes). The row's first piece sits in slot
+// first_slot of wave `first`, each later piece in slot 0 of the waves
+// first+1 .. last with a non-empty share; the online-softmax rule merges them:
+//   M = max m,  L = sum 2^(m - M) l,  out = sum 2^(m - M) o / L.
+// A lane owns 16-byte slices of the G x D output and walks the pieces kPieces
+// at a time with all their loads in flight. out_row points at head 0 of the
+// group.
+template <typename TQ, int D, int G>
+__device__ __forceinline__ void combine_split_row(TQ* out_row, const float* ws_ml, const float* ws_o, long first,
+                                                  int first_slot, long last, long nw, int total) {
+  constexpr int kSlices = G * D / 4;                       // float4 slices of one piece
+  constexpr int NF = (kSlices + kWave - 1) / kWave;        // slices per lane
+  constexpr int kPieces = NF >= 4 ? 2 : 8 / NF;            // pieces loaded together
+  const int lane = threadIdx.x & 63;
+  // The pieces were published by other wavefronts of this launch: read with
+  // device-scope loads.
+  float m[NF], l[NF];
+  float4 acc[NF];
+  {
+    const size_t row0 = ((size_t)first * 2 + first_slot) * G;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int f = min(lane + kWave * j, kSlices - 1);
+      const float2 sm = coherent_load2(ws_ml + 2 * (row0 + f / (D / 4)));
+      m[j] = sm.x;
+      l[j] = sm.y;
+      acc[j] = coherent_load4(ws_o + 4 * (row0 * (D / 4) + f));
+    }
+  }
+  for (long i0 = first + 1; i0 <= last; i0 += kPieces) {
+    float2 sm[kPieces][NF];
+    float4 ov[kPieces][NF];
+    bool live[kPieces];
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+      const long i = min(i0 + u, last);
+      live[u] = (i0 + u <= last) && share_begin(i, nw, total) != share_begin(i + 1, nw, total);
+      const size_t rowi = (size_t)i * 2 * G;               // slot 0 of wave i
+#pragma unroll
+      for (int j = 0; j < NF; ++j) {
+        const int f = min(lane + kWave * j, kSlices - 1);
+        sm[u][j] = coherent_load2(ws_ml + 2 * (rowi + f / (D / 4)));
+        ov[u][j] = coherent_load4(ws_o + 4 * (rowi * (D / 4) + f));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPieces; ++u) {
+      if (!live[u]) continue;                              // wave-uniform: empty share or past the end
+#pragma unroll
+      for (int j = 0; j < NF; ++j) merge_state(m[j], l[j], acc[j], sm[u][j].x, sm[u][j].y, ov[u][j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int f = lane + kWave * j;
+    if (f < kSlices) store_row4<TQ>(out_row + (size_t)f * 4, acc[j], 1.0f / l[j]);
+  }
+}
+
 // SH: the rows start after their shared partitions (decode_prefix_kernel has
 // run), and every row is merged with those partitions' summaries.
+// With one query row per sequence and no shared prefixes, split rows are
+// combined inside this launch: each piece's holder publishes its summary,
+// then adds the piece's window count to the counter of the row (entry f of
+// prm.counters, f = the wave whose share holds the row's first window; no
+// other split row starts in that share). The holder that brings the count to
+// the row's window total combines the pieces, writes the row and sets the
+// counter back to zero, so the counters are zero between calls. Otherwise the
+// slot descriptors are written and decode_balanced_reduce_kernel combines.
 template <typename T, int D, int G, bool MQ, bool SH, int BS, bool AP>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_balanced_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     SlotDesc* __restrict__ ws_desc, const int32_t* __restrict__ context_lens, DecodeArgs args,
     DecodeParams prm) {
   static_assert(!SH || (!MQ && UsesMfma<T>::value), "shared prefixes: one query row, matrix-core segments");
+  // Split rows combined in this launch (one query row, no shared prefixes,
+  // counters given); otherwise the slot descriptors go to the reduction.
+  constexpr bool kCanFuse = !MQ && !SH;
+  const bool FC = kCanFuse && prm.counters != nullptr;
   __shared__ SegLds<T, D, G> lds[4];
   __shared__ int cum[kMaxBalancedSeqs + 1];
   __shared__ int scan_scratch[256];
   const int nq = MQ ? args.nq : 1;   // query rows per sequence
+  const long max_ctx = (long)args.max_blocks * BS;
   const int total = window_prefix_sum(context_lens, SH ? prm.shared_start : nullptr, prm.num_seqs, args.hkv, cum,
-                                      scan_scratch);
+                                      scan_scratch, max_ctx, args.err);
 
   // Defined result for empty contexts: zero rows, spread over the workgroups.
   // With shared prefixes a row with no tokens of its own is its shared
@@ -1225,6 +1323,8 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   if (wid >= nw) return;
   SlotDesc desc[2];
   desc[0].row = desc[1].row = -1;
+  struct Pending { int row, row_start, windows, row_windows; } pend[2];   // split pieces to count (FC)
+  pend[0].row = pend[1].row = -1;
   const int x0 = total ? share_begin(wid, nw, total) : 0;
   const int x1 = total ? share_begin(wid + 1, nw, total) : 0;
   // The hardware issues the oldest wavefront first. With equal shares that
@@ -1236,7 +1336,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   while (x < x1) {
     // Locate (b, h, first window) of x and run to the end of that (b, h) or of the share.
     const int b = find_seq(cum, prm.num_seqs, x);
-    const int ctx = context_lens[b];
+    const int ctx = checked_ctx(context_lens[b], max_ctx, args.err);
     const int t0 = SH ? prm.shared_start[b] : 0;    // the row's own tokens start here
     const int nsh = SH ? (t0 + prm.part_tokens - 1) / prm.part_tokens : 0;   // shared pieces before them
     const int nwb = (ctx - t0 + 63) / 64;
@@ -1265,20 +1365,67 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
       const int slot = (x == x0) ? 0 : 1;
       // A slot holds nq * G summary rows, column (row j, head g) at j * G + g.
       const size_t base = ((size_t)wid * 2 + slot) * nq * G;
-      write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st, args.v_scale,
-                             nq, G);
-      desc[slot].row = b * args.hkv + h;
-      desc[slot].row_start = x - w0;
-      desc[slot].w0 = w0;
-      desc[slot].w1 = w1;
-      desc[slot].row_windows = nwb;
-      desc[slot].total = total;
+      if (FC) {
+        write_partial<T, D, G, kCanFuse>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st,
+                                         args.v_scale, nq, G);
+      } else {
+        write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st, args.v_scale,
+                               nq, G);
+      }
+      if (FC) {
+        // Counted after the share's last segment (below), which keeps the
+        // combine's registers out of the segment loop.
+        const Pending p{__builtin_amdgcn_readfirstlane(b * args.hkv + h), __builtin_amdgcn_readfirstlane(x - w0),
+                        __builtin_amdgcn_readfirstlane(w1 - w0), __builtin_amdgcn_readfirstlane(nwb)};
+        if (slot == 0) pend[0] = p; else pend[1] = p;
+      } else {
+        desc[slot].row = b * args.hkv + h;
+        desc[slot].row_start = x - w0;
+        desc[slot].w0 = w0;
+        desc[slot].w1 = w1;
+        desc[slot].row_windows = nwb;
+        desc[slot].total = total;
+      }
     }
     x += w1 - w0;
   }
-  if (lane == 0) {
-    ws_desc[wid * 2] = desc[0];
-    ws_desc[wid * 2 + 1] = desc[1];
+  if (FC) {
+    // Count this wave's split pieces towards their rows' totals; the wave
+    // that completes a row combines it and zeroes its counter. The counter of
+    // a row is entry f of prm.counters, f = the wave whose share holds the
+    // row's first window.
+    if (pend[0].row >= 0 || pend[1].row >= 0) {
+      wait_stores_complete();                            // the summaries are published before they count
+      bool mine[2] = {false, false};
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        if (pend[k].row < 0) continue;
+        const long f = share_of(pend[k].row_start, nw, total);
+        int old = 0;
+        if (lane == 0) old = atomicAdd(prm.counters + f, pend[k].windows);
+        old = __builtin_amdgcn_readfirstlane(old);
+        mine[k] = old + pend[k].windows == pend[k].row_windows;   // every other piece is published
+      }
+      if (mine[0] || mine[1]) {
+        asm volatile("" ::: "memory");                   // the pieces are read after the count
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if (!mine[k]) continue;
+          const int row_start = pend[k].row_start;
+          const long f = share_of(row_start, nw, total);
+          const long last = share_of((long)row_start + pend[k].row_windows - 1, nw, total);
+          const int b = pend[k].row / args.hkv, h = pend[k].row % args.hkv;
+          combine_split_row<TQ, D, G>(out_ptr + ((size_t)b * args.hkv + h) * G * D, ws_ml, ws_o, f,
+                                      share_begin(f, nw, total) == row_start ? 0 : 1, last, nw, total);
+          if (lane == 0) atomicExch(prm.counters + f, 0);
+        }
+      }
+    }
+  } else {
+    if (lane == 0) {
+      ws_desc[wid * 2] = desc[0];
+      ws_desc[wid * 2 + 1] = desc[1];
+    }
   }
 }
 
@@ -1544,7 +1691,8 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
   using TQ = typename IoType<T>::type;
   const DecodeArgs args{prm.query, prm.kpool, prm.vpool, prm.block_tables, prm.num_kv_heads,
                         prm.max_blocks, prm.scale_log2, prm.v_scale, prm.q_per_seq,
-                        prm.new_key, prm.new_value, prm.k_inv_scale, prm.v_inv_scale};
+                        prm.new_key, prm.new_value, prm.k_inv_scale, prm.v_inv_scale,
+                        prm.num_blocks, prm.err};
   TQ* out = static_cast<TQ*>(prm.out);
   hipError_t err;
   // Shared prefixes: the groups' shared partitions first (they also record
@@ -1582,6 +1730,7 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
     }
     timer.end(KernelKind::kDecodePartition, stream);
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (prm.counters != nullptr) return hipSuccess;              // split rows were combined in the launch
     timer.begin(KernelKind::kDecodeReduce, stream);
     const dim3 rgrid((unsigned)((prm.num_waves + 3) / 4), (unsigned)prm.q_per_seq);
     if ((long)prm.num_seqs * prm.num_kv_heads * 8 <= prm.num_waves) {

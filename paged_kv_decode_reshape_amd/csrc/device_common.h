@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef PKV_DEBUG
+#define PKV_DEBUG 0
+#endif
+
 namespace pkv {
 
 constexpr int kBlockSize = 16;   // tokens per KV block
@@ -97,13 +101,15 @@ __device__ __forceinline__ void widen(const Vec8& v, float* f) {
   }
 }
 
-// Two e4m3 codes (bytes 0, 1 of w, or 2, 3 with kHigh) as a bf16 pair, exactly: an
-// e4m3 value has at most 4 significant bits, so its f32 form is a bf16 value
-// whose low 16 bits are zero; the byte permute keeps the high halves.
+// Two e4m3 codes (bytes 0, 1 of w, or 2, 3 with kHigh) as a bf16 pair, exactly:
+// an e4m3 value has at most 4 significant bits and an exponent inside bf16's
+// range, so gfx950's scaled conversion with scale 1 (one instruction for the
+// pair) is exact; the first code lands in the low half.
 template <bool kHigh>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  const pkv_f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, kHigh);
-  return __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHigh);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // e4m3 code pair of (a, b) * inv_scale: the fp32 products are clamped to
@@ -223,6 +229,86 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Device-coherent exchange between wavefronts of one launch without cache-wide
+// maintenance. On MI355X each XCD has its own L2; a device-scope fence would
+// write back and invalidate a whole L2, which stalls every wavefront of that
+// XCD. Instead the data a wavefront hands to another is stored and loaded
+// with device-scope (sc1) accesses, which bypass the XCD-private cache state,
+// and the publishing wavefront waits for its stores to complete before it
+// signals (an atomic counter) -- the ordering a release fence would give for
+// exactly these stores.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void coherent_store2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 coherent_load2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+__device__ __forceinline__ float4 coherent_load4(const float* p) {
+  const float2 a = coherent_load2(p), b = coherent_load2(p + 2);
+  return make_float4(a.x, a.y, b.x, b.y);
+}
+// Every store this wavefront issued has completed (vmcnt 0); the memory
+// clobber keeps the compiler from moving memory operations across the wait.
+__device__ __forceinline__ void wait_stores_complete() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt fields at their maximum
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Device-value checks. Values read from caller buffers (block ids, context
+// lengths, slots, chunk bounds) are trusted in release builds. Built with
+// PKV_DEBUG=1, every kernel tests them before forming an address from them:
+// an out-of-range value is replaced by a safe one (block 0, a clamped
+// length) or its access is skipped, and a bit is set in the error word that
+// the host reads with pkv_debug_read_errors. The kernels still run to their
+// normal end.
+// ---------------------------------------------------------------------------
+enum : uint32_t {
+  kErrSlot = 1u,      // a slot past num_blocks * block_size: the write is skipped
+  kErrBlock = 2u,     // a block id outside [0, num_blocks): block 0 is used instead
+  kErrContext = 4u,   // a context length outside [0, max_blocks * block_size): clamped
+  kErrChunk = 8u,     // prefill chunk bounds (cu_q_lens) inconsistent: the sequence is skipped
+};
+
+__device__ __forceinline__ void debug_flag(uint32_t* err, uint32_t bit) {
+  if (err != nullptr) __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A block id read from a block table (or a copy pair).
+__device__ __forceinline__ int checked_block(int id, int num_blocks, uint32_t* err) {
+#if PKV_DEBUG
+  if ((unsigned)id >= (unsigned)num_blocks) {
+    debug_flag(err, kErrBlock);
+    return 0;
+  }
+#else
+  (void)num_blocks;
+  (void)err;
+#endif
+  return id;
+}
+
+// A context length read from context_lens: at most max_ctx tokens (the block
+// table's row length times the block size).
+__device__ __forceinline__ int checked_ctx(int ctx, long max_ctx, uint32_t* err) {
+#if PKV_DEBUG
+  if (ctx < 0 || (long)ctx > max_ctx) {
+    debug_flag(err, kErrContext);
+    return ctx < 0 ? 0 : (int)max_ctx;
+  }
+#else
+  (void)max_ctx;
+  (void)err;
+#endif
+  return ctx;
+}
 
 // 16 bf16 values at p, times inv_scale, as 16 e4m3 codes.
 __device__ __forceinline__ Vec16 quantize16(const uint16_t* p, float inv_scale) {

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstring>
 #include <cstdio>
 #include <mutex>
 #include <string>
@@ -53,12 +54,23 @@ pkv::PoolType pool_type(pkv_dtype dt) {
   return dt == PKV_FP8_E4M3 ? pkv::PoolType::kFP8 : dt == PKV_BF16 ? pkv::PoolType::kBF16 : pkv::PoolType::kF32;
 }
 
-pkv_status check_geometry(int num_blocks, int block_size, int num_kv_heads, int head_dim,
-                          pkv_dtype dtype) {
+// The value a caller passed for an enum argument (pkv_dtype,
+// pkv_kernel_kind), read as an integer: a value outside the enumeration must
+// not be loaded through the enum type.
+template <typename E>
+int enum_code(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C-ABI enums are int-sized");
+  int v = 0;
+  std::memcpy(&v, &e, sizeof(v));
+  return v;
+}
+int dtype_code(const pkv_dtype& dt) { return enum_code(dt); }
+
+pkv_status check_geometry(int num_blocks, int block_size, int num_kv_heads, int head_dim, int dtype) {
   if (num_blocks <= 0) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive (got %d)", num_blocks);
   if (num_kv_heads <= 0) return fail(PKV_ERR_INVALID_ARG, "num_kv_heads must be positive (got %d)", num_kv_heads);
   if (block_size <= 0 || head_dim <= 0) return fail(PKV_ERR_INVALID_ARG, "block_size and head_dim must be positive");
-  if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_FP8_E4M3) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (dtype != PKV_F32 && dtype != PKV_BF16 && dtype != PKV_FP8_E4M3) return fail(PKV_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (block_size != pkv::kPoolBlockSize && block_size != pkv::kPoolBlockSizeLarge)
     return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16, or 32 for bf16 and e4m3 pools)", block_size);
   if (block_size == pkv::kPoolBlockSizeLarge && dtype == PKV_F32)
@@ -144,6 +156,44 @@ int device_cu_count() {
 
 size_t round16(size_t x) { return (x + 15) / 16 * 16; }
 
+// Every non-empty decode workspace starts with completion counters, one int32
+// per balanced-split wavefront. They are zero between calls: the caller
+// zero-fills a workspace before its first use and every call leaves them zero,
+// so one workspace serves any later decode call of any variant.
+constexpr size_t kCounterBytes = (size_t)kBalancedWaveCap * sizeof(int32_t);
+
+// ---- device-value checks (PKV_DEBUG builds) ----
+#if PKV_DEBUG
+// Bits set by the kernels' checks of values read from caller buffers.
+__device__ uint32_t g_debug_error_word;
+#endif
+
+// Device address of the error word on the current device (looked up once per
+// device), or NULL in release builds and when it cannot be resolved.
+uint32_t* debug_error_word() {
+#if PKV_DEBUG
+  static std::mutex mu;
+  static uint32_t* cached[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_debug_error_word)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    cached[dev] = static_cast<uint32_t*>(p);
+  }
+  return cached[dev];
+#else
+  return nullptr;
+#endif
+}
+
 // ---- kernel timing ----
 struct TimingState {
   std::mutex mu;
@@ -200,7 +250,7 @@ const char* pkv_last_error(void) { return g_last_error.c_str(); }
 pkv_status kv_pool_bytes(int num_blocks, int block_size, int num_kv_heads, int head_dim,
                          pkv_dtype dtype, size_t* k_bytes_per_layer,
                          size_t* v_bytes_per_layer) {
-  pkv_status st = check_geometry(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  pkv_status st = check_geometry(num_blocks, block_size, num_kv_heads, head_dim, dtype_code(dtype));
   if (st != PKV_OK) return st;
   if (!k_bytes_per_layer || !v_bytes_per_layer)
     return fail(PKV_ERR_INVALID_ARG, "output pointers must not be NULL");
@@ -215,7 +265,7 @@ pkv_status kv_pool_create(pkv_pool** out, int num_layers, int num_blocks, int bl
                           void* const* k_layers, void* const* v_layers) {
   if (!out) return fail(PKV_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
-  pkv_status st = check_geometry(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  pkv_status st = check_geometry(num_blocks, block_size, num_kv_heads, head_dim, dtype_code(dtype));
   if (st != PKV_OK) return st;
   if (num_layers <= 0) return fail(PKV_ERR_INVALID_ARG, "num_layers must be positive (got %d)", num_layers);
   if (!k_layers || !v_layers) return fail(PKV_ERR_INVALID_ARG, "layer pointer arrays must not be NULL");
@@ -280,7 +330,8 @@ pkv_status reshape_and_cache(const pkv_pool* pool, int layer, const void* key,
   if (threads >= (1L << 32) - 256) return fail(PKV_ERR_UNSUPPORTED, "too many tokens in one call");
   pkv::AppendParams prm{pool->k_layers[layer], pool->v_layers[layer], key, value, slot_mapping,
                         num_tokens, pool->num_kv_heads, pool->head_dim,
-                        1.0f / pool->k_scale[layer], 1.0f / pool->v_scale[layer], pool->block_size};
+                        1.0f / pool->k_scale[layer], 1.0f / pool->v_scale[layer], pool->block_size,
+                        pool->num_blocks, debug_error_word()};
   (void)hipGetLastError();
   hipError_t err = pkv::launch_append(prm, pool_type(pool->dtype), (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "reshape_and_cache launch");
@@ -303,15 +354,24 @@ pkv_status decode_workspace(const pkv_pool* pool, int num_seqs, int q_per_seq, i
   if (num_q_heads % pool->num_kv_heads != 0)
     return fail(PKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
                 num_q_heads, pool->num_kv_heads);
+  if (q_per_seq * (num_q_heads / pool->num_kv_heads) > kMfmaColumns) {
+    *bytes = 0;   // run by the prefill-chunk kernel, which needs no workspace
+    return PKV_OK;
+  }
   DecodeSplit sp;
   pkv_status st = decode_split(pool, num_seqs, num_q_heads, max_blocks_per_seq, partition_size, &sp);
   if (st != PKV_OK) return st;
   const size_t rows = decode_summary_rows(sp, num_seqs, num_q_heads, num_q_heads / pool->num_kv_heads) *
                       (size_t)q_per_seq;
-  *bytes = rows == 0 ? 0 : round16(rows * 2 * sizeof(float)) + rows * pool->head_dim * sizeof(float);
+  *bytes = rows == 0 ? 0 : kCounterBytes + round16(rows * 2 * sizeof(float)) + rows * pool->head_dim * sizeof(float);
   if (sp.balanced) *bytes += (size_t)sp.wave_cap * 2 * pkv::decode_balanced_desc_bytes();
   return PKV_OK;
 }
+
+pkv_status prefill_run(const pkv_pool* pool, int layer, void* out, const void* query, const int32_t* cu_q_lens,
+                       int q_per_seq, const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                       int total_q_tokens, int max_q_len, int num_q_heads, int max_blocks_per_seq, float scale,
+                       void* stream);
 
 // new_key / new_value (both or neither): the fused append of
 // paged_attention_decode_append.
@@ -331,12 +391,19 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
   if (group > 8) return fail(PKV_ERR_UNSUPPORTED, "%d query heads per KV head unsupported (1..8)", group);
   if (q_per_seq > 1 && pool->dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "several queries per sequence run on the matrix cores: bf16 and e4m3 pools only");
-  if (q_per_seq * group > kMfmaColumns)
-    return fail(PKV_ERR_UNSUPPORTED, "queries_per_seq (%d) x query heads per KV head (%d) must be <= %d",
-                q_per_seq, group, kMfmaColumns);
   if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
   if (num_seqs == 0) return PKV_OK;
+  if (q_per_seq * group > kMfmaColumns) {
+    // More query rows per KV head than one matrix-core tile holds: the
+    // rows of a sequence are an equal-length prefill chunk, run by the
+    // prefill-chunk kernel (no KV-axis split, no workspace).
+    if (new_key || new_value)
+      return fail(PKV_ERR_UNSUPPORTED, "the fused append takes one query row per sequence");
+    if ((long)num_seqs * q_per_seq > INT32_MAX) return fail(PKV_ERR_UNSUPPORTED, "too many query rows in one call");
+    return prefill_run(pool, layer, out, query, nullptr, q_per_seq, block_tables, context_lens, num_seqs,
+                       num_seqs * q_per_seq, q_per_seq, num_q_heads, max_blocks_per_seq, scale, stream);
+  }
   if (!out || !query || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "out, query, block_tables and context_lens must not be NULL");
   if (!aligned(out, 16) || !aligned(query, 16)) return fail(PKV_ERR_INVALID_ARG, "out/query must be 16-byte aligned");
@@ -371,18 +438,43 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
     if ((units + 3) / 4 >= (1L << 24)) return fail(PKV_ERR_UNSUPPORTED, "too many work units in one call");
   }
   const size_t rows = decode_summary_rows(sp, num_seqs, num_q_heads, group) * (size_t)q_per_seq;
-  float* ws_ml = static_cast<float*>(workspace);
-  float* ws_o = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round16(rows * 2 * sizeof(float)))
-                         : nullptr;
-  void* ws_desc = sp.balanced ? static_cast<void*>(reinterpret_cast<char*>(ws_o) + rows * pool->head_dim * sizeof(float))
-                              : nullptr;
-  pkv::DecodeParams prm{out, ws_ml, ws_o, ws_desc, query, pool->k_layers[layer], pool->v_layers[layer],
-                        block_tables, context_lens, num_seqs, pool->num_kv_heads, group,
-                        pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
-                        num_waves, scale * 1.4426950408889634f * pool->k_scale[layer],
-                        pool->v_scale[layer], q_per_seq, nullptr, nullptr, 0, 0, nullptr, nullptr, nullptr,
-                        pool->block_size, new_key, new_value, 1.0f / pool->k_scale[layer],
-                        1.0f / pool->v_scale[layer]};
+  char* ws = static_cast<char*>(workspace);
+  pkv::DecodeParams prm{};
+  if (need > 0) {
+    prm.ws_ml = reinterpret_cast<float*>(ws + kCounterBytes);
+    prm.ws_o = reinterpret_cast<float*>(ws + kCounterBytes + round16(rows * 2 * sizeof(float)));
+    if (sp.balanced) prm.ws_desc = reinterpret_cast<char*>(prm.ws_o) + rows * pool->head_dim * sizeof(float);
+  }
+  prm.out = out;
+  prm.query = query;
+  prm.kpool = pool->k_layers[layer];
+  prm.vpool = pool->v_layers[layer];
+  prm.block_tables = block_tables;
+  prm.context_lens = context_lens;
+  prm.num_seqs = num_seqs;
+  prm.num_kv_heads = pool->num_kv_heads;
+  prm.group = group;
+  prm.head_dim = pool->head_dim;
+  prm.max_blocks = max_blocks_per_seq;
+  prm.part_tokens = sp.part_tokens;
+  prm.max_parts = sp.max_parts;
+  prm.num_waves = num_waves;
+  // One query row per sequence: the wavefront that completes a split row
+  // combines it in the launch, unless the rows are few and long (each spread
+  // over about eight or more wavefronts), where the reduction kernel's
+  // workgroup-shared combine is faster.
+  if (need > 0 && sp.balanced && q_per_seq == 1 && (long)num_seqs * pool->num_kv_heads * 8 > num_waves)
+    prm.counters = reinterpret_cast<int32_t*>(ws);
+  prm.scale_log2 = scale * 1.4426950408889634f * pool->k_scale[layer];
+  prm.v_scale = pool->v_scale[layer];
+  prm.q_per_seq = q_per_seq;
+  prm.block_size = pool->block_size;
+  prm.new_key = new_key;
+  prm.new_value = new_value;
+  prm.k_inv_scale = 1.0f / pool->k_scale[layer];
+  prm.v_inv_scale = 1.0f / pool->v_scale[layer];
+  prm.num_blocks = pool->num_blocks;
+  prm.err = debug_error_word();
   (void)hipGetLastError();
   hipError_t err = pkv::launch_decode(prm, type, (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "paged_attention_decode launch");
@@ -403,7 +495,7 @@ struct SharedLayout {
   DecodeSplit own;         // split of the own tokens
   size_t pre_rows = 0;
   size_t own_rows = 0;     // balanced slots' summary rows
-  size_t off_pre_o = 0, off_parts = 0, off_ml = 0, off_o = 0, off_desc = 0, bytes = 0;
+  size_t off_pre_ml = 0, off_pre_o = 0, off_parts = 0, off_ml = 0, off_o = 0, off_desc = 0, bytes = 0;
 };
 
 pkv_status shared_layout(const pkv_pool* pool, int num_seqs, int num_q_heads, int max_blocks_per_seq,
@@ -431,7 +523,8 @@ pkv_status shared_layout(const pkv_pool* pool, int num_seqs, int num_q_heads, in
   lay->pre_rows = (size_t)num_seqs * num_q_heads * lay->fixed.max_parts;
   lay->own_rows = lay->own.balanced ? decode_summary_rows(lay->own, num_seqs, num_q_heads, group) : 0;
   if (num_seqs == 0) return PKV_OK;
-  lay->off_pre_o = round16(lay->pre_rows * 2 * sizeof(float));
+  lay->off_pre_ml = kCounterBytes;
+  lay->off_pre_o = lay->off_pre_ml + round16(lay->pre_rows * 2 * sizeof(float));
   lay->off_parts = lay->off_pre_o + round16(lay->pre_rows * d * sizeof(float));
   lay->off_ml = lay->off_parts + round16((size_t)num_seqs * sizeof(int32_t));
   lay->off_o = lay->off_ml + round16(lay->own_rows * 2 * sizeof(float));
@@ -504,7 +597,7 @@ pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* 
     return fail(PKV_ERR_UNSUPPORTED, "too many work units in one call");
   const pkv::PoolType type = pool_type(pool->dtype);
   char* ws = static_cast<char*>(workspace);
-  float* pre_ml = reinterpret_cast<float*>(ws);
+  float* pre_ml = reinterpret_cast<float*>(ws + lay.off_pre_ml);
   float* pre_o = reinterpret_cast<float*>(ws + lay.off_pre_o);
   int32_t* shared_start = reinterpret_cast<int32_t*>(ws + lay.off_parts);
   float* ws_ml = pre_ml;
@@ -518,12 +611,37 @@ pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* 
     const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, group, false);
     num_waves = (int)std::max(1L, std::min(lay.own.wave_cap, slots));
   }
-  pkv::DecodeParams prm{out, ws_ml, ws_o, ws_desc, query, pool->k_layers[layer], pool->v_layers[layer],
-                        block_tables, context_lens, num_seqs, pool->num_kv_heads, group,
-                        pool->head_dim, max_blocks_per_seq, sp.part_tokens, sp.max_parts,
-                        num_waves, scale * 1.4426950408889634f * pool->k_scale[layer],
-                        pool->v_scale[layer], 1, group_starts, prefix_lens, num_groups, (int)member_tiles,
-                        shared_start, pre_ml, pre_o, pool->block_size};
+  pkv::DecodeParams prm{};
+  prm.out = out;
+  prm.ws_ml = ws_ml;
+  prm.ws_o = ws_o;
+  prm.ws_desc = ws_desc;
+  prm.query = query;
+  prm.kpool = pool->k_layers[layer];
+  prm.vpool = pool->v_layers[layer];
+  prm.block_tables = block_tables;
+  prm.context_lens = context_lens;
+  prm.num_seqs = num_seqs;
+  prm.num_kv_heads = pool->num_kv_heads;
+  prm.group = group;
+  prm.head_dim = pool->head_dim;
+  prm.max_blocks = max_blocks_per_seq;
+  prm.part_tokens = sp.part_tokens;
+  prm.max_parts = sp.max_parts;
+  prm.num_waves = num_waves;
+  prm.scale_log2 = scale * 1.4426950408889634f * pool->k_scale[layer];
+  prm.v_scale = pool->v_scale[layer];
+  prm.q_per_seq = 1;
+  prm.group_starts = group_starts;
+  prm.prefix_lens = prefix_lens;
+  prm.num_groups = num_groups;
+  prm.member_tiles = (int)member_tiles;
+  prm.shared_start = shared_start;
+  prm.pre_ml = pre_ml;
+  prm.pre_o = pre_o;
+  prm.block_size = pool->block_size;
+  prm.num_blocks = pool->num_blocks;
+  prm.err = debug_error_word();
   (void)hipGetLastError();
   hipError_t err = pkv::launch_decode(prm, type, (hipStream_t)stream, pkv::KernelTimer{});
   if (err != hipSuccess) return hip_fail(err, "paged_attention_decode_shared launch");
@@ -551,6 +669,8 @@ pkv_status copy_blocks(const pkv_pool* pool, const int32_t* block_pairs, int num
     prm.pairs = block_pairs;
     prm.num_pairs = num_pairs;
     prm.block_bytes = (int)block_bytes;
+    prm.num_blocks = pool->num_blocks;
+    prm.err = debug_error_word();
     hipError_t err = pkv::launch_copy_blocks(prm, (hipStream_t)stream);
     if (err != hipSuccess) return hip_fail(err, "copy_blocks launch");
   }
@@ -608,6 +728,22 @@ pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* 
                                          const int32_t* context_lens, int num_seqs,
                                          int total_q_tokens, int max_q_len, int num_q_heads,
                                          int max_blocks_per_seq, float scale, void* stream) {
+  if (num_seqs > 0 && total_q_tokens > 0 && !cu_q_lens)
+    return fail(PKV_ERR_INVALID_ARG, "out, query, cu_q_lens, block_tables and context_lens must not be NULL");
+  return prefill_run(pool, layer, out, query, cu_q_lens, 0, block_tables, context_lens, num_seqs, total_q_tokens,
+                     max_q_len, num_q_heads, max_blocks_per_seq, scale, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Prefill-chunk attention: chunk bounds from cu_q_lens, or (q_per_seq > 0,
+// cu_q_lens unused) q_per_seq rows for every sequence.
+pkv_status prefill_run(const pkv_pool* pool, int layer, void* out, const void* query, const int32_t* cu_q_lens,
+                       int q_per_seq, const int32_t* block_tables, const int32_t* context_lens, int num_seqs,
+                       int total_q_tokens, int max_q_len, int num_q_heads, int max_blocks_per_seq, float scale,
+                       void* stream) {
   pkv_status st = check_pool_layer(pool, layer);
   if (st != PKV_OK) return st;
   if (pool->dtype == PKV_F32)
@@ -623,22 +759,42 @@ pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* 
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
   if (num_seqs == 0 || total_q_tokens == 0) return PKV_OK;
   if (max_q_len == 0) return fail(PKV_ERR_INVALID_ARG, "max_q_len must be positive when there are query rows");
-  if (!out || !query || !cu_q_lens || !block_tables || !context_lens)
+  if (!out || !query || (!cu_q_lens && q_per_seq <= 0) || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "out, query, cu_q_lens, block_tables and context_lens must not be NULL");
   if (!aligned(out, 16) || !aligned(query, 16)) return fail(PKV_ERR_INVALID_ARG, "out/query must be 16-byte aligned");
   if (!aligned(cu_q_lens, 4) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
     return fail(PKV_ERR_INVALID_ARG, "integer arrays must be 4-byte aligned");
-  pkv::PrefillParams prm{out, query, pool->k_layers[layer], pool->v_layers[layer], cu_q_lens,
-                         block_tables, context_lens, num_seqs, total_q_tokens, max_q_len,
-                         pool->num_kv_heads, group, pool->head_dim, max_blocks_per_seq,
-                         scale * 1.4426950408889634f * pool->k_scale[layer], pool->v_scale[layer],
-                         pool->block_size};
+  pkv::PrefillParams prm{};
+  prm.out = out;
+  prm.query = query;
+  prm.kpool = pool->k_layers[layer];
+  prm.vpool = pool->v_layers[layer];
+  prm.cu_q_lens = cu_q_lens;
+  prm.block_tables = block_tables;
+  prm.context_lens = context_lens;
+  prm.num_seqs = num_seqs;
+  prm.total_q = total_q_tokens;
+  prm.max_q_len = max_q_len;
+  prm.num_kv_heads = pool->num_kv_heads;
+  prm.group = group;
+  prm.head_dim = pool->head_dim;
+  prm.max_blocks = max_blocks_per_seq;
+  prm.scale_log2 = scale * 1.4426950408889634f * pool->k_scale[layer];
+  prm.v_scale = pool->v_scale[layer];
+  prm.block_size = pool->block_size;
+  prm.q_per_seq = q_per_seq;
+  prm.num_blocks = pool->num_blocks;
+  prm.err = debug_error_word();
   (void)hipGetLastError();
   hipError_t err = pkv::launch_prefill(prm, pool_type(pool->dtype), (hipStream_t)stream, pkv::KernelTimer{});
   if (err == hipErrorNotSupported) return fail(PKV_ERR_UNSUPPORTED, "prefill geometry not supported");
   if (err != hipSuccess) return hip_fail(err, "paged_attention_prefill_chunk launch");
   return PKV_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 pkv_status pkv_timing_enable(int max_launches, unsigned int kind_mask) {
   if (max_launches <= 0) return fail(PKV_ERR_INVALID_ARG, "max_launches must be positive");
@@ -675,12 +831,13 @@ pkv_status pkv_timing_disable(void) {
 
 pkv_status pkv_timing_read(pkv_kernel_kind kind, int* launches, double* total_ms) {
   if (!launches || !total_ms) return fail(PKV_ERR_INVALID_ARG, "output pointers must not be NULL");
-  if ((int)kind < 0 || (int)kind >= PKV_KERNEL_KINDS) return fail(PKV_ERR_INVALID_ARG, "unknown kernel kind");
+  const int kcode = enum_code(kind);
+  if (kcode < 0 || kcode >= PKV_KERNEL_KINDS) return fail(PKV_ERR_INVALID_ARG, "unknown kernel kind");
   std::lock_guard<std::mutex> lock(g_timing.mu);
   int n = 0;
   double sum = 0.0;
   for (int i = 0; i < g_timing.used; ++i) {
-    if (g_timing.kind[i] != (int)kind) continue;
+    if (g_timing.kind[i] != kcode) continue;
     hipError_t err = hipEventSynchronize(g_timing.stop[i]);
     if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
     float ms = 0.f;
@@ -691,6 +848,49 @@ pkv_status pkv_timing_read(pkv_kernel_kind kind, int* launches, double* total_ms
   }
   *launches = n;
   *total_ms = sum;
+  return PKV_OK;
+}
+
+pkv_status pkv_debug_read_errors(unsigned int* flags, int clear) {
+  if (!flags) return fail(PKV_ERR_INVALID_ARG, "flags is NULL");
+  *flags = 0;
+#if PKV_DEBUG
+  uint32_t* word = debug_error_word();
+  if (!word) return fail(PKV_ERR_HIP, "the device error word could not be resolved");
+  hipError_t err = hipDeviceSynchronize();
+  if (err != hipSuccess) return hip_fail(err, "hipDeviceSynchronize");
+  uint32_t v = 0;
+  err = hipMemcpy(&v, word, sizeof(v), hipMemcpyDeviceToHost);
+  if (err != hipSuccess) return hip_fail(err, "hipMemcpy");
+  if (clear) {
+    const uint32_t zero = 0;
+    err = hipMemcpy(word, &zero, sizeof(zero), hipMemcpyHostToDevice);
+    if (err != hipSuccess) return hip_fail(err, "hipMemcpy");
+  }
+  *flags = v;
+  return PKV_OK;
+#else
+  (void)clear;
+  return fail(PKV_ERR_UNSUPPORTED, "this library was built without device-value checks (PKV_DEBUG=0)");
+#endif
+}
+
+pkv_status pkv_timing_read_launches(pkv_kernel_kind kind, float* ms, int capacity, int* launches) {
+  if (!launches || (!ms && capacity > 0)) return fail(PKV_ERR_INVALID_ARG, "output pointers must not be NULL");
+  if (capacity < 0) return fail(PKV_ERR_INVALID_ARG, "capacity must be >= 0");
+  const int kcode = enum_code(kind);
+  if (kcode < 0 || kcode >= PKV_KERNEL_KINDS) return fail(PKV_ERR_INVALID_ARG, "unknown kernel kind");
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  int n = 0;
+  for (int i = 0; i < g_timing.used && n < capacity; ++i) {
+    if (g_timing.kind[i] != kcode) continue;
+    hipError_t err = hipEventSynchronize(g_timing.stop[i]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventSynchronize");
+    err = hipEventElapsedTime(&ms[n], g_timing.start[i], g_timing.stop[i]);
+    if (err != hipSuccess) return hip_fail(err, "hipEventElapsedTime");
+    ++n;
+  }
+  *launches = n;
   return PKV_OK;
 }
 

@@ -35,13 +35,17 @@ struct AppendParams {
   float k_inv_scale;       // e4m3 pools: 1 / the layer's K scale (fp32)
   float v_inv_scale;       // e4m3 pools: 1 / the layer's V scale (fp32)
   int block_size;          // tokens per pool block (16 or 32)
+  int num_blocks;          // blocks in the pool (device-value checks)
+  uint32_t* err;           // device error word of the checks (PKV_DEBUG builds), else NULL
 };
 
 struct DecodeParams {
   void* out;
   float* ws_ml;            // float2 [B*q_per_seq][Hq][max_parts]: (max in base 2, normalizer)
   float* ws_o;             // float  [B*q_per_seq][Hq][max_parts][D]: unnormalized partial output
-  void* ws_desc;           // balanced split: two slot descriptors per wave
+  void* ws_desc;           // balanced split: two slot descriptors per wave (rows combined by the reduction)
+  int32_t* counters;       // balanced split, one query row, no shared prefixes: per-wave completion
+                           // counters (zero between calls); the wave that completes a split row combines it
   const void* query;
   const void* kpool;
   const void* vpool;
@@ -80,6 +84,8 @@ struct DecodeParams {
   const void* new_value;
   float k_inv_scale;
   float v_inv_scale;
+  int num_blocks;          // blocks in the pool (device-value checks)
+  uint32_t* err;           // device error word of the checks (PKV_DEBUG builds), else NULL
 };
 
 struct PrefillParams {
@@ -100,6 +106,9 @@ struct PrefillParams {
   float scale_log2;        // scale * log2(e), times the K scale of an e4m3 pool
   float v_scale;           // e4m3 pools: the V scale; else 1
   int block_size;          // tokens per pool block (16 or 32)
+  int q_per_seq;           // > 0: every sequence has this many query rows, packed in order (cu_q_lens unused)
+  int num_blocks;          // blocks in the pool (device-value checks)
+  uint32_t* err;           // device error word of the checks (PKV_DEBUG builds), else NULL
 };
 
 hipError_t launch_append(const AppendParams& prm, PoolType type, hipStream_t stream,
@@ -114,6 +123,8 @@ struct CopyParams {
   const int32_t* pairs;    // [num_pairs][2]: (source block, destination block)
   int num_pairs;
   int block_bytes;         // bytes of one block of one layer's K (or V) pool, all heads
+  int num_blocks;          // blocks in the pool (device-value checks)
+  uint32_t* err;           // device error word of the checks (PKV_DEBUG builds), else NULL
 };
 hipError_t launch_copy_blocks(const CopyParams& prm, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,

@@ -104,13 +104,38 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   constexpr int PER = (NG * kVecs + NT - 1) / NT;   // vectors each thread stages per step
   __shared__ PrefillLds<D, NWG, NG, BS> lds;
 
-  const int s = blockIdx.z;
-  const int h = blockIdx.y;
-  const int q_lo = cu_q_lens[s];
-  const int T = cu_q_lens[s + 1] - q_lo;
-  const int r_wg = blockIdx.x * kQRows * RT;   // first chunk row of this workgroup
+  // Work item of this workgroup: (sequence s, KV head h, row tile x), x
+  // fastest. The hardware hands workgroups to the 8 XCDs in turn (workgroup
+  // i to XCD i mod 8), each XCD with its own L2; the items are dealt so that
+  // XCD j runs a contiguous run of them -- all row tiles of one (sequence, KV
+  // head) together -- and each K/V tile is fetched into one L2 rather than
+  // into all eight. Any dispatch order gives the same result.
+  int s, h, xt;
+  {
+    const int n = (int)(gridDim.x * gridDim.y * gridDim.z);
+    const int L = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+    const int per = n / 8, extra = n % 8, xcd = L % 8;
+    const int item = xcd * per + min(xcd, extra) + L / 8;
+    xt = item % (int)gridDim.x;
+    h = (item / (int)gridDim.x) % (int)gridDim.y;
+    s = item / ((int)gridDim.x * (int)gridDim.y);
+  }
+  // Chunk rows of sequence s: cu_q_lens, or q_per_seq rows each when set.
+  const int q_lo = prm.q_per_seq > 0 ? s * prm.q_per_seq : cu_q_lens[s];
+  const int T = prm.q_per_seq > 0 ? prm.q_per_seq : cu_q_lens[s + 1] - q_lo;
+  const int r_wg = xt * kQRows * RT;           // first chunk row of this workgroup
+  const int ctx = checked_ctx(context_lens[s], (long)prm.max_blocks * BS, prm.err);
+#if PKV_DEBUG
+  // The chunk's rows must lie inside the query tensor, number at most
+  // max_q_len, and fit the sequence's context.
+  // (With equal chunks an empty context is allowed: its rows are zero.)
+  if (q_lo < 0 || T < 0 || (long)q_lo + T > prm.total_q || T > prm.max_q_len ||
+      (T > ctx && !(prm.q_per_seq > 0 && ctx == 0))) {
+    if (xt == 0 && h == 0 && threadIdx.x == 0) debug_flag(prm.err, kErrChunk);
+    return;
+  }
+#endif
   if (r_wg >= T) return;
-  const int ctx = context_lens[s];
   const int first_pos = ctx - T;               // absolute position of chunk row 0
   const int hkv = prm.num_kv_heads;
   const int tid = threadIdx.x;
@@ -236,7 +261,7 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
     for (int u = 0; u < PER; ++u) {
       const int pb = (wave_vec0 + u * NT) / kBlockVecs;   // block of the step, uniform
       const int lb = j * kStepBlocks + pb;
-      ids[u] = (pb < kStepBlocks && lb * BS < kv_end) ? bt[lb] : 0;
+      ids[u] = (pb < kStepBlocks && lb * BS < kv_end) ? checked_block(bt[lb], prm.num_blocks, prm.err) : 0;
     }
   };
   auto load_step = [&](int j, const int (&ids)[PER]) {
@@ -406,11 +431,13 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   }
   __syncthreads();
   if (grp > 0 || !wave_live) return;
-  // Group 0 always holds tile 0 (key 0 is visible to every row), so m_row is
-  // finite; a group that saw no key has m = -inf and weight 0.
+  // Group 0 holds tile 0 (key 0 is visible to every row), so m_row is finite
+  // whenever the context is not empty; a group that saw no key has m = -inf
+  // and weight 0. With an empty context every weight is 0 and the row is 0.
   float mx = m_row;
 #pragma unroll
   for (int k = 0; k < NG - 1; ++k) mx = fmaxf(mx, lds.merge.m[k][wl][lane]);
+  if (mx == -INFINITY) mx = 0.f;
   float wk[NG];
   wk[0] = fast_exp2(m_row - mx);
   float lsum = l_row * wk[0];
@@ -424,7 +451,7 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   // ---- normalize and store: lane writes row col, d = 16n + 4*quad .. +4 ----
   if (my_row < T) {
     uint16_t* orow = out + ((size_t)(q_lo + my_row) * hq + qh) * D;
-    const float inv = prm.v_scale / lt;
+    const float inv = lt > 0.f ? prm.v_scale / lt : 0.f;   // a row that sees no key (ctx = 0) is zero
 #pragma unroll
     for (int n = 0; n < NTILES; ++n) {
       float r[4];

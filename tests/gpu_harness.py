@@ -46,6 +46,18 @@ def raw_bits(t: torch.Tensor) -> np.ndarray:
     return t.detach().view(torch.int32).cpu().numpy().view(np.uint32)
 
 
+def workspace(ws, need: int):
+    """A fresh zero-filled decode workspace of ``need`` bytes, or the given one
+    (which must be large enough): (tensor, bytes passed to the call)."""
+    if ws is None:
+        return torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV), need
+    assert ws.numel() >= need, (ws.numel(), need)
+    return ws, ws.numel()
+
+
+COUNTER_BYTES = 4096 * 4    # completion counters at the start of every decode workspace
+
+
 class DevicePool:
     """K/V pools in HBM (one pair per layer), wrapped in a library pool handle.
 
@@ -106,7 +118,7 @@ class DevicePool:
 
     # ---- attention ----
     def decode(self, partition_size: int | None = None, query=None, tables=None, lens=None,
-               scale=None, layer: int = 0):
+               scale=None, layer: int = 0, ws=None):
         s = self.step
         bt, cl = s.decode_inputs()
         bt = bt if tables is None else tables
@@ -117,13 +129,13 @@ class DevicePool:
         part = s.partition_size if partition_size is None else partition_size
         wsb = pkv.paged_attention_decode_workspace_bytes(self.handle, nseq, s.num_q_heads,
                                                          bt.shape[1], part)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+        ws, wsb = workspace(ws, wsb)
         pkv.paged_attention_decode(self.handle, layer, out, q, int_tensor(bt), int_tensor(cl),
                                    nseq, s.num_q_heads, bt.shape[1],
                                    s.scale if scale is None else scale, part, ws, wsb)
         return out
 
-    def decode_multi(self, q_per_seq: int, partition_size: int | None = None, layer: int = 0):
+    def decode_multi(self, q_per_seq: int, partition_size: int | None = None, layer: int = 0, ws=None):
         """Several query rows per sequence: the step's prefill chunks, all of
         length q_per_seq, through paged_attention_decode_multi."""
         s = self.step
@@ -135,12 +147,12 @@ class DevicePool:
         part = s.partition_size if partition_size is None else partition_size
         wsb = pkv.paged_attention_decode_multi_workspace_bytes(self.handle, nseq, q_per_seq, s.num_q_heads,
                                                                bt.shape[1], part)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+        ws, wsb = workspace(ws, wsb)
         pkv.paged_attention_decode_multi(self.handle, layer, out, q, q_per_seq, int_tensor(bt), int_tensor(cl),
                                          nseq, s.num_q_heads, bt.shape[1], s.scale, part, ws, wsb)
         return out
 
-    def decode_shared(self, partition_size: int = 0, groups=None, prefix_lens=None, layer: int = 0):
+    def decode_shared(self, partition_size: int = 0, groups=None, prefix_lens=None, layer: int = 0, ws=None):
         """Decode through paged_attention_decode_shared with the step's sharing
         groups (``info['group_starts']``, ``info['prefix_lens']``) unless given."""
         s = self.step
@@ -152,7 +164,7 @@ class DevicePool:
         out = torch.empty((nseq, s.num_q_heads, s.head_dim), dtype=TORCH_DT[s.dtype], device=DEV)
         wsb = pkv.paged_attention_decode_shared_workspace_bytes(self.handle, nseq, s.num_q_heads,
                                                                 bt.shape[1], partition_size)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+        ws, wsb = workspace(ws, wsb)
         ng = len(gs) - 1
         max_group = int(np.max(np.diff(gs))) if ng else 1
         pkv.paged_attention_decode_shared(self.handle, layer, out, q, int_tensor(bt), int_tensor(cl),

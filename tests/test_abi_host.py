@@ -86,7 +86,8 @@ def test_workspace_sizing_and_check():
         # max context 2048 tokens, 512-token partitions -> 4 partitions per sequence
         nb = pkv.paged_attention_decode_workspace_bytes(h, 3, 32, 128, 512)
         rows = 3 * 32 * 4
-        assert nb == ((rows * 8 + 15) // 16) * 16 + rows * 128 * 4
+        counters = 4096 * 4          # completion counters at the start of every non-empty workspace
+        assert nb == counters + ((rows * 8 + 15) // 16) * 16 + rows * 128 * 4
         assert pkv.paged_attention_decode_workspace_bytes(h, 3, 32, 128, -1) == 0
         assert pkv.paged_attention_decode_workspace_bytes(h, 3, 32, 32, 512) == 0   # fits one partition
         st, msg = _status(pkv.paged_attention_decode, h, 0, 256, 256, 256, 256, 3, 32, 128, 0.1,
@@ -131,10 +132,12 @@ def test_multi_query_decode_checks():
         assert one == pkv.paged_attention_decode_workspace_bytes(h, 3, 32, 128, 512)
         rows = 3 * 32 * 4 * 4
         assert pkv.paged_attention_decode_multi_workspace_bytes(h, 3, 4, 32, 128, 512) == \
-            ((rows * 8 + 15) // 16) * 16 + rows * 128 * 4
+            4096 * 4 + ((rows * 8 + 15) // 16) * 16 + rows * 128 * 4
         assert _status(pkv.paged_attention_decode_multi_workspace_bytes, h, 3, 0, 32, 128, 512)[0] == -1
-        # rows x heads per KV head must fit the 16 matrix-core columns
-        assert _status(pkv.paged_attention_decode_multi, h, 0, 16, 16, 5, 16, 16, 1, 32, 4, 1.0)[0] == -2
+        # more rows x heads per KV head than the 16 matrix-core columns: run as
+        # equal-length prefill chunks, which need no workspace
+        assert pkv.paged_attention_decode_multi_workspace_bytes(h, 3, 5, 32, 128, 0) == 0
+        assert pkv.paged_attention_decode_multi_workspace_bytes(h, 3, 16, 32, 128, 512) == 0
         assert _status(pkv.paged_attention_decode_multi, h, 0, 16, 16, 0, 16, 16, 1, 32, 4, 1.0)[0] == -1
         # fp32 pools take one query row per sequence only
         st, msg = _status(pkv.paged_attention_decode_multi, hf, 0, 16, 16, 2, 16, 16, 1, 32, 4, 1.0)
@@ -160,14 +163,15 @@ def test_shared_prefix_decode_checks():
     h = pkv.kv_pool_create(1, 4096, 16, 8, 128, pkv.BF16, [256], [512])
     hf = pkv.kv_pool_create(1, 64, 16, 8, 128, pkv.F32, [256], [512])
     try:
-        # workspace: summaries of every (sequence, head, 512-token piece),
-        # one int32 per sequence, then the balanced split's slots (two per
-        # wave, G heads each) and descriptors; at most one wave per window
+        # workspace: completion counters, summaries of every (sequence, head,
+        # 512-token piece), one int32 per sequence, then the balanced split's
+        # slots (two per wave, G heads each) and descriptors; at most one wave
+        # per window
         rows = 3 * 32 * 4                                         # 128 blocks = 2048 tokens = 4 pieces
         waves = 3 * 8 * 2048 // 64
         r16 = lambda x: (x + 15) // 16 * 16
-        want = (r16(rows * 8) + rows * 128 * 4 + 16 + r16(waves * 2 * 4 * 8) + waves * 2 * 4 * 128 * 4 +
-                waves * 2 * 32)
+        want = (4096 * 4 + r16(rows * 8) + rows * 128 * 4 + 16 + r16(waves * 2 * 4 * 8) +
+                waves * 2 * 4 * 128 * 4 + waves * 2 * 32)
         assert pkv.paged_attention_decode_shared_workspace_bytes(h, 3, 32, 128, 0) == want
         assert pkv.paged_attention_decode_shared_workspace_bytes(h, 3, 32, 128, 512) == want
         assert pkv.paged_attention_decode_shared_workspace_bytes(h, 3, 32, 128, 256) > want
@@ -210,3 +214,19 @@ def test_fused_append_decode_checks():
     finally:
         pkv.kv_pool_destroy(h)
         pkv.kv_pool_destroy(hf)
+
+
+def test_enum_arguments_outside_their_range_are_rejected():
+    # values outside pkv_dtype / pkv_kernel_kind are read as integers and rejected
+    assert _status(pkv.kv_pool_create, 1, 4, 16, 1, 64, 5, [256], [512])[0] == -1
+    assert _status(pkv.kv_pool_create, 1, 4, 16, 1, 64, -3, [256], [512])[0] == -1
+    for kind in (-1, 5, 1 << 20):
+        assert _status(pkv.pkv_timing_read, kind)[0] == -1
+        assert _status(pkv.pkv_timing_read_launches, kind, 4)[0] == -1
+
+
+def test_debug_read_errors_in_the_release_library():
+    if os.environ.get("PKV_LIBRARY_PATH"):
+        pytest.skip("a substitute library is loaded")
+    st, msg = _status(pkv.pkv_debug_read_errors)
+    assert st == -2 and "PKV_DEBUG" in msg

@@ -1,9 +1,8 @@
 """GPU parity with 32-token blocks against the CPU oracle.
 
-The pages call sixteen tokens a common block size and note that thirty-two
-is often better on workloads dominated by very long generations ("The
-Serving Playbook", "The block table lives in the hottest kernel in the
-system"). bf16 and e4m3 pools take block_size 32. The pool layout is that of
+The pages treat 16 tokens as the usual block size and favour 32 when the
+traffic is mostly long generations ("The Serving Playbook", "The block table
+lives in the hottest kernel in the system"). bf16 and e4m3 pools take block_size 32. The pool layout is that of
 16-token blocks with 32 tokens per vector run: K [blocks][Hkv][D/x][32][x],
 V [blocks][Hkv][32][D].
 

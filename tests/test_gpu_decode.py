@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
     import full_refs
-    from gpu_harness import DevicePool, POISON_BITS, assert_close, int_tensor, to_device, to_f32
+    from gpu_harness import COUNTER_BYTES, DevicePool, POISON_BITS, assert_close, int_tensor, to_device, to_f32
 
 
 def oracle_decode(step, seqs=None, lens=None, tables=None, query=None, scale=None):
@@ -217,3 +217,41 @@ def test_decode_poisoned_unused_entries():
     assert (step.block_tables[0, 1:] == step.poison_block).all()
     run_and_check(step)
     run_and_check(step, partition_size=64)
+
+
+def test_decode_workspace_reuse_counters_return_to_zero():
+    """One zero-filled workspace serves a run of decode calls of different
+    batches, splits and variants. The completion counters at its start are
+    zero after every call, and every output matches the oracle. The contexts
+    make rows that span many wavefronts' shares and shares that are empty."""
+    a = W.custom("ws_a", seed=520, dtype="bf16", hq=32, hkv=8, d=128, ctx=[3000, 1, 700, 5000, 64, 0, 129])
+    rng = np.random.default_rng(521)
+    b = W.custom("ws_b", seed=522, dtype="bf16", hq=8, hkv=2, d=64,
+                 ctx=rng.integers(1, 2500, size=64).tolist())
+    c = W.custom("ws_c", seed=523, dtype="bf16", hq=32, hkv=8, d=128, ctx=[900, 3, 4100], q_lens=[3, 3, 3])
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda:0")
+    pools = {}
+    for step in (a, b, c):
+        pools[step.name] = DevicePool(step)
+        pools[step.name].fill()
+    refs = {a.name: oracle_decode(a), b.name: oracle_decode(b)}
+    for step, part in [(a, 0), (b, 0), (a, 128), (b, -1), (a, 0), (b, 64), (b, 0)]:
+        out = to_f32(pools[step.name].decode(part, ws=ws))
+        torch.cuda.synchronize()
+        assert not ws[:COUNTER_BYTES].any(), f"{step.name} part={part}: counters left non-zero"
+        assert_close(out, refs[step.name], "bf16", f"{step.name} part={part}")
+    # several query rows per sequence (combined by the separate reduction), then plain decode again
+    out = to_f32(pools[c.name].decode_multi(3, 0, ws=ws))
+    torch.cuda.synchronize()
+    assert not ws[:COUNTER_BYTES].any()
+    pk = oracle.new_pool(c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
+    pv = oracle.new_pool(c.num_blocks, c.block_size, c.num_kv_heads, c.head_dim)
+    oracle.append(pk, pv, c.cached_key.f32, c.cached_value.f32, c.cached_slots)
+    oracle.append(pk, pv, c.new_key.f32, c.new_value.f32, c.new_slots)
+    bt, cl = c.prefill_inputs()
+    assert_close(out, oracle.paged_prefill_chunk(c.prefill_query.f32, c.cu_q_lens, pk, pv, bt, cl, c.scale),
+                 "bf16", "multi")
+    out = to_f32(pools[a.name].decode(0, ws=ws))
+    torch.cuda.synchronize()
+    assert not ws[:COUNTER_BYTES].any()
+    assert_close(out, refs[a.name], "bf16", "a after multi")

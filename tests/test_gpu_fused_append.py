@@ -29,7 +29,7 @@ def _fused(pool, step, part):
     nseq = len(cl)
     out = torch.empty((nseq, s.num_q_heads, s.head_dim), dtype=TORCH_DT[s.dtype], device=DEV)
     wsb = pkv.paged_attention_decode_workspace_bytes(pool.handle, nseq, s.num_q_heads, bt.shape[1], part)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=DEV)
     # the step's new rows in sequence order (one per sequence with ctx >= 1)
     hkv, d = s.num_kv_heads, s.head_dim
     k = np.zeros((nseq, hkv, d), np.uint16)

@@ -53,7 +53,7 @@ def test_captured_step_matches_eager(kv, tq):
     nseq = len(cl)
     wsb = pkv.paged_attention_decode_multi_workspace_bytes(pool.handle, nseq, tq, step.num_q_heads,
                                                            bt.shape[1], 0)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=DEV)
     out_eager = torch.empty((nseq * tq, step.num_q_heads, step.head_dim), dtype=torch.bfloat16, device=DEV)
     out_graph = torch.empty_like(out_eager)
     run_eager, _ = _step_fn(pool, step, kv, ws, out_eager, tq)
@@ -118,7 +118,7 @@ def test_captured_shared_prefix_decode_matches_eager():
     gs, pl = int_tensor(step.info["group_starts"]), int_tensor(step.info["prefix_lens"])
     max_group = int(np.max(np.diff(step.info["group_starts"])))
     wsb = pkv.paged_attention_decode_shared_workspace_bytes(pool.handle, nseq, step.num_q_heads, bt.shape[1], 0)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=DEV)
     k_new, v_new = to_device(step.new_key), to_device(step.new_value)
     slots = int_tensor(step.new_slots, torch.int64)
     q, bt_d, cl_d = to_device(step.decode_query), int_tensor(bt), int_tensor(cl)
@@ -143,7 +143,7 @@ def test_captured_block32_step_matches_eager():
     bt, cl = step.decode_inputs()
     nseq = len(cl)
     wsb = pkv.paged_attention_decode_multi_workspace_bytes(pool.handle, nseq, 1, step.num_q_heads, bt.shape[1], 0)
-    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(wsb, 16), dtype=torch.uint8, device=DEV)
     outs = [torch.empty((nseq, step.num_q_heads, step.head_dim), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
     run_eager, _ = _step_fn(pool, step, "bf16", ws, outs[0], 1)
     run_graph, _ = _step_fn(pool, step, "bf16", ws, outs[1], 1)

@@ -17,7 +17,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from gpu_harness import DevicePool, assert_close, to_device, to_f32
+    import paged_kv_decode_reshape_amd as pkv
+    from gpu_harness import DevicePool, assert_close, int_tensor, to_device, to_f32
 
 
 def oracle_multi(step, k_scale=None, v_scale=None, rows=None):
@@ -87,3 +88,34 @@ def test_multi_llama8b_b256_lognormal():
     out = to_f32(pool.decode_multi(4, 0))
     torch.cuda.synchronize()
     assert_close(out, oracle_multi(step), "bf16", step.name)
+
+
+@pytest.mark.parametrize("hq,hkv,tq,kv", [
+    (32, 8, 5, "bf16"), (32, 8, 6, "bf16"), (32, 8, 7, "bf16"), (32, 8, 8, "bf16"),
+    (64, 8, 3, "bf16"), (64, 8, 4, "bf16"), (32, 8, 8, "fp8"), (64, 8, 3, "fp8"), (16, 16, 17, "bf16")])
+def test_multi_more_rows_than_one_tile(hq, hkv, tq, kv):
+    """queries_per_seq x (query heads per KV head) > 16: the rows of a
+    sequence run as an equal-length chunk on the prefill-chunk kernel.
+    Speculative verification of up to 7 draft tokens at G = 4 and 3 at G = 8;
+    an empty context gives zero rows."""
+    ctx = [0, tq, tq + 1, 16, 17, 63, 64, 65, 300, 1000, 2500]
+    step = W.custom(f"mq_big{hq}_{hkv}_{tq}_{kv}", seed=870 + hq + tq, dtype="bf16", hq=hq, hkv=hkv, d=128,
+                    ctx=[c for c in ctx if c >= tq], q_lens=[tq] * len([c for c in ctx if c >= tq]))
+    ks, vs = (1.0 / 96, 1.0 / 32) if kv == "fp8" else (None, None)
+    pool = DevicePool(step, kv=kv, k_scales=None if ks is None else [ks], v_scales=None if vs is None else [vs])
+    pool.fill()
+    out = to_f32(pool.decode_multi(tq, 0))
+    torch.cuda.synchronize()
+    assert_close(out, oracle_multi(step, ks, vs), "bf16", step.name)
+    # an empty context: zero rows
+    bt, cl = step.prefill_inputs()
+    cl0 = cl.copy()
+    cl0[0] = 0
+    q = to_device(step.prefill_query)
+    nseq = len(cl)
+    o2 = torch.full((nseq * tq, hq, 128), 3.0, dtype=torch.bfloat16, device="cuda:0")
+    pkv.paged_attention_decode_multi(pool.handle, 0, o2, q, tq, int_tensor(bt), int_tensor(cl0), nseq, hq,
+                                     bt.shape[1], step.scale, 0, None, 0)
+    torch.cuda.synchronize()
+    assert (o2[:tq].float() == 0).all()
+    assert_close(to_f32(o2[tq:]), out[tq:], "bf16", "rows after the empty context")

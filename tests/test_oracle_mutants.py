@@ -25,7 +25,8 @@ MUTANTS = {
     "v_uses_k": ("out[i] = _softmax_row(s) @ v[:, h, :]", "out[i] = _softmax_row(s) @ k[:, h, :]"),
     "combine_no_rescale": ("w1 = np.exp(m1 - m) * l1", "w1 = l1"),
     "combine_wrong_sign": ("w2 = np.exp(m2 - m) * l2", "w2 = np.exp(m - m2) * l2"),
-    "kv_bytes_no_factor_two": ("return 2 * layers", "return layers"),
+    "kv_bytes_no_factor_two": ("vectors_per_token = 2 * layers * kv_heads", "vectors_per_token = layers * kv_heads"),
+    "kv_bytes_dtype_dropped": ("bytes_per_vector = head_dim * dtype_bytes", "bytes_per_vector = head_dim"),
     "blocks_floor": ("return (int(ctx) + block_size - 1) // block_size", "return int(ctx) // block_size"),
     "negative_slots_written": ("keep = slots >= 0", "keep = slots >= -1"),
     "copy_reversed": ("pool_k[dst] = pool_k[src]\n        pool_v[dst] = pool_v[src]",
