@@ -198,6 +198,24 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
                                   int partition_size, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * computation as paged_attention_decode (same arguments minus the workspace,
+ * same kernels, same results), with the workspace in a library-owned device
+ * array of 36 MiB (each GPU the library runs on holds one until the process
+ * ends). It allocates nothing and calls no allocating routine. Calls whose
+ * workspace (paged_attention_decode_workspace_bytes) exceeds 36 MiB return
+ * PKV_ERR_WORKSPACE; the balanced split (partition_size 0) of up to 4096
+ * sequences with up to 8 query heads per KV head at head_dim 128 needs at
+ * most ~33 MiB. Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams, or host threads enqueueing
+ * without ordering) race and give undefined results; calls ordered on one
+ * stream are safe. */
+pkv_status paged_attention_decode_noalloc(const pkv_pool* pool, int layer, void* out, const void* query,
+                                          const int32_t* block_tables, const int32_t* context_lens,
+                                          int num_seqs, int num_q_heads, int max_blocks_per_seq, float scale,
+                                          int partition_size, void* stream);
+
 /* Append and decode in one call, for latency-bound steps: the same result as
  * reshape_and_cache of each sequence's new token at position
  * context_lens[b] - 1 (slot block_tables[b][(ctx-1) / block_size] *

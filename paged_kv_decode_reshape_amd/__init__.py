@@ -21,7 +21,8 @@ __all__ = [
     "KERNEL_DECODE_REDUCE", "KERNEL_PREFILL", "KERNEL_DECODE_PREFIX", "library_path", "load",
     "kv_pool_bytes", "kv_pool_create", "kv_pool_set_fp8_scales", "kv_pool_destroy",
     "reshape_and_cache", "copy_blocks",
-    "paged_attention_decode_workspace_bytes", "paged_attention_decode", "paged_attention_decode_append",
+    "paged_attention_decode_workspace_bytes", "paged_attention_decode", "paged_attention_decode_noalloc",
+    "paged_attention_decode_append",
     "paged_attention_decode_multi_workspace_bytes", "paged_attention_decode_multi",
     "paged_attention_decode_shared_workspace_bytes", "paged_attention_decode_shared",
     "paged_attention_prefill_chunk", "pkv_timing_enable", "pkv_timing_disable",
@@ -63,6 +64,8 @@ _SIGNATURES = {
     "paged_attention_decode": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_int, c_int, c_int, c_float, c_int, c_void_p, c_size_t,
                                        c_void_p]),
+    "paged_attention_decode_noalloc": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                               c_int, c_int, c_int, c_float, c_int, c_void_p]),
     "paged_attention_decode_append": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_int, c_int, c_int, c_float, c_int,
                                               c_void_p, c_size_t, c_void_p]),
@@ -222,6 +225,14 @@ def paged_attention_decode(pool, layer, out, query, block_tables, context_lens, 
                                          _ptr(context_lens), num_seqs, num_q_heads,
                                          max_blocks_per_seq, float(scale), partition_size,
                                          _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def paged_attention_decode_noalloc(pool, layer, out, query, block_tables, context_lens, num_seqs,
+                                   num_q_heads, max_blocks_per_seq, scale, partition_size=0, stream=None):
+    _check(load().paged_attention_decode_noalloc(pool, layer, _ptr(out), _ptr(query), _ptr(block_tables),
+                                                 _ptr(context_lens), num_seqs, num_q_heads,
+                                                 max_blocks_per_seq, float(scale), partition_size,
+                                                 _stream(stream)))
 
 
 def paged_attention_decode_append(pool, layer, out, query, key, value, block_tables, context_lens, num_seqs,

@@ -194,6 +194,40 @@ uint32_t* debug_error_word() {
 #endif
 }
 
+// ---- allocation-free decode: a library-owned scratch workspace ----
+// paged_attention_decode_noalloc runs paged_attention_decode with this array
+// as its workspace. Each GPU the library runs on holds its own copy of the
+// array until the process ends; its first kCounterBytes (the completion
+// counters) start zero at load and every completed call leaves them zero.
+// Host code never uses the array's name as an address: the device address of
+// the current device's copy comes from hipGetSymbolAddress, looked up once per
+// device and kept.
+constexpr size_t kScratchBytes = (size_t)36 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of the current device's scratch array, or NULL (with the
+// error recorded) when it cannot be resolved.
+void* scratch_address() {
+  static std::mutex mu;
+  static void* cached[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    cached[dev] = ptr;
+  }
+  return cached[dev];
+}
+
 // ---- kernel timing ----
 struct TimingState {
   std::mutex mu;
@@ -691,6 +725,30 @@ pkv_status paged_attention_decode(const pkv_pool* pool, int layer, void* out,
                                   size_t workspace_bytes, void* stream) {
   return decode_run(pool, layer, out, query, 1, block_tables, context_lens, num_seqs, num_q_heads,
                     max_blocks_per_seq, scale, partition_size, workspace, workspace_bytes, stream);
+}
+
+pkv_status paged_attention_decode_noalloc(const pkv_pool* pool, int layer, void* out, const void* query,
+                                          const int32_t* block_tables, const int32_t* context_lens,
+                                          int num_seqs, int num_q_heads, int max_blocks_per_seq, float scale,
+                                          int partition_size, void* stream) {
+  size_t need = 0;
+  pkv_status st = check_pool_layer(pool, layer);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_seqs == 0) return PKV_OK;
+  st = decode_workspace(pool, num_seqs, 1, num_q_heads, max_blocks_per_seq, partition_size, &need);
+  if (st != PKV_OK) return st;
+  if (need > kScratchBytes)
+    return fail(PKV_ERR_WORKSPACE,
+                "this call needs a %zu-byte workspace, more than the %zu bytes of the library's scratch array; "
+                "use paged_attention_decode with a caller workspace", need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_address();
+    if (ws == nullptr) return fail(PKV_ERR_HIP, "hipGetSymbolAddress of the scratch array failed");
+  }
+  return decode_run(pool, layer, out, query, 1, block_tables, context_lens, num_seqs, num_q_heads,
+                    max_blocks_per_seq, scale, partition_size, ws, need, stream);
 }
 
 pkv_status paged_attention_decode_append(const pkv_pool* pool, int layer, void* out, const void* query,
