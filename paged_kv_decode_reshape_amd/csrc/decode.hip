@@ -843,19 +843,26 @@ __device__ __forceinline__ auto run_seg(const DecodeArgs& a, SegLds<T, D, G>& ld
   }
 }
 
-template <typename T, int D, int G>
+// Resident wavefronts per SIMD a decode kernel is built for. The one-row
+// matrix-core kernels (bf16, e4m3) fit 168 VGPRs: three waves per SIMD,
+// which the gather needs to keep enough loads in flight. The bf16 variants at
+// head_dim 128 that carry more state per wave (several query rows, shared
+// prefixes, the fused append, 32-token blocks) do not fit 168 without
+// spilling to scratch and are built for 256 (two waves). fp32 lane-per-token
+// segments: two, or one from 5 query heads per KV head on, whose per-head
+// accumulators do not fit 256.
+template <typename T, int D, int G, bool MQ = false, bool SH = false, int BS = kBlockSize, bool AP = false>
 constexpr int decode_waves_per_simd() {
-  // Matrix-core segments (bf16, e4m3) fit 168 VGPRs: three waves per SIMD,
-  // which the gather needs to keep enough loads in flight. fp32
-  // lane-per-token segments: two.
-  return sizeof(T) <= 2 ? 3 : 2;
+  if constexpr (sizeof(T) == 4) return (D == 128 && G >= 5) ? 1 : 2;
+  if constexpr (sizeof(T) == 2 && D == 128 && (MQ || SH || AP || BS != kBlockSize)) return 2;
+  return 3;
 }
 
 // ---------------------------------------------------------------------------
 // Fixed partitions: one wavefront per (b, h, partition).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int G, bool MQ, int BS, bool AP>
-__global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_partition_kernel(
+__global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, false, BS, AP>())) void decode_partition_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
   using TQ = typename IoType<T>::type;
@@ -949,7 +956,7 @@ __device__ __forceinline__ int group_shared_tokens(const int32_t* __restrict__ c
 }
 
 template <typename T, int D, int G, int BS>
-__global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_prefix_kernel(
+__global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, false, true, BS, false>())) void decode_prefix_kernel(
     const int32_t* __restrict__ context_lens, DecodeArgs args, DecodeParams prm) {
   __shared__ MfmaWaveLds<D> lds[4];
   constexpr int MPW = prefix_members_per_wave(G);
@@ -1270,7 +1277,7 @@ __device__ __forceinline__ void combine_split_row(TQ* out_row, const float* ws_m
 // counter back to zero, so the counters are zero between calls. Otherwise the
 // slot descriptors are written and decode_balanced_reduce_kernel combines.
 template <typename T, int D, int G, bool MQ, bool SH, int BS, bool AP>
-__global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decode_balanced_kernel(
+__global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP>())) void decode_balanced_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
     SlotDesc* __restrict__ ws_desc, const int32_t* __restrict__ context_lens, DecodeArgs args,
     DecodeParams prm) {
@@ -1323,8 +1330,6 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
   if (wid >= nw) return;
   SlotDesc desc[2];
   desc[0].row = desc[1].row = -1;
-  struct Pending { int row, row_start, windows, row_windows; } pend[2];   // split pieces to count (FC)
-  pend[0].row = pend[1].row = -1;
   const int x0 = total ? share_begin(wid, nw, total) : 0;
   const int x1 = total ? share_begin(wid + 1, nw, total) : 0;
   // The hardware issues the oldest wavefront first. With equal shares that
@@ -1365,56 +1370,48 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G>())) void decod
       const int slot = (x == x0) ? 0 : 1;
       // A slot holds nq * G summary rows, column (row j, head g) at j * G + g.
       const size_t base = ((size_t)wid * 2 + slot) * nq * G;
-      if (FC) {
-        write_partial<T, D, G, kCanFuse>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st,
-                                         args.v_scale, nq, G);
-      } else {
-        write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st, args.v_scale,
-                               nq, G);
-      }
-      if (FC) {
-        // Counted after the share's last segment (below), which keeps the
-        // combine's registers out of the segment loop.
-        const Pending p{__builtin_amdgcn_readfirstlane(b * args.hkv + h), __builtin_amdgcn_readfirstlane(x - w0),
-                        __builtin_amdgcn_readfirstlane(w1 - w0), __builtin_amdgcn_readfirstlane(nwb)};
-        if (slot == 0) pend[0] = p; else pend[1] = p;
-      } else {
-        desc[slot].row = b * args.hkv + h;
-        desc[slot].row_start = x - w0;
-        desc[slot].w0 = w0;
-        desc[slot].w1 = w1;
-        desc[slot].row_windows = nwb;
-        desc[slot].total = total;
-      }
+      // One query row, no shared prefixes: device-scope stores, so that a
+      // wavefront of this launch can combine the piece (either way the
+      // reduction kernel reads it after the launch).
+      write_partial<T, D, G, kCanFuse>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st,
+                                       args.v_scale, nq, G);
+      desc[slot].row = b * args.hkv + h;
+      desc[slot].row_start = x - w0;
+      desc[slot].w0 = w0;
+      desc[slot].w1 = w1;
+      desc[slot].row_windows = nwb;
+      desc[slot].total = total;
     }
     x += w1 - w0;
   }
   if (FC) {
-    // Count this wave's split pieces towards their rows' totals; the wave
-    // that completes a row combines it and zeroes its counter. The counter of
-    // a row is entry f of prm.counters, f = the wave whose share holds the
-    // row's first window.
-    if (pend[0].row >= 0 || pend[1].row >= 0) {
+    // Count this wave's split pieces (its slot descriptors) towards their
+    // rows' totals, after the share's last segment so that the combine's
+    // registers stay out of the segment loop; the wave that completes a row
+    // combines it and zeroes its counter. The counter of a row is entry f of
+    // prm.counters, f = the wave whose share holds the row's first window.
+    if (desc[0].row >= 0 || desc[1].row >= 0) {
       wait_stores_complete();                            // the summaries are published before they count
       bool mine[2] = {false, false};
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        if (pend[k].row < 0) continue;
-        const long f = share_of(pend[k].row_start, nw, total);
+        if (desc[k].row < 0) continue;
+        const long f = share_of(desc[k].row_start, nw, total);
+        const int windows = desc[k].w1 - desc[k].w0;
         int old = 0;
-        if (lane == 0) old = atomicAdd(prm.counters + f, pend[k].windows);
+        if (lane == 0) old = atomicAdd(prm.counters + f, windows);
         old = __builtin_amdgcn_readfirstlane(old);
-        mine[k] = old + pend[k].windows == pend[k].row_windows;   // every other piece is published
+        mine[k] = old + windows == desc[k].row_windows;  // every other piece is published
       }
       if (mine[0] || mine[1]) {
         asm volatile("" ::: "memory");                   // the pieces are read after the count
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           if (!mine[k]) continue;
-          const int row_start = pend[k].row_start;
+          const int row_start = desc[k].row_start;
           const long f = share_of(row_start, nw, total);
-          const long last = share_of((long)row_start + pend[k].row_windows - 1, nw, total);
-          const int b = pend[k].row / args.hkv, h = pend[k].row % args.hkv;
+          const long last = share_of((long)row_start + desc[k].row_windows - 1, nw, total);
+          const int b = desc[k].row / args.hkv, h = desc[k].row % args.hkv;
           combine_split_row<TQ, D, G>(out_ptr + ((size_t)b * args.hkv + h) * G * D, ws_ml, ws_o, f,
                                       share_begin(f, nw, total) == row_start ? 0 : 1, last, nw, total);
           if (lane == 0) atomicExch(prm.counters + f, 0);
@@ -1788,22 +1785,6 @@ hipError_t launch_decode_tg(const DecodeParams& prm, hipStream_t stream, const K
   return launch_decode_tgm<T, D, G, false, kBlockSize>(prm, stream, timer);
 }
 
-template <typename T, int D, int G, bool MQ>
-int balanced_waves_per_cu() {
-  static int cached = 0;
-  if (cached == 0) {
-    int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ, false, kBlockSize, false>, 256, 0) !=
-            hipSuccess ||
-        blocks <= 0) {
-      (void)hipGetLastError();
-      blocks = decode_waves_per_simd<T, D, G>();
-    }
-    cached = 4 * blocks;
-  }
-  return cached;
-}
-
 template <typename T, int D>
 hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream, const KernelTimer& timer) {
   switch (prm.group) {
@@ -1819,27 +1800,52 @@ hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream, const Ke
   }
 }
 
-template <typename T, int D, bool MQ>
-int waves_per_cu_tm(int group) {
-  switch (group) {
-    case 1: return balanced_waves_per_cu<T, D, 1, MQ>();
-    case 2: return balanced_waves_per_cu<T, D, 2, MQ>();
-    case 3: return balanced_waves_per_cu<T, D, 3, MQ>();
-    case 4: return balanced_waves_per_cu<T, D, 4, MQ>();
-    case 5: return balanced_waves_per_cu<T, D, 5, MQ>();
-    case 6: return balanced_waves_per_cu<T, D, 6, MQ>();
-    case 7: return balanced_waves_per_cu<T, D, 7, MQ>();
-    case 8: return balanced_waves_per_cu<T, D, 8, MQ>();
-    default: return 8;
+// Resident wavefronts per CU of one balanced-kernel variant (cached).
+template <typename T, int D, int G, bool MQ, bool SH, int BS, bool AP>
+int balanced_waves_per_cu() {
+  static int cached = 0;
+  if (cached == 0) {
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ, SH, BS, AP>, 256, 0) !=
+            hipSuccess ||
+        blocks <= 0) {
+      (void)hipGetLastError();
+      blocks = decode_waves_per_simd<T, D, G, MQ, SH, BS, AP>();
+    }
+    cached = 4 * blocks;
   }
+  return cached;
+}
+
+template <typename T, int D, int G>
+int waves_per_cu_tg(const BalancedVariant& v) {
+  if constexpr (UsesMfma<T>::value) {
+    if (v.block_size == 32) {
+      if (v.multi) return balanced_waves_per_cu<T, D, G, true, false, 32, false>();
+      if (v.shared) return balanced_waves_per_cu<T, D, G, false, true, 32, false>();
+      if (v.append) return balanced_waves_per_cu<T, D, G, false, false, 32, true>();
+      return balanced_waves_per_cu<T, D, G, false, false, 32, false>();
+    }
+    if (v.multi) return balanced_waves_per_cu<T, D, G, true, false, kBlockSize, false>();
+    if (v.shared) return balanced_waves_per_cu<T, D, G, false, true, kBlockSize, false>();
+    if (v.append) return balanced_waves_per_cu<T, D, G, false, false, kBlockSize, true>();
+  }
+  return balanced_waves_per_cu<T, D, G, false, false, kBlockSize, false>();
 }
 
 template <typename T, int D>
-int waves_per_cu_t(int group, bool multi) {
-  if constexpr (UsesMfma<T>::value) {
-    if (multi) return waves_per_cu_tm<T, D, true>(group);
+int waves_per_cu_t(const BalancedVariant& v) {
+  switch (v.group) {
+    case 1: return waves_per_cu_tg<T, D, 1>(v);
+    case 2: return waves_per_cu_tg<T, D, 2>(v);
+    case 3: return waves_per_cu_tg<T, D, 3>(v);
+    case 4: return waves_per_cu_tg<T, D, 4>(v);
+    case 5: return waves_per_cu_tg<T, D, 5>(v);
+    case 6: return waves_per_cu_tg<T, D, 6>(v);
+    case 7: return waves_per_cu_tg<T, D, 7>(v);
+    case 8: return waves_per_cu_tg<T, D, 8>(v);
+    default: return 8;
   }
-  return waves_per_cu_tm<T, D, false>(group);
 }
 
 }  // namespace
@@ -1848,12 +1854,12 @@ int decode_balanced_max_seqs() { return kMaxBalancedSeqs; }
 
 size_t decode_balanced_desc_bytes() { return sizeof(SlotDesc); }
 
-int decode_balanced_waves_per_cu(PoolType type, int head_dim, int group, bool multi) {
+int decode_balanced_waves_per_cu(PoolType type, int head_dim, const BalancedVariant& v) {
   if (type == PoolType::kFP8)
-    return head_dim == 128 ? waves_per_cu_t<uint8_t, 128>(group, multi) : waves_per_cu_t<uint8_t, 64>(group, multi);
+    return head_dim == 128 ? waves_per_cu_t<uint8_t, 128>(v) : waves_per_cu_t<uint8_t, 64>(v);
   if (type == PoolType::kBF16)
-    return head_dim == 128 ? waves_per_cu_t<uint16_t, 128>(group, multi) : waves_per_cu_t<uint16_t, 64>(group, multi);
-  return head_dim == 128 ? waves_per_cu_t<float, 128>(group, false) : waves_per_cu_t<float, 64>(group, false);
+    return head_dim == 128 ? waves_per_cu_t<uint16_t, 128>(v) : waves_per_cu_t<uint16_t, 64>(v);
+  return head_dim == 128 ? waves_per_cu_t<float, 128>(v) : waves_per_cu_t<float, 64>(v);
 }
 
 hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,

@@ -465,7 +465,10 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
   const pkv::PoolType type = pool_type(pool->dtype);
   int num_waves = 0;
   if (sp.balanced) {
-    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, group, q_per_seq > 1);
+    // The fused append is sized like plain decode (not by its own occupancy)
+    // so that both split the rows identically and give bit-identical outputs.
+    const pkv::BalancedVariant v{group, q_per_seq > 1, false, false, pool->block_size};
+    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, v);
     num_waves = (int)std::max(1L, std::min(sp.wave_cap, slots));
   } else {
     const long units = (long)pool->num_kv_heads * num_seqs * sp.max_parts;
@@ -642,7 +645,8 @@ pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* 
     ws_ml = reinterpret_cast<float*>(ws + lay.off_ml);
     ws_o = reinterpret_cast<float*>(ws + lay.off_o);
     ws_desc = ws + lay.off_desc;
-    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, group, false);
+    const pkv::BalancedVariant v{group, false, true, false, pool->block_size};
+    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, v);
     num_waves = (int)std::max(1L, std::min(lay.own.wave_cap, slots));
   }
   pkv::DecodeParams prm{};

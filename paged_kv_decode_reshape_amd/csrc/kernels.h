@@ -129,10 +129,17 @@ struct CopyParams {
 hipError_t launch_copy_blocks(const CopyParams& prm, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer);
-// Balanced decode: resident wavefronts per CU of its kernel (multi: the
-// several-query-rows variant), the largest batch its in-LDS prefix sum
-// handles, and the size of one slot descriptor.
-int decode_balanced_waves_per_cu(PoolType type, int head_dim, int group, bool multi);
+// Balanced decode: resident wavefronts per CU of the kernel variant a call
+// runs, the largest batch its in-LDS prefix sum handles, and the size of one
+// slot descriptor.
+struct BalancedVariant {
+  int group;         // query heads per KV head
+  bool multi;        // several query rows per sequence
+  bool shared;       // shared-prefix decode (own tokens)
+  bool append;       // fused append
+  int block_size;    // 16 or 32
+};
+int decode_balanced_waves_per_cu(PoolType type, int head_dim, const BalancedVariant& v);
 int decode_balanced_max_seqs();
 size_t decode_balanced_desc_bytes();
 hipError_t launch_prefill(const PrefillParams& prm, PoolType type, hipStream_t stream, const KernelTimer& timer);

@@ -65,8 +65,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // at least 4 so that K/V staging is spread over enough threads.
 __host__ __device__ constexpr int prefill_row_subtiles(int g) { return (g <= 4 && 4 % g == 0) ? 4 / g : 1; }
 // Groups of waves per workgroup (each takes every NG-th key tile): three when a
-// group has at most 4 waves (12 waves, 3 per SIMD), else two.
-__host__ __device__ constexpr int prefill_groups(int g) { return g * prefill_row_subtiles(g) <= 4 ? 3 : 2; }
+// group has at most 4 waves (12 waves, 3 per SIMD), else two. G = 3 takes two
+// (6 waves) and G = 7 one (7 waves), for 256 VGPRs per wave: with more waves
+// per SIMD their bf16 kernels spill to scratch.
+__host__ __device__ constexpr int prefill_groups(int g) {
+  return g == 7 ? 1 : (g * prefill_row_subtiles(g) <= 4 && g != 3) ? 3 : 2;
+}
 
 template <int D, int NWG, int NG, int BS>
 union PrefillLds {
@@ -78,9 +82,9 @@ union PrefillLds {
     alignas(16) uint16_t v[NG][kKeyTile][kVStride];                     // V tiles, [key][head dim]
   } tile;
   struct {                                                               // groups 1.., at the end
-    alignas(16) float o[NG - 1][NWG][D / 16][4][kWave];
-    float m[NG - 1][NWG][kWave];
-    float l[NG - 1][NWG][kWave];
+    alignas(16) float o[NG > 1 ? NG - 1 : 1][NWG][D / 16][4][kWave];
+    float m[NG > 1 ? NG - 1 : 1][NWG][kWave];
+    float l[NG > 1 ? NG - 1 : 1][NWG][kWave];
   } merge;
 };
 
