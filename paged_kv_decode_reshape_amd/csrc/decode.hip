@@ -843,18 +843,19 @@ __device__ __forceinline__ auto run_seg(const DecodeArgs& a, SegLds<T, D, G>& ld
   }
 }
 
-// Resident wavefronts per SIMD a decode kernel is built for. The one-row
-// matrix-core kernels (bf16, e4m3) fit 168 VGPRs: three waves per SIMD,
-// which the gather needs to keep enough loads in flight. The bf16 variants at
-// head_dim 128 that carry more state per wave (several query rows, shared
-// prefixes, the fused append, 32-token blocks) do not fit 168 without
-// spilling to scratch and are built for 256 (two waves). fp32 lane-per-token
+// Resident wavefronts per SIMD a decode kernel is built for. bf16 matrix-core
+// kernels at head_dim 128: two (256 VGPRs). At three (168 VGPRs) the one-row
+// kernel just fits and its variants (several query rows, shared prefixes,
+// the fused append, 32-token blocks) spill; the one-row kernel also measured
+// faster at two (fewer, longer shares per CU: 171 against 178.5 us on the
+// B=256 lognormal step). e4m3 and head_dim 64: three, where the registers
+// fit and the e4m3 kernel measured the same at two. fp32 lane-per-token
 // segments: two, or one from 5 query heads per KV head on, whose per-head
 // accumulators do not fit 256.
 template <typename T, int D, int G, bool MQ = false, bool SH = false, int BS = kBlockSize, bool AP = false>
 constexpr int decode_waves_per_simd() {
   if constexpr (sizeof(T) == 4) return (D == 128 && G >= 5) ? 1 : 2;
-  if constexpr (sizeof(T) == 2 && D == 128 && (MQ || SH || AP || BS != kBlockSize)) return 2;
+  if constexpr (sizeof(T) == 2 && D == 128) return 2;
   return 3;
 }
 
