@@ -256,9 +256,11 @@ pkv_status paged_attention_decode_append(const pkv_pool* pool, int layer, void* 
  *     paged_attention_decode; the workspace size comes from
  *     paged_attention_decode_multi_workspace_bytes. context_lens[b] == 0 gives
  *     zero rows; 0 < context_lens[b] < queries_per_seq is a caller error.
- * bf16 and e4m3 pools; queries_per_seq x (num_q_heads / num_kv_heads) <= 16
- * (the rows of one KV head share one matrix-core tile), else
- * PKV_ERR_UNSUPPORTED. queries_per_seq == 1 is paged_attention_decode. */
+ * bf16 and e4m3 pools. While queries_per_seq x (num_q_heads / num_kv_heads)
+ * <= 16 the rows of one KV head share one matrix-core tile of the decode
+ * kernels. Beyond that each sequence's rows run as an equal-length chunk on
+ * the prefill-chunk kernel (no KV-axis split): the workspace size is then 0
+ * and workspace may be NULL. queries_per_seq == 1 is paged_attention_decode. */
 pkv_status paged_attention_decode_multi_workspace_bytes(const pkv_pool* pool, int num_seqs,
                                                         int queries_per_seq, int num_q_heads,
                                                         int max_blocks_per_seq, int partition_size,
