@@ -498,9 +498,12 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
   prm.num_waves = num_waves;
   // One query row per sequence: the wavefront that completes a split row
   // combines it in the launch, unless the rows are few and long (each spread
-  // over about eight or more wavefronts), where the reduction kernel's
-  // workgroup-shared combine is faster.
-  if (need > 0 && sp.balanced && q_per_seq == 1 && (long)num_seqs * pool->num_kv_heads * 8 > num_waves)
+  // over more than eight wavefronts), where the reduction kernel's
+  // workgroup-shared combine is faster. (Measured on Qwen-shaped steps: rows
+  // over 8 wavefronts are combined faster in the launch, 18-19 us against
+  // 20-21 us per step with the extra kernel; rows over 32 slower, 28-32 us
+  // against 21-25 us.)
+  if (need > 0 && sp.balanced && q_per_seq == 1 && (long)num_seqs * pool->num_kv_heads * 8 >= num_waves)
     prm.counters = reinterpret_cast<int32_t*>(ws);
   prm.scale_log2 = scale * 1.4426950408889634f * pool->k_scale[layer];
   prm.v_scale = pool->v_scale[layer];
