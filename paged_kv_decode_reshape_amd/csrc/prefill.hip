@@ -46,6 +46,15 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 constexpr int kQRows = 16;          // query rows per wavefront (the MFMA M / N)
 constexpr int kKeyTile = 64;        // keys per tile = 4 blocks
 constexpr int kMaxGroup = 8;
+// bf16 pools: two phases per step, each ending in a barrier. The score MFMAs
+// and softmax read the K tiles, then each wave stages the step's V tiles; P.V
+// reads the V tiles, then each wave stages the next step's K tiles. The
+// stores of one wave overlap the matrix work of others, with no phase of
+// stores alone (54-55 us against 57-58 us on a 512-row chunk over 2560 keys).
+// e4m3 pools widen codes as they stage them and keep one staging phase per
+// step (54 us against 58 us split).
+template <typename TP>
+constexpr bool prefill_split_phases() { return sizeof(TP) == 2; }
 // s_waitcnt immediate for vmcnt(0) alone on gfx9-family parts (expcnt and
 // lgkmcnt fields at their maximum, i.e. not waited for).
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -102,6 +111,7 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   constexpr int NG = prefill_groups(G);   // groups
   constexpr int NT = NG * 64 * NWG;       // threads per workgroup
   constexpr int KSTEPS = D / 32;          // MFMA k-steps over the head dim for S
+  constexpr bool kSplit = prefill_split_phases<TP>();
   constexpr int NTILES = D / 16;          // 16-row output tiles over the head dim
   constexpr int VPR = D / 8;              // 16-byte vectors per token row
   constexpr int kVecs = kKeyTile * VPR;   // 16-byte vectors per key tile of K (and of V)
@@ -287,6 +297,32 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   };
   // Clearing happens here, when the loaded values are needed anyway, so the
   // loads of the next step are not waited for early.
+  auto store_k = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q0 = wave_vec0 + u * NT;
+      if (!kAllSlots && q0 >= NG * kVecs) continue;
+      const int t = q0 / kVecs, qq0 = q0 % kVecs;
+      *reinterpret_cast<uint4*>(lds_k + (uint32_t)(t * (kKeyTile * D) + qq0 * 8) * 2u + lane_k) = to_bf16(kreg[u]);
+    }
+    (void)j;
+  };
+  auto store_v = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q0 = wave_vec0 + u * NT;
+      if (!kAllSlots && q0 >= NG * kVecs) continue;
+      const int t = q0 / kVecs, qq0 = q0 % kVecs;
+      const int key0 = j * NG * kKeyTile + (q0 / kBlockVecs) * BS;   // first key of the block
+      const int tok0 = (qq0 / VPR) % BS;
+      if (key0 + tok0 + lane_tok >= kv_end) {
+#pragma unroll
+        for (int i = 0; i < SW; ++i) vreg[u].w[i] = 0u;
+      }
+      *reinterpret_cast<uint4*>(lds_v + (uint32_t)((t * kKeyTile + qq0 / VPR) * PrefillLds<D, NWG, NG, BS>::kVStride) * 2u +
+                                lane_vl) = to_bf16(vreg[u]);
+    }
+  };
   auto store_step = [&](int j) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -316,18 +352,27 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
   // needed anyway: the loop then enters with no vector load outstanding, and
   // the compiler does not hold the tile's MFMAs for the prefetched step.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if constexpr (kSplit) {
+    if (nsteps > 0) store_k(0);
+    __syncthreads();
+  }
   const int vkey = 4 * quad + (col >> 2);   // transposed V read: key offset and column of this lane
   const int vcol = 4 * (col & 3);
   for (int j = 0; j < nsteps; ++j) {
-    __syncthreads();   // the previous step's tiles are no longer read
-    store_step(j);
-    __syncthreads();   // this step's tiles are in LDS
-    if (j + 1 < nsteps) {                   // in flight during the MFMAs below
-      load_step(j + 1, ids_next);
-      if (j + 2 < nsteps) step_ids(j + 2, ids_next);
+    if constexpr (!kSplit) {
+      __syncthreads();   // the previous step's tiles are no longer read
+      store_step(j);
+      __syncthreads();   // this step's tiles are in LDS
+      if (j + 1 < nsteps) {                   // in flight during the MFMAs below
+        load_step(j + 1, ids_next);
+        if (j + 2 < nsteps) step_ids(j + 2, ids_next);
+      }
     }
     const int key0 = (NG * j + grp) * kKeyTile;
-    if (key0 >= kv_end || key0 > wave_last_key) continue;   // past the range or the causal diagonal
+    // Tiles past the range or past the causal diagonal are skipped.
+    const bool active = key0 < kv_end && key0 <= wave_last_key;
+    bf16x8 phi[2], plo[2];
+    if (active) {
 
     // ---- S^T = K Q^T, one 16-key block per MFMA tile: lane holds S^T[16r + 4*quad + i][row col] ----
     f32x4 st[4];
@@ -381,7 +426,6 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
     // ---- P^T fragments in registers: P split into bf16 high + remainder ----
     // B operand of O^T += V^T P^T for key half kk: k-index j of lane (quad, col)
     // is key 32kk + 16*(j/4) + 4*quad + j%4 -- the lane's own probabilities.
-    bf16x8 phi[2], plo[2];
     float ls = 0.f;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -399,7 +443,18 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
       plo[kk] = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
     }
     l_row += ls;
-
+    }
+    if constexpr (kSplit) {
+      // Every wave is past its reads of the K tiles: stage this step's V
+      // tiles, put the next step's loads in flight, and publish.
+      store_v(j);
+      if (j + 1 < nsteps) {
+        load_step(j + 1, ids_next);
+        if (j + 2 < nsteps) step_ids(j + 2, ids_next);
+      }
+      __syncthreads();
+    }
+    if (active) {
     // ---- O^T += V^T P^T ----
     // A = V^T[d][the same 8 keys] comes from the natural V tile through the
     // transposing LDS read: within each 16-lane group, lane L addresses 4
@@ -419,6 +474,13 @@ __global__ __launch_bounds__(64 * G * prefill_row_subtiles(G) * prefill_groups(G
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi[kk], o[n], 0, 0, 0);
         o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo[kk], o[n], 0, 0, 0);
       }
+    }
+    }
+    if constexpr (kSplit) {
+      // Every wave is past its reads of the V tiles: stage the next step's
+      // K tiles and publish.
+      if (j + 1 < nsteps) store_k(j + 1);
+      __syncthreads();
     }
   }
 
