@@ -255,6 +255,8 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture each step in a HIP graph (torch.cuda.CUDAGraph) and time the replays")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="skip the gather-ceiling pass (paged_kv_gather_checksum over the same tiles)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before warmup, copy this many MiB device-to-device once (a plain copy "
                          "of known size, to scale hardware byte counters)")
@@ -462,6 +464,27 @@ def main():
         evs[i][1].record(stream_now)
     torch.cuda.synchronize()
     step_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    # Gather ceiling: the decode's K/V words read through the same tables, the
+    # same pool rotation and the same split, with no attention arithmetic
+    # (paged_kv_gather_checksum); its kernel's event times, in a pass of its own.
+    gather_us = None
+    if not args.no_gather and tq == 1 and not shared and nseq <= 8192:
+        chk = torch.empty((nseq, s.num_kv_heads), dtype=torch.int32, device=dev)
+        gws = torch.empty(((nseq + 1) * 4 + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+
+        def gather(i):
+            pkv.paged_kv_gather_checksum(pool, i % reps, chk, bt_d, cl_d, nseq, bt.shape[1], gws, gws.numel(),
+                                         torch.cuda.current_stream(dev))
+
+        for i in range(args.warmup):
+            gather(i)
+        torch.cuda.synchronize()
+        pkv.pkv_timing_enable(args.steps + 8, [pkv.KERNEL_GATHER])
+        for i in range(args.steps):
+            gather(args.warmup + i)
+        torch.cuda.synchronize()
+        gather_us = [x * 1e3 for x in pkv.pkv_timing_read_launches(pkv.KERNEL_GATHER, args.steps + 8)]
+        pkv.pkv_timing_disable()
     ms_per_step = wall * 1e3 / args.steps
     avg_us = {k: (ms / n * 1e3 if n else 0.0) for k, (n, ms) in kt.items()}
     avg_us = {k: avg_us[k] for k, _ in kinds_all}
@@ -549,6 +572,16 @@ def main():
                                "frac": round(achieved_read / HBM_PEAK_GBS, 4), "us": round(read_us, 2)},
         },
     }
+    if gather_us:
+        g_mean = sum(gather_us) / len(gather_us)
+        g_gbs = ab["decode_kv"] / (g_mean * 1e-6) / 1e9
+        result["gather_ceiling"] = {
+            "kernel": "gather_kernel (paged_kv_gather_checksum: the decode's K/V words, no arithmetic)",
+            "us": percentiles(gather_us),
+            "achieved": round(g_gbs, 1), "unit": "GB/s", "frac_of_peak": round(g_gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": ab["decode_kv"],
+            "decode_over_gather": round(decode_us / g_mean, 4) if decode_us else None,
+        }
     if has_prefill and avg_us["prefill"]:
         tf = ab["prefill_flops"] / (avg_us["prefill"] * 1e-6) / 1e12
         result["prefill_mfma"] = {"tflops": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,

@@ -336,6 +336,33 @@ pkv_status paged_attention_prefill_chunk(const pkv_pool* pool, int layer, void* 
                                          int total_q_tokens, int max_q_len, int num_q_heads,
                                          int max_blocks_per_seq, float scale, void* stream);
 
+/* ---- gather ceiling (measurement support, not part of the attention path) ----
+ * Decode at serving batch sizes is bound by streaming the KV cache through the
+ * block table ("The Serving Playbook", "The block table lives in the hottest
+ * kernel in the system"; "Inference Engineering, Part 2", "The KV cache").
+ * This call reads exactly the K/V words paged_attention_decode reads for the
+ * same arguments -- tokens 0 .. context_lens[b]-1 of every (sequence, KV head)
+ * row, through block_tables, with the decode kernels' 16-byte streaming loads
+ * and the balanced split's work order -- and does no attention arithmetic: it
+ * folds them into
+ *   checksum[b][h] = XOR of every 32-bit word of K_b[t][h] and V_b[t][h],
+ *                    t < context_lens[b]  (0 for an empty sequence),
+ * the words taken as the pool stores them. Its kernel time (timing kind
+ * PKV_KERNEL_GATHER) is the rate a gather of these tiles sustains on the
+ * device, against which the decode kernel's time can be set.
+ *   checksum: uint32 [num_seqs][num_kv_heads], device memory, overwritten.
+ *   block_tables, context_lens, max_blocks_per_seq: as for
+ *     paged_attention_decode.
+ *   workspace: at least (num_seqs + 1) * 4 bytes of device memory (contents
+ *     on entry ignored).
+ *   1 <= num_seqs <= 8192 (0 is a no-op); any pool dtype and geometry.
+ * Two kernels are enqueued on `stream` (a one-workgroup plan kernel, then the
+ * gather). */
+pkv_status paged_kv_gather_checksum(const pkv_pool* pool, int layer, uint32_t* checksum,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int num_seqs, int max_blocks_per_seq, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
 /* ---- kernel timing (measurement support, not part of the attention path) ----
  * While enabled, every kernel of the kinds selected by kind_mask (bit k for
  * pkv_kernel_kind k; 0 selects all) that the library enqueues is bracketed by
@@ -352,7 +379,8 @@ typedef enum {
     PKV_KERNEL_DECODE_REDUCE = 2,
     PKV_KERNEL_PREFILL = 3,
     PKV_KERNEL_DECODE_PREFIX = 4,   /* shared-prefix partitions of paged_attention_decode_shared */
-    PKV_KERNEL_KINDS = 5
+    PKV_KERNEL_GATHER = 5,          /* the gather kernel of paged_kv_gather_checksum */
+    PKV_KERNEL_KINDS = 6
 } pkv_kernel_kind;
 
 pkv_status pkv_timing_enable(int max_launches, unsigned int kind_mask);

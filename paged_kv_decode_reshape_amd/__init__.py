@@ -18,14 +18,14 @@ import os
 
 __all__ = [
     "PkvError", "F32", "BF16", "FP8_E4M3", "KERNEL_APPEND", "KERNEL_DECODE_PARTITION",
-    "KERNEL_DECODE_REDUCE", "KERNEL_PREFILL", "KERNEL_DECODE_PREFIX", "library_path", "load",
+    "KERNEL_DECODE_REDUCE", "KERNEL_PREFILL", "KERNEL_DECODE_PREFIX", "KERNEL_GATHER", "library_path", "load",
     "kv_pool_bytes", "kv_pool_create", "kv_pool_set_fp8_scales", "kv_pool_destroy",
     "reshape_and_cache", "copy_blocks",
     "paged_attention_decode_workspace_bytes", "paged_attention_decode", "paged_attention_decode_noalloc",
     "paged_attention_decode_append",
     "paged_attention_decode_multi_workspace_bytes", "paged_attention_decode_multi",
     "paged_attention_decode_shared_workspace_bytes", "paged_attention_decode_shared",
-    "paged_attention_prefill_chunk", "pkv_timing_enable", "pkv_timing_disable",
+    "paged_attention_prefill_chunk", "paged_kv_gather_checksum", "pkv_timing_enable", "pkv_timing_disable",
     "pkv_timing_read", "pkv_timing_read_launches", "pkv_last_error", "pkv_debug_read_errors",
     "DEBUG_SLOT", "DEBUG_BLOCK", "DEBUG_CONTEXT", "DEBUG_CHUNK", "library_variant", "EXPORTED_SYMBOLS",
 ]
@@ -33,6 +33,7 @@ __all__ = [
 F32, BF16, FP8_E4M3 = 0, 1, 2
 KERNEL_APPEND, KERNEL_DECODE_PARTITION, KERNEL_DECODE_REDUCE, KERNEL_PREFILL = 0, 1, 2, 3
 KERNEL_DECODE_PREFIX = 4
+KERNEL_GATHER = 5
 DEBUG_SLOT, DEBUG_BLOCK, DEBUG_CONTEXT, DEBUG_CHUNK = 1, 2, 4, 8
 
 _STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID_ARG", -2: "PKV_ERR_UNSUPPORTED",
@@ -82,6 +83,8 @@ _SIGNATURES = {
     "paged_attention_prefill_chunk": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p,
                                               c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                               c_int, c_float, c_void_p]),
+    "paged_kv_gather_checksum": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int,
+                                         c_void_p, c_size_t, c_void_p]),
     "pkv_timing_enable": (c_int, [c_int, ctypes.c_uint]),
     "pkv_timing_disable": (c_int, []),
     "pkv_timing_read": (c_int, [c_int, _P(c_int), _P(ctypes.c_double)]),
@@ -293,6 +296,13 @@ def paged_attention_prefill_chunk(pool, layer, out, query, cu_q_lens, block_tabl
                                                 _ptr(context_lens), num_seqs, total_q_tokens,
                                                 max_q_len, num_q_heads, max_blocks_per_seq,
                                                 float(scale), _stream(stream)))
+
+
+def paged_kv_gather_checksum(pool, layer, checksum, block_tables, context_lens, num_seqs,
+                             max_blocks_per_seq, workspace, workspace_bytes, stream=None):
+    _check(load().paged_kv_gather_checksum(pool, layer, _ptr(checksum), _ptr(block_tables),
+                                           _ptr(context_lens), num_seqs, max_blocks_per_seq,
+                                           _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def pkv_timing_enable(max_launches, kinds=None):

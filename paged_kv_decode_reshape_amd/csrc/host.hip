@@ -718,6 +718,49 @@ pkv_status copy_blocks(const pkv_pool* pool, const int32_t* block_pairs, int num
   return PKV_OK;
 }
 
+pkv_status paged_kv_gather_checksum(const pkv_pool* pool, int layer, uint32_t* checksum,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    int num_seqs, int max_blocks_per_seq, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  pkv_status st = check_pool_layer(pool, layer);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (num_seqs > pkv::kGatherMaxSeqs)
+    return fail(PKV_ERR_UNSUPPORTED, "%d sequences: at most %d per call", num_seqs, pkv::kGatherMaxSeqs);
+  if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (num_seqs == 0) return PKV_OK;
+  if (!checksum || !block_tables || !context_lens || !workspace)
+    return fail(PKV_ERR_INVALID_ARG, "checksum, block_tables, context_lens and workspace must not be NULL");
+  if (!aligned(checksum, 4) || !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(workspace, 4))
+    return fail(PKV_ERR_INVALID_ARG, "checksum, block_tables, context_lens and workspace must be 4-byte aligned");
+  const size_t need = ((size_t)num_seqs + 1) * sizeof(int32_t);
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
+  // Window counts are summed in int32 on the device.
+  const long windows_per_row = ((long)max_blocks_per_seq * pool->block_size + 63) / 64;
+  if ((long)num_seqs * pool->num_kv_heads * windows_per_row >= INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "too many 64-token windows in one call");
+  pkv::GatherParams prm{};
+  prm.checksum = checksum;
+  prm.starts = static_cast<int32_t*>(workspace);
+  prm.kpool = pool->k_layers[layer];
+  prm.vpool = pool->v_layers[layer];
+  prm.block_tables = block_tables;
+  prm.context_lens = context_lens;
+  prm.num_seqs = num_seqs;
+  prm.num_kv_heads = pool->num_kv_heads;
+  prm.max_blocks = max_blocks_per_seq;
+  prm.block_size = pool->block_size;
+  prm.num_blocks = pool->num_blocks;
+  prm.num_cus = device_cu_count();
+  prm.err = debug_error_word();
+  const int row_bytes = pool->head_dim * (int)elem_bytes(pool->dtype);
+  (void)hipGetLastError();
+  hipError_t err = pkv::launch_gather(prm, row_bytes, (hipStream_t)stream, pkv::KernelTimer{});
+  if (err != hipSuccess) return hip_fail(err, "paged_kv_gather_checksum launch");
+  return PKV_OK;
+}
+
 pkv_status paged_attention_decode_workspace_bytes(const pkv_pool* pool, int num_seqs,
                                                   int num_q_heads, int max_blocks_per_seq,
                                                   int partition_size, size_t* bytes) {

@@ -11,7 +11,14 @@ namespace pkv {
 constexpr int kPoolBlockSize = 16;
 constexpr int kPoolBlockSizeLarge = 32;
 
-enum class KernelKind : int { kAppend = 0, kDecodePartition = 1, kDecodeReduce = 2, kPrefill = 3, kDecodePrefix = 4 };
+enum class KernelKind : int {
+  kAppend = 0,
+  kDecodePartition = 1,
+  kDecodeReduce = 2,
+  kPrefill = 3,
+  kDecodePrefix = 4,
+  kGather = 5
+};
 
 // Records a pair of HIP events around a launch when kernel timing is enabled
 // (a no-op otherwise). Defined in host.hip.
@@ -143,5 +150,26 @@ int decode_balanced_waves_per_cu(PoolType type, int head_dim, const BalancedVari
 int decode_balanced_max_seqs();
 size_t decode_balanced_desc_bytes();
 hipError_t launch_prefill(const PrefillParams& prm, PoolType type, hipStream_t stream, const KernelTimer& timer);
+
+// The decode gather alone (a per-row XOR checksum of the K/V words a decode
+// call reads), for measuring the memory ceiling.
+struct GatherParams {
+  uint32_t* checksum;      // [num_seqs][num_kv_heads]
+  int32_t* starts;         // workspace int32 [num_seqs + 1]: windows before each sequence
+  const void* kpool;
+  const void* vpool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs;            // 1 .. kGatherMaxSeqs
+  int num_kv_heads;
+  int max_blocks;
+  int block_size;          // 16 or 32
+  int num_blocks;          // blocks in the pool (device-value checks)
+  int num_cus;
+  uint32_t* err;           // device error word of the checks (PKV_DEBUG builds), else NULL
+};
+constexpr int kGatherMaxSeqs = 8192;
+// row_bytes: head_dim * element bytes (64, 128, 256 or 512).
+hipError_t launch_gather(const GatherParams& prm, int row_bytes, hipStream_t stream, const KernelTimer& timer);
 
 }  // namespace pkv

@@ -220,7 +220,7 @@ def test_enum_arguments_outside_their_range_are_rejected():
     # values outside pkv_dtype / pkv_kernel_kind are read as integers and rejected
     assert _status(pkv.kv_pool_create, 1, 4, 16, 1, 64, 5, [256], [512])[0] == -1
     assert _status(pkv.kv_pool_create, 1, 4, 16, 1, 64, -3, [256], [512])[0] == -1
-    for kind in (-1, 5, 1 << 20):
+    for kind in (-1, 6, 1 << 20):
         assert _status(pkv.pkv_timing_read, kind)[0] == -1
         assert _status(pkv.pkv_timing_read_launches, kind, 4)[0] == -1
 
@@ -230,3 +230,20 @@ def test_debug_read_errors_in_the_release_library():
         pytest.skip("a substitute library is loaded")
     st, msg = _status(pkv.pkv_debug_read_errors)
     assert st == -2 and "PKV_DEBUG" in msg
+
+
+def test_gather_checksum_validates_on_the_host():
+    h = pkv.kv_pool_create(1, 4, 16, 1, 64, pkv.F32, [256], [768])
+    try:
+        # checksum, block_tables, context_lens, workspace: fake device addresses
+        args = (16, 32, 48)
+        assert _status(pkv.paged_kv_gather_checksum, h, 1, *args, 1, 1, 64, 64)[0] == -1      # layer
+        assert _status(pkv.paged_kv_gather_checksum, h, 0, *args, -1, 1, 64, 64)[0] == -1     # num_seqs
+        assert _status(pkv.paged_kv_gather_checksum, h, 0, *args, 8193, 1, 64, 1 << 20)[0] == -2
+        assert _status(pkv.paged_kv_gather_checksum, h, 0, *args, 1, 0, 64, 64)[0] == -1      # max blocks
+        assert _status(pkv.paged_kv_gather_checksum, h, 0, *args, 4, 1, 64, 16)[0] == -4      # workspace
+        assert _status(pkv.paged_kv_gather_checksum, h, 0, *args, 4, 1, None, 64)[0] == -1
+        assert _status(pkv.paged_kv_gather_checksum, h, 0, 18, 32, 48, 4, 1, 64, 64)[0] == -1  # misaligned
+        pkv.paged_kv_gather_checksum(h, 0, *args, 0, 1, 64, 64)   # no sequences: a no-op
+    finally:
+        pkv.kv_pool_destroy(h)
