@@ -365,10 +365,12 @@ pkv_status paged_kv_gather_checksum(const pkv_pool* pool, int layer, uint32_t* c
 
 /* ---- kernel timing (measurement support, not part of the attention path) ----
  * While enabled, every kernel of the kinds selected by kind_mask (bit k for
- * pkv_kernel_kind k; 0 selects all) that the library enqueues is bracketed by
- * a pair of HIP events on the same stream (events are created by
- * pkv_timing_enable, never inside the calls). Each pair adds a small gap to
- * the stream, so measure only the kinds needed. pkv_timing_read waits for the
+ * pkv_kernel_kind k; 0 selects all) that the library enqueues is launched
+ * with a pair of HIP events that the launch itself stamps at the kernel's
+ * start and end (hipExtLaunchKernelGGL; the events are created by
+ * pkv_timing_enable, never inside the calls), so a pair times the kernel
+ * alone. Timed launches cost a little host time, so measure only the kinds
+ * needed. pkv_timing_read waits for the
  * recorded events and returns, for one kernel kind, the number of launches
  * recorded and their summed duration in milliseconds. Recording stops
  * silently once max_launches launches have been recorded. Not for use under

@@ -90,9 +90,9 @@ hipError_t launch_append_fp8(const AppendParams& prm, hipStream_t stream, const 
   const unsigned grid = (unsigned)((threads + 255) / 256);
   timer.begin(KernelKind::kAppend, stream);
   if (prm.block_size == 32) {
-    hipLaunchKernelGGL((append_fp8_kernel<D, 32>), dim3(grid), dim3(256), 0, stream, prm);
+    PKV_LAUNCH((append_fp8_kernel<D, 32>), dim3(grid), dim3(256), 0, stream, prm);
   } else {
-    hipLaunchKernelGGL((append_fp8_kernel<D, kBlockSize>), dim3(grid), dim3(256), 0, stream, prm);
+    PKV_LAUNCH((append_fp8_kernel<D, kBlockSize>), dim3(grid), dim3(256), 0, stream, prm);
   }
   timer.end(KernelKind::kAppend, stream);
   return hipGetLastError();
@@ -105,9 +105,9 @@ hipError_t launch_append_t(const AppendParams& prm, hipStream_t stream, const Ke
   const unsigned grid = (unsigned)((threads + 255) / 256);
   timer.begin(KernelKind::kAppend, stream);
   if (prm.block_size == 32) {
-    hipLaunchKernelGGL((append_kernel<T, D, 32>), dim3(grid), dim3(256), 0, stream, prm);
+    PKV_LAUNCH((append_kernel<T, D, 32>), dim3(grid), dim3(256), 0, stream, prm);
   } else {
-    hipLaunchKernelGGL((append_kernel<T, D, kBlockSize>), dim3(grid), dim3(256), 0, stream, prm);
+    PKV_LAUNCH((append_kernel<T, D, kBlockSize>), dim3(grid), dim3(256), 0, stream, prm);
   }
   timer.end(KernelKind::kAppend, stream);
   return hipGetLastError();

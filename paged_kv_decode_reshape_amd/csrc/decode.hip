@@ -1701,7 +1701,7 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
       const long punits = (long)prm.num_kv_heads * prm.member_tiles * prm.num_groups * prm.max_parts;
       const long pblocks = std::max((punits + 3) / 4, ((long)prm.num_seqs + 255) / 256);
       timer.begin(KernelKind::kDecodePrefix, stream);
-      hipLaunchKernelGGL((decode_prefix_kernel<T, D, G, BS>), dim3((unsigned)pblocks), dim3(256), 0, stream,
+      PKV_LAUNCH((decode_prefix_kernel<T, D, G, BS>), dim3((unsigned)pblocks), dim3(256), 0, stream,
                          prm.context_lens, args, prm);
       timer.end(KernelKind::kDecodePrefix, stream);
       if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -1713,17 +1713,17 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
     const dim3 grid((unsigned)((prm.num_waves + 3) / 4));
     if constexpr (kShareable) {
       if (prm.shared_start != nullptr) {
-        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, true, BS, false>), grid, dim3(256), 0, stream, out,
+        PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, true, BS, false>), grid, dim3(256), 0, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       } else if (prm.new_key != nullptr) {
-        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS, true>), grid, dim3(256), 0, stream, out,
+        PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, false, BS, true>), grid, dim3(256), 0, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       } else {
-        hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), 0, stream, out,
+        PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), 0, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       }
     } else {
-      hipLaunchKernelGGL((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), 0, stream, out,
+      PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), 0, stream, out,
                          prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
     }
     timer.end(KernelKind::kDecodePartition, stream);
@@ -1733,10 +1733,10 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
     const dim3 rgrid((unsigned)((prm.num_waves + 3) / 4), (unsigned)prm.q_per_seq);
     if ((long)prm.num_seqs * prm.num_kv_heads * 8 <= prm.num_waves) {
       // Few rows for many waves: each row spans about eight or more waves.
-      hipLaunchKernelGGL((decode_balanced_reduce_coop_kernel<TQ, D, G>), rgrid, dim3(256), 0, stream, out,
+      PKV_LAUNCH((decode_balanced_reduce_coop_kernel<TQ, D, G>), rgrid, dim3(256), 0, stream, out,
                          prm.ws_ml, prm.ws_o, desc, prm);
     } else {
-      hipLaunchKernelGGL((decode_balanced_reduce_kernel<TQ, D, G>), rgrid, dim3(256), 0, stream, out, prm.ws_ml,
+      PKV_LAUNCH((decode_balanced_reduce_kernel<TQ, D, G>), rgrid, dim3(256), 0, stream, out, prm.ws_ml,
                          prm.ws_o, desc, prm);
     }
     timer.end(KernelKind::kDecodeReduce, stream);
@@ -1747,13 +1747,13 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
   bool fused = false;
   if constexpr (kShareable) {
     if (prm.new_key != nullptr) {
-      hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ, BS, true>), dim3((unsigned)((units + 3) / 4)),
+      PKV_LAUNCH((decode_partition_kernel<T, D, G, MQ, BS, true>), dim3((unsigned)((units + 3) / 4)),
                          dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
       fused = true;
     }
   }
   if (!fused) {
-    hipLaunchKernelGGL((decode_partition_kernel<T, D, G, MQ, BS, false>), dim3((unsigned)((units + 3) / 4)),
+    PKV_LAUNCH((decode_partition_kernel<T, D, G, MQ, BS, false>), dim3((unsigned)((units + 3) / 4)),
                        dim3(256), 0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, args, prm);
   }
   timer.end(KernelKind::kDecodePartition, stream);
@@ -1761,7 +1761,7 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
   if (prm.max_parts > 1) {
     const long pairs = (long)prm.num_seqs * prm.q_per_seq * prm.num_kv_heads * G;
     timer.begin(KernelKind::kDecodeReduce, stream);
-    hipLaunchKernelGGL((decode_reduce_kernel<TQ, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256),
+    PKV_LAUNCH((decode_reduce_kernel<TQ, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256),
                        0, stream, out, prm.ws_ml, prm.ws_o, prm.context_lens, prm);
     timer.end(KernelKind::kDecodeReduce, stream);
     err = hipGetLastError();

@@ -209,7 +209,7 @@ hipError_t launch_gather_nl(const GatherParams& prm, hipStream_t stream, const K
   }
   hipLaunchKernelGGL(gather_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, prm);
   timer.begin(KernelKind::kGather, stream);
-  hipLaunchKernelGGL(kern, dim3(blocks * prm.num_cus), dim3(256), lds, stream, prm);
+  PKV_LAUNCH(kern, dim3(blocks * prm.num_cus), dim3(256), lds, stream, prm);
   timer.end(KernelKind::kGather, stream);
   return hipGetLastError();
 }

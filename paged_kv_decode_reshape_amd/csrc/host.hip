@@ -239,7 +239,8 @@ struct TimingState {
   std::vector<int> kind;
 };
 TimingState g_timing;
-thread_local int g_timing_slot = -1;
+thread_local int g_timing_slot = -1;      // the slot begin() claimed on this thread, or -1
+thread_local bool g_timing_taken = false;  // a launch has taken that slot's events
 
 void destroy_events_locked() {
   for (auto e : g_timing.start) (void)hipEventDestroy(e);
@@ -256,23 +257,41 @@ void destroy_events_locked() {
 namespace pkv {
 
 void KernelTimer::begin(KernelKind kind, hipStream_t stream) const {
+  (void)stream;
   g_timing_slot = -1;
+  g_timing_taken = false;
   if (!g_timing.enabled || !(g_timing.kinds & (1u << (int)kind))) return;
   std::lock_guard<std::mutex> lock(g_timing.mu);
   if (!g_timing.enabled || g_timing.used >= g_timing.cap) return;
   const int slot = g_timing.used++;
   g_timing.kind[slot] = (int)kind;
-  (void)hipEventRecord(g_timing.start[slot], stream);
   g_timing_slot = slot;
+}
+
+bool take_timed_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (g_timing_slot < 0 || g_timing_taken) return false;
+  std::lock_guard<std::mutex> lock(g_timing.mu);
+  if (g_timing_slot >= (int)g_timing.stop.size()) return false;
+  *start = g_timing.start[g_timing_slot];
+  *stop = g_timing.stop[g_timing_slot];
+  g_timing_taken = true;
+  return true;
 }
 
 void KernelTimer::end(KernelKind kind, hipStream_t stream) const {
   (void)kind;
   if (g_timing_slot < 0) return;
-  std::lock_guard<std::mutex> lock(g_timing.mu);
-  if (g_timing_slot < (int)g_timing.stop.size())
-    (void)hipEventRecord(g_timing.stop[g_timing_slot], stream);
+  if (!g_timing_taken) {
+    // No launch took the pair: record both so that the slot reads as an
+    // (empty) interval rather than as events never recorded.
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    if (g_timing_slot < (int)g_timing.stop.size()) {
+      (void)hipEventRecord(g_timing.start[g_timing_slot], stream);
+      (void)hipEventRecord(g_timing.stop[g_timing_slot], stream);
+    }
+  }
   g_timing_slot = -1;
+  g_timing_taken = false;
 }
 
 }  // namespace pkv

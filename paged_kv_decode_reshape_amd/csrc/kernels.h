@@ -1,6 +1,7 @@
 // Launch interfaces between the C-ABI host layer and the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,12 +21,30 @@ enum class KernelKind : int {
   kGather = 5
 };
 
-// Records a pair of HIP events around a launch when kernel timing is enabled
-// (a no-op otherwise). Defined in host.hip.
+// Times a launch when kernel timing is enabled for its kind (a no-op
+// otherwise). begin() claims an event pair; the launch between begin() and
+// end() is made with PKV_LAUNCH, which has the runtime stamp the pair at the
+// kernel's own start and end (hipExtLaunchKernelGGL), so the pair times the
+// kernel rather than the kernel plus separate event packets around it. If no
+// PKV_LAUNCH took the pair, end() records both events itself. Defined in
+// host.hip.
 struct KernelTimer {
   void begin(KernelKind kind, hipStream_t stream) const;
   void end(KernelKind kind, hipStream_t stream) const;
 };
+
+// The event pair a begin() on this thread opened and no launch has taken yet
+// (and marks it taken); false when there is none.
+bool take_timed_events(hipEvent_t* start, hipEvent_t* stop);
+
+#define PKV_LAUNCH(kernel, grid, block, lds, stream, ...)                                          \
+  do {                                                                                           \
+    hipEvent_t pkv_e0_ = nullptr, pkv_e1_ = nullptr;                                             \
+    if (::pkv::take_timed_events(&pkv_e0_, &pkv_e1_))                                            \
+      hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, pkv_e0_, pkv_e1_, 0, __VA_ARGS__); \
+    else                                                                                         \
+      hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                         \
+  } while (0)
 
 // Element type of a pool (the values match pkv_dtype).
 enum class PoolType : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };

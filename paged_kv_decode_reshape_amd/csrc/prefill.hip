@@ -540,12 +540,12 @@ hipError_t launch_prefill_dg(const PrefillParams& prm, hipStream_t stream) {
                   (unsigned)prm.num_seqs);
   const dim3 block(64 * G * RT * prefill_groups(G));
   if (prm.block_size == 32) {
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, TP, 32>), grid, block, 0, stream,
+    PKV_LAUNCH((prefill_chunk_kernel<D, G, TP, 32>), grid, block, 0, stream,
                        static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
                        static_cast<const TP*>(prm.kpool), static_cast<const TP*>(prm.vpool),
                        prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
   } else {
-    hipLaunchKernelGGL((prefill_chunk_kernel<D, G, TP, kBlockSize>), grid, block, 0, stream,
+    PKV_LAUNCH((prefill_chunk_kernel<D, G, TP, kBlockSize>), grid, block, 0, stream,
                        static_cast<uint16_t*>(prm.out), static_cast<const uint16_t*>(prm.query),
                        static_cast<const TP*>(prm.kpool), static_cast<const TP*>(prm.vpool),
                        prm.cu_q_lens, prm.block_tables, prm.context_lens, prm);
