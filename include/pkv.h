@@ -36,6 +36,9 @@
  *     value and out; bf16 for all four with a PKV_FP8_E4M3 pool. Integer
  *     tensors are int32 except slot_mapping (int64).
  *   - Every pointer must be 16-byte aligned; tensors are dense row-major.
+ *   - scale (the softmax scale of the attention calls, 1/sqrt(head_dim) in the
+ *     usual case) must be finite and positive, and so must its product with
+ *     log2(e) and an e4m3 layer's K scale; otherwise PKV_ERR_INVALID_ARG.
  *   - Errors: a non-zero pkv_status is returned and nothing is enqueued;
  *     pkv_last_error() gives a message (thread-local). Values *inside*
  *     device buffers (block ids, lengths, slots) cannot be checked without a

@@ -86,6 +86,18 @@ pkv_status check_pool_layer(const pkv_pool* pool, int layer) {
   return PKV_OK;
 }
 
+// The softmax scale (after check_pool_layer): finite and positive, and so is
+// its product with log2(e) and the layer's K scale. The prefill-chunk kernel
+// takes each tile's maximum over the raw scores and scales it once, and folds
+// the scale into each weight's exponent: with a negative factor the maximum
+// would be the wrong end, and with zero a masked score would give NaN.
+pkv_status check_scale(const pkv_pool* pool, int layer, float scale) {
+  const float s2 = scale * 1.4426950408889634f * pool->k_scale[layer];
+  if (!std::isfinite(scale) || !(scale > 0.f) || !std::isfinite(s2) || !(s2 > 0.f))
+    return fail(PKV_ERR_INVALID_ARG, "scale must be finite and positive (got %g)", (double)scale);
+  return PKV_OK;
+}
+
 // Decode work split. Balanced (partition_size == 0, up to 4096 sequences):
 // the window sequence is shared equally by num_waves wavefronts, the
 // workspace holding two partial summaries per wavefront. Otherwise fixed
@@ -445,7 +457,7 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
   if (q_per_seq > 1 && pool->dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "several queries per sequence run on the matrix cores: bf16 and e4m3 pools only");
   if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
-  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  if (const pkv_status sc = check_scale(pool, layer, scale); sc != PKV_OK) return sc;
   if (num_seqs == 0) return PKV_OK;
   if (q_per_seq * group > kMfmaColumns) {
     // More query rows per KV head than one matrix-core tile holds: the
@@ -626,7 +638,7 @@ pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* 
   const int group = num_q_heads / pool->num_kv_heads;
   if (group > 8) return fail(PKV_ERR_UNSUPPORTED, "%d query heads per KV head unsupported (1..8)", group);
   if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
-  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  if (const pkv_status sc = check_scale(pool, layer, scale); sc != PKV_OK) return sc;
   if (num_seqs == 0) return PKV_OK;
   if (num_groups <= 0 || num_groups > num_seqs)
     return fail(PKV_ERR_INVALID_ARG, "num_groups must be in [1, num_seqs] (got %d)", num_groups);
@@ -883,7 +895,7 @@ pkv_status prefill_run(const pkv_pool* pool, int layer, void* out, const void* q
   const int group = num_q_heads / pool->num_kv_heads;
   if (group > 8) return fail(PKV_ERR_UNSUPPORTED, "%d query heads per KV head unsupported (1..8)", group);
   if (max_blocks_per_seq <= 0) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
-  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  if (const pkv_status sc = check_scale(pool, layer, scale); sc != PKV_OK) return sc;
   if (num_seqs == 0 || total_q_tokens == 0) return PKV_OK;
   if (max_q_len == 0) return fail(PKV_ERR_INVALID_ARG, "max_q_len must be positive when there are query rows");
   if (!out || !query || (!cu_q_lens && q_per_seq <= 0) || !block_tables || !context_lens)

@@ -68,6 +68,11 @@ def test_pool_create_validates_pointers():
         assert _status(pkv.paged_attention_decode, h, 0, 16, 16, 16, 16, 1, 4, 1, 1.0, 100)[0] == -1
         assert _status(pkv.paged_attention_decode, h, 0, 16, 16, 16, 16, 1, 4, 1,
                        float("nan"))[0] == -1
+        for bad_scale in (0.0, -0.125, float("inf"), 3e38):      # 3e38 * log2(e) overflows
+            st, msg = _status(pkv.paged_attention_decode, h, 0, 16, 16, 16, 16, 1, 4, 1, bad_scale)
+            assert st == -1 and "scale" in msg
+            assert _status(pkv.paged_attention_prefill_chunk, h, 0, 16, 16, 16, 16, 16, 1, 4, 4, 4, 1,
+                           bad_scale)[0] in (-1, -2)
         assert _status(pkv.reshape_and_cache, h, 0, 16, 16, 16, -1)[0] == -1
         assert _status(pkv.reshape_and_cache, h, 0, 8, 16, 16, 1)[0] == -1        # misaligned key
         # prefill runs on bf16 MFMA only
