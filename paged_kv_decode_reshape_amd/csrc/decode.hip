@@ -406,7 +406,7 @@ __device__ __forceinline__ Summary<G, DecodeShape<T, D, G>::kVEpv> run_segment(
 template <typename T, int D, int G>
 __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row,
                                            const Summary<G, DecodeShape<T, D, G>::kVEpv>& st, float v_scale,
-                                           int /*nq: 1*/, int /*hq*/) {
+                                           int /*nq: 1*/, int /*hq*/, void* /*stage*/ = nullptr) {
   using TQ = typename IoType<T>::type;
   constexpr int EPV = DecodeShape<T, D, G>::kVEpv;
   constexpr int EPQ = ElemTraits<TQ>::kPerVec;
@@ -434,7 +434,7 @@ template <typename T, int D, int G, bool kCoherent = false>
 __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base,
                                               size_t o_stride,
                                               const Summary<G, DecodeShape<T, D, G>::kVEpv>& st, float v_scale,
-                                              int /*nq: 1*/, int /*pj*/) {
+                                              int /*nq: 1*/, int /*pj*/, void* /*stage*/ = nullptr) {
   constexpr int EPV = DecodeShape<T, D, G>::kVEpv;
   constexpr int VPR = D / EPV;
   const int lane = threadIdx.x & 63;
@@ -500,6 +500,10 @@ struct MfmaWaveLds {
   static constexpr int kStride = D + 8;
   alignas(16) uint16_t v[32][kStride];
 };
+// The same area stages a wave's finished summaries on their way out: up to
+// 16 columns of D floats.
+static_assert(sizeof(MfmaWaveLds<64>) >= 16 * 64 * 4 && sizeof(MfmaWaveLds<128>) >= 16 * 128 * 4,
+              "a wave's LDS holds 16 columns of a summary");
 
 // Running summary of head col (every lane of the column holds the same m;
 // l is a per-lane partial until the end of the segment). o: lane (quad, col)
@@ -772,49 +776,80 @@ __device__ __forceinline__ MfmaSummary<D> run_segment_mfma(const DecodeArgs& a, 
   return st;
 }
 
-// Final rows from a matrix-core summary: lane (quad, col < nq * G) writes
-// query row col / G, head col % G of the group, d = 16n + 4*quad .. +4.
-// out_row points at row 0, head 0 of the group; rows are hq heads apart.
+// Final rows from a matrix-core summary: column col < nq * G is query row
+// col / G, head col % G of the group, and lane (quad, col) holds its
+// d = 16n + 4*quad .. +4. out_row points at row 0, head 0 of the group; rows
+// are hq heads apart. The rows go through stage (the wave's own LDS, at least
+// nq * G * D * 2 bytes, free to overwrite) and leave as 16-byte lanes over
+// whole rows: one wave instruction writes 1 KiB of consecutive heads. Stored
+// straight from the matrix layout, every instruction would write 32-byte
+// pieces of 16 rows; such scattered writes among the streaming reads cost the
+// B = 256 decode about 4 us.
 template <typename T, int D, int G>
 __device__ __forceinline__ void write_rows(typename IoType<T>::type* out_row, const MfmaSummary<D>& st,
-                                           float v_scale, int nq, int hq) {
+                                           float v_scale, int nq, int hq, void* stage) {
   const int lane = threadIdx.x & 63;
   const int quad = lane >> 4, col = lane & 15;
-  if (col < nq * G) {
-    const float inv = v_scale / st.l;
-    uint16_t* row = reinterpret_cast<uint16_t*>(out_row) + ((size_t)(col / G) * hq + col % G) * D;
+  const int ncol = nq * G;
+  const float inv = v_scale / st.l;
+  uint16_t* h = static_cast<uint16_t*>(stage);            // [ncol][D] bf16
+  wave_lds_sync();
+  if (col < ncol) {
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
       const mf_f32x4 o = st.o[n];
-      *reinterpret_cast<uint2*>(row + 16 * n + 4 * quad) =
+      *reinterpret_cast<uint2*>(h + col * D + 16 * n + 4 * quad) =
           make_uint2(f32_to_bf16_bits(o[0] * inv) | (f32_to_bf16_bits(o[1] * inv) << 16),
                      f32_to_bf16_bits(o[2] * inv) | (f32_to_bf16_bits(o[3] * inv) << 16));
     }
   }
+  wave_lds_sync();
+  for (int c = lane; c < ncol * (D / 8); c += kWave) {
+    const int r = c / (D / 8), v = c % (D / 8);
+    const uint4 x = *reinterpret_cast<const uint4*>(h + r * D + 8 * v);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(out_row) + ((size_t)(r / G) * hq + r % G) * D + 8 * v) = x;
+  }
+  wave_lds_sync();
 }
 
 // Partial summary of column col = (row j, head g) at index j * pj + g.
 // kCoherent: device-scope stores, for a summary another wavefront of the
 // launch combines.
+// The partial goes through stage (the wave's own LDS, at least nq * G * D * 4
+// bytes, free to overwrite) and leaves as 16-byte lanes over whole columns
+// (1 KiB per wave instruction). Written straight from the matrix layout, a
+// device-scope partial would reach memory as 8-byte pieces, eight to a line,
+// which cost the B = 256 decode about 9 us.
 template <typename T, int D, int G, bool kCoherent = false>
 __device__ __forceinline__ void write_partial(float2* ml, size_t ml_stride, float* o_base, size_t o_stride,
-                                              const MfmaSummary<D>& st, float v_scale, int nq, int pj) {
+                                              const MfmaSummary<D>& st, float v_scale, int nq, int pj,
+                                              void* stage) {
   const int lane = threadIdx.x & 63;
   const int quad = lane >> 4, col = lane & 15;
-  if (col < nq * G) {
-    const size_t idx = (size_t)(col / G) * pj + col % G;
-    float* wo = o_base + idx * o_stride;
+  const int ncol = nq * G;
+  {
+    float* f = static_cast<float*>(stage);                // [ncol][D]
+    wave_lds_sync();
+    if (col < ncol) {
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
-      const mf_f32x4 o = st.o[n];
-      float* p = wo + 16 * n + 4 * quad;
-      if constexpr (kCoherent) {
-        coherent_store2(p, o[0] * v_scale, o[1] * v_scale);
-        coherent_store2(p + 2, o[2] * v_scale, o[3] * v_scale);
-      } else {
-        *reinterpret_cast<float4*>(p) = make_float4(o[0] * v_scale, o[1] * v_scale, o[2] * v_scale, o[3] * v_scale);
+      for (int n = 0; n < D / 16; ++n) {
+        const mf_f32x4 o = st.o[n];
+        *reinterpret_cast<float4*>(f + col * D + 16 * n + 4 * quad) =
+            make_float4(o[0] * v_scale, o[1] * v_scale, o[2] * v_scale, o[3] * v_scale);
       }
     }
+    wave_lds_sync();
+    for (int c = lane; c < ncol * (D / 4); c += kWave) {
+      const int r = c / (D / 4), v = c % (D / 4);
+      const float4 x = *reinterpret_cast<const float4*>(f + r * D + 4 * v);
+      float* dst = o_base + ((size_t)(r / G) * pj + r % G) * o_stride + 4 * v;
+      if constexpr (kCoherent) coherent_store4(dst, x);
+      else *reinterpret_cast<float4*>(dst) = x;
+    }
+    wave_lds_sync();
+  }
+  if (col < ncol) {
+    const size_t idx = (size_t)(col / G) * pj + col % G;
     if (quad == 0) {
       if constexpr (kCoherent) coherent_store2(reinterpret_cast<float*>(ml + idx * ml_stride), st.m, st.l);
       else ml[idx * ml_stride] = make_float2(st.m, st.l);
@@ -856,6 +891,10 @@ template <typename T, int D, int G, bool MQ = false, bool SH = false, int BS = k
 constexpr int decode_waves_per_simd() {
   if constexpr (sizeof(T) == 4) return (D == 128 && G >= 5) ? 1 : 2;
   if constexpr (sizeof(T) == 2 && D == 128) return 2;
+  // The fused append with 32-token e4m3 blocks needs a few more registers
+  // than three waves per SIMD leave; it serves small steps, and its launches
+  // are sized like plain decode's either way.
+  if constexpr (sizeof(T) == 1 && D == 128 && BS == 32 && AP) return 2;
   return 3;
 }
 
@@ -903,11 +942,11 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, false, BS,
   int done = 0;
   const auto st = run_seg<T, D, G, MQ, BS, AP>(args, lds[wave], b, h, tok_begin, tok_end, ctx, done, 0);
   if (ctx <= prm.part_tokens) {
-    write_rows<T, D, G>(out_row, st, args.v_scale, nq, hq);
+    write_rows<T, D, G>(out_row, st, args.v_scale, nq, hq, &lds[wave]);
   } else {
     write_partial<T, D, G>(reinterpret_cast<float2*>(ws_ml) + qh0 * prm.max_parts + part, prm.max_parts,
                            ws_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st,
-                           args.v_scale, nq, hq);
+                           args.v_scale, nq, hq, &lds[wave]);
   }
 }
 
@@ -1009,7 +1048,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, false, true, B
   const size_t qh0 = (size_t)(seq0 + m0) * hq + (size_t)h * G;
   write_partial<T, D, G>(reinterpret_cast<float2*>(prm.pre_ml) + qh0 * prm.max_parts + part, prm.max_parts,
                          prm.pre_o + (qh0 * prm.max_parts + part) * D, (size_t)prm.max_parts * D, st,
-                         args.v_scale, nm, hq);
+                         args.v_scale, nm, hq, &lds[wave]);
 }
 
 __device__ __forceinline__ float lane_xor16(float x) { return __shfl_xor(x, 16); }
@@ -1361,10 +1400,10 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
           write_rows_shared<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, prm.pre_ml, prm.pre_o, qh0,
                                      prm.max_parts, nsh);
         } else {
-          write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, nq, hq);
+          write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, nq, hq, &lds[wave]);
         }
       } else {
-        write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, nq, hq);
+        write_rows<T, D, G>(out_ptr + qh0 * D, st, args.v_scale, nq, hq, &lds[wave]);
       }
     } else {
       // Slot 0 holds the share's first segment, slot 1 its last one.
@@ -1375,7 +1414,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
       // wavefront of this launch can combine the piece (either way the
       // reduction kernel reads it after the launch).
       write_partial<T, D, G, kCanFuse>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st,
-                                       args.v_scale, nq, G);
+                                       args.v_scale, nq, G, &lds[wave]);
       desc[slot].row = b * args.hkv + h;
       desc[slot].row_start = x - w0;
       desc[slot].w0 = w0;

@@ -244,6 +244,14 @@ __device__ __forceinline__ void coherent_store2(float* p, float a, float b) {
   const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
   __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16 bytes written through to device scope, like coherent_store2 (the same
+// cache-policy bit on a 16-byte vector store; its completion is counted by
+// vmcnt like any other vector store).
+__device__ __forceinline__ void coherent_store4(float* p, float4 v) {
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  const f32x4_t x = {v.x, v.y, v.z, v.w};
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(x) : "memory");
+}
 __device__ __forceinline__ float2 coherent_load2(const float* p) {
   const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
