@@ -1306,6 +1306,64 @@ __device__ __forceinline__ void combine_split_row(TQ* out_row, const float* ws_m
   }
 }
 
+// A split row whose pieces all lie in one workgroup's four waves is combined
+// through LDS: each piece's (m, l) and unnormalized o (times the V scale) go
+// to the holder's slot, [G][D] floats written from the matrix layout.
+template <int D, int G>
+__device__ __forceinline__ void write_partial_lds(float* o, float2* ml, const MfmaSummary<D>& st, float v_scale) {
+  const int lane = threadIdx.x & 63;
+  const int quad = lane >> 4, col = lane & 15;
+  if (col < G) {
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const mf_f32x4 v = st.o[n];
+      *reinterpret_cast<float4*>(o + col * D + 16 * n + 4 * quad) =
+          make_float4(v[0] * v_scale, v[1] * v_scale, v[2] * v_scale, v[3] * v_scale);
+    }
+    if (quad == 0) ml[col] = make_float2(st.m, st.l);
+  }
+}
+
+// The combine of such a row: its first piece in slot first_slot of wave
+// `first`, each later piece in slot 0 of waves first+1 .. last with a
+// non-empty share (all of the same workgroup); part / pml are the
+// workgroup's slots, [wave][slot][G][D] and [wave][slot][G].
+template <typename TQ, int D, int G>
+__device__ __forceinline__ void combine_split_row_lds(TQ* out_row, const float* part, const float2* pml, long first,
+                                                      int first_slot, long last, long nw, int total) {
+  constexpr int kSlices = G * D / 4;                       // float4 slices of one piece
+  constexpr int NF = (kSlices + kWave - 1) / kWave;        // slices per lane
+  const int lane = threadIdx.x & 63;
+  float m[NF], l[NF];
+  float4 acc[NF];
+  {
+    const int p = (int)(first % 4) * 2 + first_slot;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int f = min(lane + kWave * j, kSlices - 1);
+      const float2 sm = pml[p * G + f / (D / 4)];
+      m[j] = sm.x;
+      l[j] = sm.y;
+      acc[j] = *reinterpret_cast<const float4*>(part + p * G * D + 4 * f);
+    }
+  }
+  for (long i = first + 1; i <= last; ++i) {
+    if (share_begin(i, nw, total) == share_begin(i + 1, nw, total)) continue;   // wave-uniform: empty share
+    const int p = (int)(i % 4) * 2;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int f = min(lane + kWave * j, kSlices - 1);
+      const float2 sm = pml[p * G + f / (D / 4)];
+      merge_state(m[j], l[j], acc[j], sm.x, sm.y, *reinterpret_cast<const float4*>(part + p * G * D + 4 * f));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const int f = lane + kWave * j;
+    if (f < kSlices) store_row4<TQ>(out_row + (size_t)f * 4, acc[j], 1.0f / l[j]);
+  }
+}
+
 // SH: the rows start after their shared partitions (decode_prefix_kernel has
 // run), and every row is merged with those partitions' summaries.
 // With one query row per sequence and no shared prefixes, split rows are
@@ -1314,8 +1372,11 @@ __device__ __forceinline__ void combine_split_row(TQ* out_row, const float* ws_m
 // prm.counters, f = the wave whose share holds the row's first window; no
 // other split row starts in that share). The holder that brings the count to
 // the row's window total combines the pieces, writes the row and sets the
-// counter back to zero, so the counters are zero between calls. Otherwise the
-// slot descriptors are written and decode_balanced_reduce_kernel combines.
+// counter back to zero, so the counters are zero between calls. With bf16
+// pools a row whose pieces all lie in one workgroup does the same through LDS
+// (summaries, counter and combine), with no device-scope store or atomic.
+// Otherwise the slot descriptors are written and
+// decode_balanced_reduce_kernel combines.
 template <typename T, int D, int G, bool MQ, bool SH, int BS, bool AP>
 __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP>())) void decode_balanced_kernel(
     typename IoType<T>::type* __restrict__ out_ptr, float* __restrict__ ws_ml, float* __restrict__ ws_o,
@@ -1329,6 +1390,17 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
   __shared__ SegLds<T, D, G> lds[4];
   __shared__ int cum[kMaxBalancedSeqs + 1];
   __shared__ int scan_scratch[256];
+  // Split rows whose pieces all lie in this workgroup's four waves meet in
+  // LDS (bf16 pools, G * D <= 512: two workgroups per CU still fit): the
+  // partials [wave][slot][G][D], their (m, l), and one counter per wave (the
+  // wave whose share holds the row's first window). Only a cut between the
+  // last wave of one workgroup and the first of the next sends a row through
+  // the device-scope workspace, so about three split rows in four stay here.
+  constexpr bool kLdsCombine = kCanFuse && sizeof(T) == 2 && G * D <= 512;
+  __shared__ float lds_part[kLdsCombine ? 4 * 2 * G * D : 4];
+  __shared__ float2 lds_pml[kLdsCombine ? 4 * 2 * G : 1];
+  __shared__ int lds_cnt[kLdsCombine ? 4 : 1];
+  if (kLdsCombine && threadIdx.x < 4) lds_cnt[threadIdx.x] = 0;   // published by the prefix sum's barriers
   const int nq = MQ ? args.nq : 1;   // query rows per sequence
   const long max_ctx = (long)args.max_blocks * BS;
   const int total = window_prefix_sum(context_lens, SH ? prm.shared_start : nullptr, prm.num_seqs, args.hkv, cum,
@@ -1370,6 +1442,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
   if (wid >= nw) return;
   SlotDesc desc[2];
   desc[0].row = desc[1].row = -1;
+  bool desc_local[2] = {false, false};               // the slot's row is combined through LDS
   const int x0 = total ? share_begin(wid, nw, total) : 0;
   const int x1 = total ? share_begin(wid + 1, nw, total) : 0;
   // The hardware issues the oldest wavefront first. With equal shares that
@@ -1408,6 +1481,17 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
     } else {
       // Slot 0 holds the share's first segment, slot 1 its last one.
       const int slot = (x == x0) ? 0 : 1;
+      bool local = false;
+      if constexpr (kLdsCombine) {
+        if (FC) local = share_of(x - w0, nw, total) / 4 == share_of((long)(x - w0) + nwb - 1, nw, total) / 4;
+      }
+      desc_local[slot] = local;
+      if constexpr (kLdsCombine) {
+        if (local)
+          write_partial_lds<D, G>(lds_part + (wave * 2 + slot) * G * D, lds_pml + (wave * 2 + slot) * G, st,
+                                  args.v_scale);
+      }
+      if (!local) {
       // A slot holds nq * G summary rows, column (row j, head g) at j * G + g.
       const size_t base = ((size_t)wid * 2 + slot) * nq * G;
       // One query row, no shared prefixes: device-scope stores, so that a
@@ -1415,6 +1499,7 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
       // reduction kernel reads it after the launch).
       write_partial<T, D, G, kCanFuse>(reinterpret_cast<float2*>(ws_ml) + base, 1, ws_o + base * D, D, st,
                                        args.v_scale, nq, G, &lds[wave]);
+      }
       desc[slot].row = b * args.hkv + h;
       desc[slot].row_start = x - w0;
       desc[slot].w0 = w0;
@@ -1429,9 +1514,14 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
     // rows' totals, after the share's last segment so that the combine's
     // registers stay out of the segment loop; the wave that completes a row
     // combines it and zeroes its counter. The counter of a row is entry f of
-    // prm.counters, f = the wave whose share holds the row's first window.
+    // prm.counters, f = the wave whose share holds the row's first window,
+    // or, for a row held by this workgroup alone, lds_cnt[f % 4] (which
+    // starts at zero with the workgroup).
     if (desc[0].row >= 0 || desc[1].row >= 0) {
-      wait_stores_complete();                            // the summaries are published before they count
+      const bool any_global = (desc[0].row >= 0 && !desc_local[0]) || (desc[1].row >= 0 && !desc_local[1]);
+      const bool any_local = desc_local[0] || desc_local[1];
+      if (any_global) wait_stores_complete();            // the summaries are published before they count
+      if (any_local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       bool mine[2] = {false, false};
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
@@ -1439,12 +1529,19 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
         const long f = share_of(desc[k].row_start, nw, total);
         const int windows = desc[k].w1 - desc[k].w0;
         int old = 0;
-        if (lane == 0) old = atomicAdd(prm.counters + f, windows);
+        if (lane == 0) {
+          if (kLdsCombine && desc_local[k])
+            old = __hip_atomic_fetch_add(&lds_cnt[kLdsCombine ? f % 4 : 0], windows, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+          else
+            old = atomicAdd(prm.counters + f, windows);
+        }
         old = __builtin_amdgcn_readfirstlane(old);
         mine[k] = old + windows == desc[k].row_windows;  // every other piece is published
       }
       if (mine[0] || mine[1]) {
         asm volatile("" ::: "memory");                   // the pieces are read after the count
+        if (any_local) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           if (!mine[k]) continue;
@@ -1452,9 +1549,16 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
           const long f = share_of(row_start, nw, total);
           const long last = share_of((long)row_start + desc[k].row_windows - 1, nw, total);
           const int b = desc[k].row / args.hkv, h = desc[k].row % args.hkv;
-          combine_split_row<TQ, D, G>(out_ptr + ((size_t)b * args.hkv + h) * G * D, ws_ml, ws_o, f,
-                                      share_begin(f, nw, total) == row_start ? 0 : 1, last, nw, total);
-          if (lane == 0) atomicExch(prm.counters + f, 0);
+          const int first_slot = share_begin(f, nw, total) == row_start ? 0 : 1;
+          if (desc_local[k]) {
+            if constexpr (kLdsCombine)
+              combine_split_row_lds<TQ, D, G>(out_ptr + ((size_t)b * args.hkv + h) * G * D, lds_part, lds_pml, f,
+                                              first_slot, last, nw, total);
+          } else {
+            combine_split_row<TQ, D, G>(out_ptr + ((size_t)b * args.hkv + h) * G * D, ws_ml, ws_o, f, first_slot,
+                                        last, nw, total);
+            if (lane == 0) atomicExch(prm.counters + f, 0);
+          }
         }
       }
     }
