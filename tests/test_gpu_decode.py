@@ -137,6 +137,20 @@ def test_decode_dtypes_head_dims(dtype, d):
     run_and_check(step, partition_size=64)
 
 
+@pytest.mark.parametrize("d,hq,hkv", [(128, 32, 8), (128, 8, 8), (128, 24, 8), (64, 64, 8), (128, 64, 8)])
+def test_decode_in_launch_combine(d, hq, hkv):
+    """1024 rows for about 2048 resident wavefronts (a row per eight waves or
+    more, so the partition launch combines its split rows itself), 1..400
+    tokens each: rows span two or three waves, and several hundred of them
+    have every piece inside one four-wave workgroup (combined through LDS
+    when G * D <= 512: the first four cases) while as many are cut between
+    workgroups (combined through the workspace; the last case, G * D = 1024,
+    takes that path for all)."""
+    ctx = np.random.Generator(np.random.PCG64(700 + hq)).integers(1, 401, 128).tolist()
+    step = W.custom(f"fc{d}_{hq}_{hkv}", seed=700 + hq, dtype="bf16", hq=hq, hkv=hkv, d=d, ctx=ctx)
+    run_and_check(step)
+
+
 @pytest.mark.parametrize("part", [-1, 0, 64, 128, 192, 512])
 def test_decode_partition_sizes_agree(part):
     step = W.custom("parts", seed=400, dtype="bf16", hq=8, hkv=2, d=128,
