@@ -48,6 +48,8 @@
 //     100-160 us and shortens the launch by about 6%.
 //   * fixed partitions of P tokens: one wavefront per (b, h, partition),
 //     partitions dispatched in descending index order (long sequences first).
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -1306,6 +1308,24 @@ __device__ __forceinline__ void combine_split_row(TQ* out_row, const float* ws_m
   }
 }
 
+// Split rows held by one workgroup can meet in LDS in the one-row kernels of
+// the matrix-core pools with G * D <= 512 (a piece is 2 KiB or less).
+template <typename T, int D, int G, bool MQ, bool SH>
+__host__ __device__ constexpr bool balanced_lds_combine() {
+  return !MQ && !SH && UsesMfma<T>::value && G * D <= 512;
+}
+
+// Dynamic LDS of the balanced kernel: the window prefix over sequences
+// (num_seqs + 1 ints, in whole 16-byte units), then, for the LDS combine, the
+// partials of [4 waves][2 slots] pieces and their (m, l) pairs.
+__host__ __device__ constexpr size_t balanced_cum_bytes(int num_seqs) {
+  return ((size_t)(num_seqs + 1) * sizeof(int) + 15) & ~(size_t)15;
+}
+template <int D, int G>
+constexpr size_t balanced_part_bytes() {
+  return (size_t)8 * G * D * sizeof(float) + (size_t)8 * G * sizeof(float2);
+}
+
 // A split row whose pieces all lie in one workgroup's four waves is combined
 // through LDS: each piece's (m, l) and unnormalized o (times the V scale) go
 // to the holder's slot, [G][D] floats written from the matrix layout.
@@ -1388,17 +1408,20 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
   constexpr bool kCanFuse = !MQ && !SH;
   const bool FC = kCanFuse && prm.counters != nullptr;
   __shared__ SegLds<T, D, G> lds[4];
-  __shared__ int cum[kMaxBalancedSeqs + 1];
   __shared__ int scan_scratch[256];
-  // Split rows whose pieces all lie in this workgroup's four waves meet in
-  // LDS (bf16 pools, G * D <= 512: two workgroups per CU still fit): the
-  // partials [wave][slot][G][D], their (m, l), and one counter per wave (the
-  // wave whose share holds the row's first window). Only a cut between the
-  // last wave of one workgroup and the first of the next sends a row through
-  // the device-scope workspace, so about three split rows in four stay here.
-  constexpr bool kLdsCombine = kCanFuse && sizeof(T) == 2 && G * D <= 512;
-  __shared__ float lds_part[kLdsCombine ? 4 * 2 * G * D : 4];
-  __shared__ float2 lds_pml[kLdsCombine ? 4 * 2 * G : 1];
+  // Dynamic LDS: the window prefix over sequences (cum), then, when
+  // prm.lds_parts is set, the partials of split rows whose pieces all lie in
+  // this workgroup's four waves, [wave][slot][G][D] floats, and their (m, l).
+  // Such rows meet in LDS, with one counter per wave (the wave whose share
+  // holds the row's first window). Only a cut between the last wave of one
+  // workgroup and the first of the next sends a row through the device-scope
+  // workspace, so about three split rows in four stay here.
+  extern __shared__ __align__(16) int balanced_dyn[];
+  int* const cum = balanced_dyn;
+  constexpr bool kLdsCombine = balanced_lds_combine<T, D, G, MQ, SH>();
+  float* const lds_part =
+      reinterpret_cast<float*>(reinterpret_cast<char*>(balanced_dyn) + balanced_cum_bytes(prm.num_seqs));
+  float2* const lds_pml = reinterpret_cast<float2*>(lds_part + 8 * G * D);
   __shared__ int lds_cnt[kLdsCombine ? 4 : 1];
   if (kLdsCombine && threadIdx.x < 4) lds_cnt[threadIdx.x] = 0;   // published by the prefix sum's barriers
   const int nq = MQ ? args.nq : 1;   // query rows per sequence
@@ -1483,7 +1506,8 @@ __global__ __launch_bounds__(256, (decode_waves_per_simd<T, D, G, MQ, SH, BS, AP
       const int slot = (x == x0) ? 0 : 1;
       bool local = false;
       if constexpr (kLdsCombine) {
-        if (FC) local = share_of(x - w0, nw, total) / 4 == share_of((long)(x - w0) + nwb - 1, nw, total) / 4;
+        if (FC && prm.lds_parts)
+          local = share_of(x - w0, nw, total) / 4 == share_of((long)(x - w0) + nwb - 1, nw, total) / 4;
       }
       desc_local[slot] = local;
       if constexpr (kLdsCombine) {
@@ -1854,19 +1878,23 @@ hipError_t launch_decode_tgm(const DecodeParams& prm, hipStream_t stream, const 
     timer.begin(KernelKind::kDecodePartition, stream);
     SlotDesc* desc = static_cast<SlotDesc*>(prm.ws_desc);
     const dim3 grid((unsigned)((prm.num_waves + 3) / 4));
+    size_t dyn = balanced_cum_bytes(prm.num_seqs);
+    if constexpr (balanced_lds_combine<T, D, G, MQ, false>()) {
+      if (prm.lds_parts && prm.counters != nullptr) dyn += balanced_part_bytes<D, G>();
+    }
     if constexpr (kShareable) {
       if (prm.shared_start != nullptr) {
-        PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, true, BS, false>), grid, dim3(256), 0, stream, out,
+        PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, true, BS, false>), grid, dim3(256), dyn, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       } else if (prm.new_key != nullptr) {
-        PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, false, BS, true>), grid, dim3(256), 0, stream, out,
+        PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, false, BS, true>), grid, dim3(256), dyn, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       } else {
-        PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), 0, stream, out,
+        PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), dyn, stream, out,
                            prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
       }
     } else {
-      PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), 0, stream, out,
+      PKV_LAUNCH((decode_balanced_kernel<T, D, G, MQ, false, BS, false>), grid, dim3(256), dyn, stream, out,
                          prm.ws_ml, prm.ws_o, desc, prm.context_lens, args, prm);
     }
     timer.end(KernelKind::kDecodePartition, stream);
@@ -1944,50 +1972,68 @@ hipError_t launch_decode_t(const DecodeParams& prm, hipStream_t stream, const Ke
   }
 }
 
-// Resident wavefronts per CU of one balanced-kernel variant (cached).
+// Resident workgroups per CU of one balanced-kernel variant with `dyn`
+// bytes of dynamic LDS. The last answer for each of the two sizes a call
+// asks about (without and with the LDS partials: `which`) is cached.
 template <typename T, int D, int G, bool MQ, bool SH, int BS, bool AP>
-int balanced_waves_per_cu() {
-  static int cached = 0;
-  if (cached == 0) {
-    int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ, SH, BS, AP>, 256, 0) !=
-            hipSuccess ||
-        blocks <= 0) {
-      (void)hipGetLastError();
-      blocks = decode_waves_per_simd<T, D, G, MQ, SH, BS, AP>();
-    }
-    cached = 4 * blocks;
+int balanced_blocks_per_cu(size_t dyn, int which) {
+  static std::atomic<uint64_t> cached[2];   // (dyn << 8) | workgroups; 0 = none yet
+  const uint64_t c = cached[which].load(std::memory_order_relaxed);
+  if (c != 0 && (c >> 8) == dyn) return (int)(c & 0xff);
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_balanced_kernel<T, D, G, MQ, SH, BS, AP>, 256,
+                                                   dyn) != hipSuccess ||
+      blocks <= 0) {
+    (void)hipGetLastError();
+    blocks = which == 0 ? decode_waves_per_simd<T, D, G, MQ, SH, BS, AP>() : 0;
   }
-  return cached;
+  blocks = std::min(blocks, 255);
+  cached[which].store(((uint64_t)dyn << 8) | (uint64_t)blocks, std::memory_order_relaxed);
+  return blocks;
+}
+
+// Resident wavefronts per CU of a variant at num_seqs sequences, and whether
+// the LDS partials fit without lowering that count (only then are they used,
+// so the split never depends on them).
+template <typename T, int D, int G, bool MQ, bool SH, int BS, bool AP>
+int balanced_waves_per_cu(int num_seqs, bool* lds_parts) {
+  const size_t cum = balanced_cum_bytes(num_seqs);
+  const int blocks = balanced_blocks_per_cu<T, D, G, MQ, SH, BS, AP>(cum, 0);
+  bool parts = false;
+  if constexpr (balanced_lds_combine<T, D, G, MQ, SH>())
+    parts = balanced_blocks_per_cu<T, D, G, MQ, SH, BS, AP>(cum + balanced_part_bytes<D, G>(), 1) == blocks;
+  *lds_parts = parts;
+  return 4 * blocks;
 }
 
 template <typename T, int D, int G>
-int waves_per_cu_tg(const BalancedVariant& v) {
+int waves_per_cu_tg(const BalancedVariant& v, int n, bool* p) {
   if constexpr (UsesMfma<T>::value) {
     if (v.block_size == 32) {
-      if (v.multi) return balanced_waves_per_cu<T, D, G, true, false, 32, false>();
-      if (v.shared) return balanced_waves_per_cu<T, D, G, false, true, 32, false>();
-      if (v.append) return balanced_waves_per_cu<T, D, G, false, false, 32, true>();
-      return balanced_waves_per_cu<T, D, G, false, false, 32, false>();
+      if (v.multi) return balanced_waves_per_cu<T, D, G, true, false, 32, false>(n, p);
+      if (v.shared) return balanced_waves_per_cu<T, D, G, false, true, 32, false>(n, p);
+      if (v.append) return balanced_waves_per_cu<T, D, G, false, false, 32, true>(n, p);
+      return balanced_waves_per_cu<T, D, G, false, false, 32, false>(n, p);
     }
-    if (v.multi) return balanced_waves_per_cu<T, D, G, true, false, kBlockSize, false>();
-    if (v.shared) return balanced_waves_per_cu<T, D, G, false, true, kBlockSize, false>();
-    if (v.append) return balanced_waves_per_cu<T, D, G, false, false, kBlockSize, true>();
+    if (v.multi) return balanced_waves_per_cu<T, D, G, true, false, kBlockSize, false>(n, p);
+    if (v.shared) return balanced_waves_per_cu<T, D, G, false, true, kBlockSize, false>(n, p);
+    if (v.append) return balanced_waves_per_cu<T, D, G, false, false, kBlockSize, true>(n, p);
   }
-  return balanced_waves_per_cu<T, D, G, false, false, kBlockSize, false>();
+  return balanced_waves_per_cu<T, D, G, false, false, kBlockSize, false>(n, p);
 }
 
 template <typename T, int D>
-int waves_per_cu_t(const BalancedVariant& v) {
+int waves_per_cu_t(const BalancedVariant& v, int n, bool* p) {
+  *p = false;
   switch (v.group) {
-    case 1: return waves_per_cu_tg<T, D, 1>(v);
-    case 2: return waves_per_cu_tg<T, D, 2>(v);
-    case 3: return waves_per_cu_tg<T, D, 3>(v);
-    case 4: return waves_per_cu_tg<T, D, 4>(v);
-    case 5: return waves_per_cu_tg<T, D, 5>(v);
-    case 6: return waves_per_cu_tg<T, D, 6>(v);
-    case 7: return waves_per_cu_tg<T, D, 7>(v);
-    case 8: return waves_per_cu_tg<T, D, 8>(v);
+    case 1: return waves_per_cu_tg<T, D, 1>(v, n, p);
+    case 2: return waves_per_cu_tg<T, D, 2>(v, n, p);
+    case 3: return waves_per_cu_tg<T, D, 3>(v, n, p);
+    case 4: return waves_per_cu_tg<T, D, 4>(v, n, p);
+    case 5: return waves_per_cu_tg<T, D, 5>(v, n, p);
+    case 6: return waves_per_cu_tg<T, D, 6>(v, n, p);
+    case 7: return waves_per_cu_tg<T, D, 7>(v, n, p);
+    case 8: return waves_per_cu_tg<T, D, 8>(v, n, p);
     default: return 8;
   }
 }
@@ -1998,12 +2044,16 @@ int decode_balanced_max_seqs() { return kMaxBalancedSeqs; }
 
 size_t decode_balanced_desc_bytes() { return sizeof(SlotDesc); }
 
-int decode_balanced_waves_per_cu(PoolType type, int head_dim, const BalancedVariant& v) {
+int decode_balanced_waves_per_cu(PoolType type, int head_dim, const BalancedVariant& v, int num_seqs,
+                                 bool* lds_parts) {
   if (type == PoolType::kFP8)
-    return head_dim == 128 ? waves_per_cu_t<uint8_t, 128>(v) : waves_per_cu_t<uint8_t, 64>(v);
+    return head_dim == 128 ? waves_per_cu_t<uint8_t, 128>(v, num_seqs, lds_parts)
+                           : waves_per_cu_t<uint8_t, 64>(v, num_seqs, lds_parts);
   if (type == PoolType::kBF16)
-    return head_dim == 128 ? waves_per_cu_t<uint16_t, 128>(v) : waves_per_cu_t<uint16_t, 64>(v);
-  return head_dim == 128 ? waves_per_cu_t<float, 128>(v) : waves_per_cu_t<float, 64>(v);
+    return head_dim == 128 ? waves_per_cu_t<uint16_t, 128>(v, num_seqs, lds_parts)
+                           : waves_per_cu_t<uint16_t, 64>(v, num_seqs, lds_parts);
+  return head_dim == 128 ? waves_per_cu_t<float, 128>(v, num_seqs, lds_parts)
+                         : waves_per_cu_t<float, 64>(v, num_seqs, lds_parts);
 }
 
 hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,

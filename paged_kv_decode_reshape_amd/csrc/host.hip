@@ -495,11 +495,13 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
   }
   const pkv::PoolType type = pool_type(pool->dtype);
   int num_waves = 0;
+  bool lds_parts = false;
   if (sp.balanced) {
     // The fused append is sized like plain decode (not by its own occupancy)
     // so that both split the rows identically and give bit-identical outputs.
     const pkv::BalancedVariant v{group, q_per_seq > 1, false, false, pool->block_size};
-    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, v);
+    const long slots =
+        (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, v, num_seqs, &lds_parts);
     num_waves = (int)std::max(1L, std::min(sp.wave_cap, slots));
   } else {
     const long units = (long)pool->num_kv_heads * num_seqs * sp.max_parts;
@@ -534,8 +536,10 @@ pkv_status decode_run(const pkv_pool* pool, int layer, void* out, const void* qu
   // over 8 wavefronts are combined faster in the launch, 18-19 us against
   // 20-21 us per step with the extra kernel; rows over 32 slower, 28-32 us
   // against 21-25 us.)
-  if (need > 0 && sp.balanced && q_per_seq == 1 && (long)num_seqs * pool->num_kv_heads * 8 >= num_waves)
+  if (need > 0 && sp.balanced && q_per_seq == 1 && (long)num_seqs * pool->num_kv_heads * 8 >= num_waves) {
     prm.counters = reinterpret_cast<int32_t*>(ws);
+    prm.lds_parts = lds_parts;
+  }
   prm.scale_log2 = scale * 1.4426950408889634f * pool->k_scale[layer];
   prm.v_scale = pool->v_scale[layer];
   prm.q_per_seq = q_per_seq;
@@ -680,7 +684,9 @@ pkv_status paged_attention_decode_shared(const pkv_pool* pool, int layer, void* 
     ws_o = reinterpret_cast<float*>(ws + lay.off_o);
     ws_desc = ws + lay.off_desc;
     const pkv::BalancedVariant v{group, false, true, false, pool->block_size};
-    const long slots = (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, v);
+    bool lds_parts = false;   // shared prefixes: split rows go to the reduction
+    const long slots =
+        (long)device_cu_count() * pkv::decode_balanced_waves_per_cu(type, pool->head_dim, v, num_seqs, &lds_parts);
     num_waves = (int)std::max(1L, std::min(lay.own.wave_cap, slots));
   }
   pkv::DecodeParams prm{};

@@ -85,6 +85,7 @@ struct DecodeParams {
   int part_tokens;         // fixed partitions: tokens per partition (multiple of 64)
   int max_parts;           // fixed partitions: partitions of the longest possible sequence
   int num_waves;           // > 0: balanced split over this many wavefronts
+  int lds_parts;           // balanced split with counters: split rows held by one workgroup meet in LDS
   float scale_log2;        // scale * log2(e), times the K scale of an e4m3 pool
   float v_scale;           // e4m3 pools: the V scale; else 1
   int q_per_seq;           // query rows per sequence, at positions ctx - q_per_seq .. ctx - 1
@@ -156,8 +157,9 @@ hipError_t launch_copy_blocks(const CopyParams& prm, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& prm, PoolType type, hipStream_t stream,
                          const KernelTimer& timer);
 // Balanced decode: resident wavefronts per CU of the kernel variant a call
-// runs, the largest batch its in-LDS prefix sum handles, and the size of one
-// slot descriptor.
+// runs at num_seqs sequences (and in *lds_parts whether its split rows held
+// by one workgroup can be combined in LDS at that occupancy), the largest
+// batch its in-LDS prefix sum handles, and the size of one slot descriptor.
 struct BalancedVariant {
   int group;         // query heads per KV head
   bool multi;        // several query rows per sequence
@@ -165,7 +167,8 @@ struct BalancedVariant {
   bool append;       // fused append
   int block_size;    // 16 or 32
 };
-int decode_balanced_waves_per_cu(PoolType type, int head_dim, const BalancedVariant& v);
+int decode_balanced_waves_per_cu(PoolType type, int head_dim, const BalancedVariant& v, int num_seqs,
+                                 bool* lds_parts);
 int decode_balanced_max_seqs();
 size_t decode_balanced_desc_bytes();
 hipError_t launch_prefill(const PrefillParams& prm, PoolType type, hipStream_t stream, const KernelTimer& timer);
