@@ -151,6 +151,15 @@ def test_decode_in_launch_combine(d, hq, hkv):
     run_and_check(step)
 
 
+def test_decode_balanced_batch_limit():
+    """4096 sequences, the most the balanced split takes (its window prefix
+    then fills 16 KiB of dynamic LDS beside the LDS partials), with empty
+    and short contexts."""
+    ctx = np.random.Generator(np.random.PCG64(760)).integers(0, 97, 4096).tolist()
+    step = W.custom("b4096", seed=760, dtype="bf16", hq=4, hkv=1, d=128, ctx=ctx)
+    run_and_check(step)
+
+
 @pytest.mark.parametrize("part", [-1, 0, 64, 128, 192, 512])
 def test_decode_partition_sizes_agree(part):
     step = W.custom("parts", seed=400, dtype="bf16", hq=8, hkv=2, d=128,

@@ -118,6 +118,18 @@ def test_fp8_decode_parity(hq, hkv, d, part):
     check_decode(step, 1.0 / 96, 1.0 / 32, partition_size=part)
 
 
+@pytest.mark.parametrize("batch,cmax", [(256, 200), (640, 100)])
+def test_fp8_decode_in_launch_combine(batch, cmax):
+    """Enough rows for the partition launch to combine its split rows itself.
+    At 256 sequences the partials of rows held by one workgroup fit in LDS
+    beside the window prefix at three workgroups per CU, and those rows meet
+    there; at 640 the prefix leaves no room, and every split row goes through
+    the workspace. Both give the oracle's result."""
+    ctx = np.random.Generator(np.random.PCG64(761 + batch)).integers(1, cmax + 1, batch).tolist()
+    step = W.custom(f"f8fc{batch}", seed=761 + batch, dtype="bf16", hq=8, hkv=2, d=128, ctx=ctx)
+    check_decode(step, 1.0 / 96, 1.0 / 32)
+
+
 def test_fp8_decode_unit_scales():
     """Scale 1: inputs near zero land on subnormal codes."""
     step = W.custom("f8dec_unit", seed=720, dtype="bf16", hq=8, hkv=2, d=128, ctx=[5, 77, 400])
